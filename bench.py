@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""W4A4-g128 GEMM throughput including activation quantization, on the
+LLaMA-2-70B FFN linear shapes (and, by flag, the other workloads).
+
+One step = one pass of the INT4 hot path over one batch of M tokens through the
+three FFN linears (w1 and w3: K=8192 -> N=28672; w2: K=28672 -> N=8192): for
+each linear, per-token group-128 INT4 quantization of its fp16 input followed by
+the group-dequantized INT4 GEMM (fp32 Y). Weights are packed once, untimed
+(offline). Inputs are synthetic (seeded), resident in HBM before timing starts.
+
+Prints one JSON line. `value` = useful ops (2*M*N*K summed over the linears)
+per second of the timed steps, in TOPS. `roofline` is for the GEMM kernel (the
+dominant one), timed per launch with HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded row/column sample of the same
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--tokens M]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4-g128 GEMM TOPS incl. act-quant, LLaMA-70B FFN shapes; % of MFMA peak"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix-core peak (5.0 POP/s)
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4/fp6 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+# name -> (tokens M, [(K, N), ...], act group, weight group, format)
+WORKLOADS = {
+    "llama2_70b_ffn": (4096, [(8192, 28672), (8192, 28672), (28672, 8192)], 128, 128, "int4"),
+    "llama2_7b_ffn": (2048, [(4096, 11008), (4096, 11008), (11008, 4096)], 128, 128, "int4"),
+    "granularity": (4096, [(8192, 8192)], 128, 128, "int4"),
+    "qwen25_7b_mxfp4_ffn": (4096, [(3584, 18944), (3584, 18944), (18944, 3584)], 32, 32, "mxfp4"),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
+    """Time the CPU oracle on n_rows tokens x n_cols output features per linear."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from w4a4_quantized_gemm_quantize_amd import synth
+
+    rows = synth.sample_rows(M, n_rows, seed=11)
+    work = []
+    for li, (K, N) in enumerate(wl):
+        cols = synth.sample_rows(N, min(n_cols, N), seed=12 + li)
+        x = synth.activations(M, K, dist="t3", seed=li, rows=rows)
+        w = synth.weights(N, K, seed=100 + li, rows=cols)
+        wpk = oracle.int4_quantize(w, gw) if fmt == "int4" else oracle.mxfp4_quantize(w)  # offline, untimed
+        work.append((x, wpk, K, len(cols)))
+    ops = 0
+    t0 = time.perf_counter()
+    for x, wpk, K, nc in work:
+        if fmt == "int4":
+            qa, sa = oracle.int4_quantize(x, ga)
+            oracle.w4a4_gemm(qa, sa, ga, wpk[0], wpk[1], gw)
+        else:
+            ca, ea = oracle.mxfp4_quantize(x)
+            oracle.mxfp4_gemm(ca, ea, wpk[0], wpk[1])
+        ops += 2 * len(rows) * nc * K
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {
+        "value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+        "sample": (f"{len(rows)} of {M} tokens x {min(n_cols, wl[0][1])}-col sample of each linear's N "
+                   f"(all K), act-quant + GEMM, {dt:.1f} s on the host"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_70b_ffn", choices=sorted(WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=None, help="override M")
+    ap.add_argument("--group-a", type=int, default=None, help="override the activation group")
+    ap.add_argument("--ydtype", choices=["f32", "f16"], default="f32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-cols", type=int, default=4096)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from w4a4_quantized_gemm_quantize_amd import _lib, ops, synth
+
+    M0, wl, ga, gw, fmt = WORKLOADS[args.workload]
+    M = args.tokens or M0
+    if args.group_a:
+        ga = args.group_a
+    ydt = torch.float32 if args.ydtype == "f32" else torch.float16
+    dev = torch.device("cuda:0")
+    _lib.load_library()
+    log(f"workload {args.workload}: M={M} linears={wl} ga={ga} gw={gw} fmt={fmt}")
+
+    layers = []
+    for li, (K, N) in enumerate(wl):
+        x = torch.from_numpy(synth.activations(M, K, dist="t3", seed=li)).to(dev)
+        w = torch.from_numpy(synth.weights(N, K, seed=100 + li)).to(dev)
+        if fmt == "int4":
+            wq, ws = ops.w4a4_pack_weight(w, gw)
+            xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M, K // ga), dtype=torch.float32, device=dev)
+        else:
+            wq, ws = ops.mxfp4_quantize(w)
+            xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        del w
+        y = torch.empty((M, N), dtype=ydt, device=dev)
+        layers.append(dict(K=K, N=N, x=x, wq=wq, ws=ws, xq=xq, xs=xs, y=y))
+        log(f"linear {li}: K={K} N={N} ready")
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        for li, L in enumerate(layers):
+            if ev is not None:
+                ev[li][0].record()
+            if fmt == "int4":
+                ops.w4a4_quantize_act(L["x"], ga, out=(L["xq"], L["xs"]))
+            else:
+                ops.mxfp4_quantize(L["x"], out=(L["xq"], L["xs"]))
+            if ev is not None:
+                ev[li][1].record()
+            if fmt == "int4":
+                ops.w4a4_gemm(L["xq"], L["xs"], ga, L["wq"], L["ws"], gw, out=L["y"])
+            else:
+                ops.mxfp4_gemm(L["xq"], L["xs"], L["wq"], L["ws"], out=L["y"])
+            if ev is not None:
+                ev[li][2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed = start.elapsed_time(end) / 1e3
+    log(f"timed {args.steps} steps: {elapsed * 1e3:.2f} ms (wall {wall * 1e3:.2f} ms)")
+
+    ops_per_step = sum(2 * M * L["N"] * L["K"] for L in layers)
+    value = ops_per_step * args.steps / elapsed / 1e12
+
+    gemm_s = np.zeros(len(layers))
+    quant_s = np.zeros(len(layers))
+    for s in range(args.steps):
+        for li in range(len(layers)):
+            e = evs[s][li]
+            quant_s[li] += e[0].elapsed_time(e[1]) / 1e3
+            gemm_s[li] += e[1].elapsed_time(e[2]) / 1e3
+    gemm_ops = sum(2 * M * L["N"] * L["K"] for L in layers) * args.steps
+    achieved = gemm_ops / gemm_s.sum() / 1e12
+    peak = PEAK_INT8_TOPS if fmt == "int4" else PEAK_FP4_TFLOPS
+    ybytes = 4 if ydt == torch.float32 else 2
+    quant_bytes = 0
+    for L in layers:
+        sbytes = 4 * (L["K"] // ga) if fmt == "int4" else L["K"] // 32
+        quant_bytes += M * (2 * L["K"] + L["K"] // 2 + sbytes)
+    quant_gbs = quant_bytes * args.steps / quant_s.sum() / 1e9
+    per_linear = []
+    for li, L in enumerate(layers):
+        per_linear.append({
+            "K": L["K"], "N": L["N"],
+            "gemm_us": gemm_s[li] / args.steps * 1e6,
+            "gemm_tops": 2 * M * L["N"] * L["K"] / (gemm_s[li] / args.steps) / 1e12,
+            "quant_us": quant_s[li] / args.steps * 1e6,
+        })
+
+    result = {
+        "metric": METRIC if args.workload == "llama2_70b_ffn" else f"{fmt} GEMM TOPS incl. act-quant, {args.workload}",
+        "value": value,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4" if fmt == "int4" else "fp4",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "tokens": M,
+            "linears_KxN": [f"{K}x{N}" for K, N in wl],
+            "group_a": ga if fmt == "int4" else 32, "group_w": gw if fmt == "int4" else 32,
+            "y_dtype": args.ydtype, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": None,
+        },
+        "act_quant": {"GB/s": quant_gbs, "frac_hbm": quant_gbs / PEAK_HBM_GBS},
+        "per_linear": per_linear,
+        "fraction_of_mfma_peak_incl_quant": value / peak,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, M, ga, gw, fmt, args.cpu_rows, args.cpu_cols)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,164 @@
+/*
+ * w4a4.h -- C ABI of libw4a4.so: W4A4 group-quantized GEMM and MXFP4 GEMM on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (see the operation comments below for the passages):
+ *   Y[M,N] = X[M,K] * W[N,K]^T for a linear layer whose activations X and
+ *   weights W are both 4-bit ("W4A4"), either
+ *   - INT4 with one fp32 scale per group of g consecutive K elements
+ *     ("APEX4: Efficient Pure W4A4 LLM Inference via Intra-SM Compute
+ *     Rebalancing", abstract: the W4A4-g128 pure INT4 GEMM whose per-group
+ *     dequantization runs on the vector units, and its mixed-granularity mode),
+ *   - or MXFP4: FP4 E2M1 values with one E8M0 power-of-two scale per 32 K
+ *     elements ("the open-standard MXFP4", FP4 RL post-training abstract on the
+ *     "Depth Registers Unlock W4A4 on SwiGLU" page; block rule from the OCP
+ *     Microscaling Formats v1.0 specification).
+ *
+ * Conventions (all entry points):
+ *   - Every data pointer is a DEVICE pointer, owned by the caller. The library
+ *     allocates no memory and keeps no mutable state; it is thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous on that stream; nothing synchronizes.
+ *   - Arguments are validated first, synchronously, before any HIP call. On a
+ *     validation failure the call returns the status and launches nothing.
+ *     A launch failure reported by hipGetLastError() returns W4A4_E_HIP.
+ *   - Extents are int64_t element counts. A zero extent (M, N or rows == 0) is a
+ *     valid no-op; pointers whose extent is zero may then be NULL.
+ *   - Buffers must not overlap. Results are deterministic (no atomics).
+ *   - Packed 4-bit layout (INT4 and MXFP4 alike): row-major [rows][K/2] bytes,
+ *     K contiguous, two codes per byte, the even k in the LOW nibble.
+ *     INT4 codes are two's complement in [-8, 7]; MXFP4 codes are E2M1
+ *     (sign<<3 | magnitude index into {0,0.5,1,1.5,2,3,4,6}).
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_E_NULL = 1,   /* a required pointer is NULL */
+  W4A4_E_SHAPE = 2,  /* negative extent, K not a supported multiple, ld too small, or window out of range */
+  W4A4_E_GROUP = 3,  /* unsupported group size, group does not divide K, or groups do not nest */
+  W4A4_E_ALIGN = 4,  /* a pointer or leading dimension breaks the alignment rule of the call */
+  W4A4_E_DTYPE = 5,  /* unknown output dtype */
+  W4A4_E_HIP = 6     /* the HIP runtime reported an error for the launch */
+} w4a4_status_t;
+
+typedef enum {
+  W4A4_Y_F32 = 0,    /* fp32 output */
+  W4A4_Y_F16 = 1     /* fp16 output, round to nearest even from the fp32 result */
+} w4a4_ydtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* w4a4_status_str(int status);
+
+/*
+ * Symmetric INT4 quantization of activations, per row, in groups of `group`
+ * consecutive K elements (APEX4 abstract: W4A4-g128, activations quantized to
+ * 4 bits per group of 128; other group sizes serve its mixed-granularity mode).
+ * Per group: a = max|x|; s = fl32(a / 7); q = clamp(rne(fl32(x / s)), -8, 7)
+ * with correctly rounded binary32 divisions; an all-zero group gives s = 0 and
+ * codes 0. (The pages give no formula: this is the plain symmetric reading.)
+ *
+ *   x     fp16 [M][ldx] row-major, 16-byte aligned, ldx >= K, ldx % 8 == 0
+ *   M, K  K > 0, K % 8 == 0 (K % group == 0 required as well)
+ *   group 64, 128, 256, 512, or group == K ("per token")
+ *   xq    out: u8 [M][K/2] packed codes (layout above), 4-byte aligned
+ *   xs    out: f32 [M][K/group] scales, 4-byte aligned
+ */
+w4a4_status_t w4a4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group,
+                                uint8_t* xq, float* xs, void* stream);
+
+/*
+ * Offline weight quantization (APEX4 abstract: 4-bit weights, "W4"): the same
+ * rule as w4a4_quantize_act applied to the rows of W[N][K] (ldw = K).
+ *
+ *   w     fp16 [N][K], 16-byte aligned
+ *   wq    out: u8 [N][K/2];  ws  out: f32 [N][K/group]
+ */
+w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t group,
+                               uint8_t* wq, float* ws, void* stream);
+
+/*
+ * W4A4 group-dequantized GEMM (APEX4 abstract: pure INT4 matrix products, with
+ * the per-group dequantization -- the vector-unit bottleneck it studies -- folded
+ * into the accumulation). With g = min(group_a, group_w):
+ *   P_b[m,n] = sum_{k in block b of g} qa[m,k] * qw[n,k]          (exact int32)
+ *   Y[m,n]   = sum_b s_a[m, b*g/group_a] * s_w[n, b*g/group_w] * P_b[m,n]  (fp32)
+ *
+ *   xq, xs          packed activation codes [M][K/2] and scales [M][K/group_a]
+ *   wq, ws          packed weight codes [N][K/2] and scales [N][K/group_w]
+ *   group_a/group_w each a multiple of 64 dividing K (64, 128, 256, 512, ..., K);
+ *                   the larger must be a multiple of the smaller
+ *   M, N, K         M, N >= 0; K > 0 and K % 128 == 0
+ *   y               out: [M][ldy] fp32 or fp16 (y_dtype), ldy >= N,
+ *                   aligned to its element size
+ *   xq, wq 16-byte aligned; xs, ws 4-byte aligned.
+ */
+w4a4_status_t w4a4_gemm(const uint8_t* xq, const float* xs, int32_t group_a,
+                        const uint8_t* wq, const float* ws, int32_t group_w,
+                        int64_t M, int64_t N, int64_t K,
+                        void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * Debug export of the integer group partials P_b of w4a4_gemm, computed by the
+ * same load / unpack / matrix-core code, for the output window
+ * [m0, m0+mc) x [n0, n0+nc):
+ *   partials  out: int32 [K/g][mc][nc], g = min(group_a, group_w)
+ * The window must lie inside [0,M) x [0,N); mc, nc > 0.
+ */
+w4a4_status_t w4a4_gemm_debug_partials(const uint8_t* xq, const float* xs, int32_t group_a,
+                                       const uint8_t* wq, const float* ws, int32_t group_w,
+                                       int64_t M, int64_t N, int64_t K,
+                                       int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                                       int32_t* partials, void* stream);
+
+/*
+ * MXFP4 quantization of the rows of X (OCP MX v1.0 rule; the pages name the
+ * format only): per block of 32 K elements, E = floor(log2(max|x|)) - 2
+ * (E = -127 for an all-zero block), scale byte E + 127, element codes =
+ * E2M1(x / 2^E) rounded to nearest, ties to even, saturating at 6, sign kept.
+ *
+ *   x     fp16 [rows][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0; K % 32 == 0
+ *   q     out: u8 [rows][K/2] packed E2M1 codes, 4-byte aligned
+ *   e8m0  out: u8 [rows][K/32] scale bytes
+ * Used for activations online and for weights offline.
+ */
+w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                             uint8_t* q, uint8_t* e8m0, void* stream);
+
+/*
+ * MXFP4 GEMM on the matrix cores' block-scaled FP4 path:
+ *   Y[m,n] = sum_b 2^(Ea[m,b] + Ew[n,b]) * sum_{k in block b} va[m,k] * vw[n,k]
+ * accumulated in fp32.
+ *
+ *   xq, xe   activation codes [M][K/2], scale bytes [M][K/32]
+ *   wq, we   weight codes [N][K/2], scale bytes [N][K/32]
+ *   K > 0, K % 128 == 0; y as for w4a4_gemm. xq, wq 16-byte aligned.
+ */
+w4a4_status_t mxfp4_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
+                         int64_t M, int64_t N, int64_t K,
+                         void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * Debug export of the exact per-block integers I_b = sum_{k in b} (2 va)(2 vw)
+ * of mxfp4_gemm, from the same matrix-core instruction run one 32-block at a
+ * time with unit scales, for the window [m0, m0+mc) x [n0, n0+nc):
+ *   partials  out: int32 [K/32][mc][nc]
+ */
+w4a4_status_t mxfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xe,
+                                        const uint8_t* wq, const uint8_t* we,
+                                        int64_t M, int64_t N, int64_t K,
+                                        int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                                        int32_t* partials, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

@@ -1,0 +1,128 @@
+"""The C ABI (CPU only): libw4a4.so loads, exports every function that
+include/w4a4.h declares with the argument count the binding uses, and rejects
+bad arguments with the documented status before touching the GPU.
+
+The validation calls below return before any HIP call, so they run without a
+GPU. Pointers passed are fake but never dereferenced on those paths.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a4_quantized_gemm_quantize_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4.h")
+
+OK, E_NULL, E_SHAPE, E_GROUP, E_ALIGN, E_DTYPE = 0, 1, 2, 3, 4, 5
+P = 0x10000          # a fake, 64 KiB-aligned "device pointer"
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(([^;]*?)\)\s*;", text, flags=re.M | re.S):
+        name, args = m.group(1), m.group(2)
+        out[name] = 0 if args.strip() in ("", "void") else args.count(",") + 1
+    return out
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libw4a4.so is not built (python -m w4a4_quantized_gemm_quantize_amd.build)")
+    return _lib.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decls = header_functions()
+    assert set(decls) >= set(_lib.SIGNATURES) | {"w4a4_status_str"}
+    for name, nargs in decls.items():
+        assert hasattr(lib, name), name
+        if name in _lib.SIGNATURES:
+            assert len(_lib.SIGNATURES[name]) == nargs, name
+
+
+def test_status_strings(lib):
+    for st in range(7):
+        s = lib.w4a4_status_str(st)
+        assert s and s != b"unknown status"
+    assert lib.w4a4_status_str(99) == b"unknown status"
+
+
+def q(*a):
+    return _lib.status_of("w4a4_quantize_act", *a)
+
+
+def test_quantize_act_validation(lib):
+    M, K = 4, 256
+    assert q(P, -1, K, K, 128, P, P, None) == E_SHAPE
+    assert q(P, M, 0, K, 128, P, P, None) == E_SHAPE
+    assert q(P, M, 260, 264, 128, P, P, None) == E_SHAPE      # K % 8 != 0 ... 260 % 8 = 4
+    assert q(P, M, K, K - 8, 128, P, P, None) == E_SHAPE     # ldx < K
+    assert q(P, M, K, K, 96, P, P, None) == E_GROUP
+    assert q(P, M, K, K, 512, P, P, None) == E_GROUP         # 512 does not divide 256
+    assert q(P, M, 384, 384, 256, P, P, None) == E_GROUP
+    assert q(P, M, K, K + 4, 128, P, P, None) == E_ALIGN     # ldx % 8
+    assert q(P, 0, K, K, 128, None, None, None) == OK        # empty: no-op
+    assert q(None, M, K, K, 128, P, P, None) == E_NULL
+    assert q(P, M, K, K, 128, None, P, None) == E_NULL
+    assert q(P + 8, M, K, K, 128, P, P, None) == E_ALIGN
+    assert q(P, M, K, K, 128, P + 2, P, None) == E_ALIGN
+    assert _lib.status_of("w4a4_pack_weight", P, M, K, 100, P, P, None) == E_GROUP
+    assert _lib.status_of("w4a4_pack_weight", None, M, K, 128, P, P, None) == E_NULL
+
+
+def g(*a):
+    return _lib.status_of("w4a4_gemm", *a)
+
+
+def test_gemm_validation(lib):
+    M, N, K = 16, 32, 256
+    assert g(P, P, 128, P, P, 128, M, N, 200, P, 0, N, None) == E_SHAPE       # K % 128
+    assert g(P, P, 128, P, P, 128, -1, N, K, P, 0, N, None) == E_SHAPE
+    assert g(P, P, 96, P, P, 128, M, N, K, P, 0, N, None) == E_GROUP
+    assert g(P, P, 128, P, P, 192, M, N, 384, P, 0, N, None) == E_GROUP       # not nested
+    assert g(P, P, 512, P, P, 128, M, N, K, P, 0, N, None) == E_GROUP         # 512 !| 256
+    assert g(P, P, 128, P, P, 128, 0, N, K, None, 0, N, None) == OK           # empty
+    assert g(P, P, 128, P, P, 128, M, 0, K, None, 0, 0, None) == OK
+    assert g(None, P, 128, P, P, 128, M, N, K, P, 0, N, None) == E_NULL
+    assert g(P, P, 128, P, None, 128, M, N, K, P, 0, N, None) == E_NULL
+    assert g(P + 4, P, 128, P, P, 128, M, N, K, P, 0, N, None) == E_ALIGN
+    assert g(P, P + 1, 128, P, P, 128, M, N, K, P, 0, N, None) == E_ALIGN
+    assert g(P, P, 128, P, P, 128, M, N, K, P, 7, N, None) == E_DTYPE
+    assert g(P, P, 128, P, P, 128, M, N, K, P, 0, N - 1, None) == E_SHAPE     # ldy < N
+    assert g(P, P, 128, P, P, 128, M, N, K, None, 0, N, None) == E_NULL
+    assert g(P, P, 128, P, P, 128, M, N, K, P + 2, 0, N, None) == E_ALIGN     # f32 y
+    dp = lambda *a: _lib.status_of("w4a4_gemm_debug_partials", *a)
+    assert dp(P, P, 128, P, P, 128, M, N, K, 0, M + 1, 0, N, P, None) == E_SHAPE
+    assert dp(P, P, 128, P, P, 128, M, N, K, 5, 0, 0, N, P, None) == E_SHAPE
+    assert dp(P, P, 128, P, P, 128, M, N, K, 0, M, -1, 4, P, None) == E_SHAPE
+    assert dp(P, P, 128, P, P, 128, M, N, K, 0, M, 0, N, None, None) == E_NULL
+
+
+def test_mxfp4_validation(lib):
+    mq = lambda *a: _lib.status_of("mxfp4_quantize", *a)
+    assert mq(P, 4, 48, 48, P, P, None) == E_SHAPE
+    assert mq(P, 4, 64, 60, P, P, None) == E_SHAPE
+    assert mq(P, 4, 64, 68, P, P, None) == E_ALIGN
+    assert mq(P, 0, 64, 64, None, None, None) == OK
+    assert mq(None, 4, 64, 64, P, P, None) == E_NULL
+    mg = lambda *a: _lib.status_of("mxfp4_gemm", *a)
+    assert mg(P, P, P, P, 4, 4, 96, P, 0, 4, None) == E_SHAPE
+    assert mg(P, P, P, P, 4, 4, 128, P, 2, 4, None) == E_DTYPE
+    assert mg(P, P + 2, P, P, 4, 4, 128, P, 0, 4, None) == E_ALIGN
+    assert mg(P, P, P, None, 4, 4, 128, P, 0, 4, None) == E_NULL
+    assert mg(P, P, P, P, 0, 4, 128, None, 0, 4, None) == OK
+    mp = lambda *a: _lib.status_of("mxfp4_gemm_debug_partials", *a)
+    assert mp(P, P, P, P, 4, 4, 128, 0, 5, 0, 4, P, None) == E_SHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libw4a4.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load_library()

@@ -1,0 +1,160 @@
+"""GPU parity of the W4A4 GEMM against the oracle.
+
+Per-group int32 partials must match bit for bit (debug entry point, same
+load/unpack/MFMA code); Y must satisfy |Y_gpu - Y| <= 1e-5 * T + 1e-6 with
+T = sum_b |s_a s_w P_b|. Small cases span several tiles with ragged edges and
+are checked in full; the workload shapes run at full size in the production
+launch configuration and are checked on a seeded sample of outputs."""
+import numpy as np
+import pytest
+
+import oracle
+from w4a4_quantized_gemm_quantize_amd import synth
+from helpers import assert_y16_close, assert_y_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from w4a4_quantized_gemm_quantize_amd import ops as o
+    return o
+
+
+def run_case(M, N, K, ga, gw, seed=0, dist="t3", window=None, check_fp16=False):
+    import torch
+    x = synth.activations(M, K, dist=dist, seed=seed)
+    w = synth.weights(N, K, seed=seed)
+    o = ops()
+    xq, xs = o.w4a4_quantize_act(dev(x), ga)
+    wq, ws = o.w4a4_pack_weight(dev(w), gw)
+    y = o.w4a4_gemm(xq, xs, ga, wq, ws, gw)
+    qa, sa = oracle.int4_quantize(x, ga)
+    qw, sw = oracle.int4_quantize(w, gw)
+    Y, T = oracle.w4a4_gemm(qa, sa, ga, qw, sw, gw)
+    ratio = assert_y_close(host(y), Y, T, f"Y M={M} N={N} K={K} ga={ga} gw={gw}")
+    if check_fp16:
+        y16 = o.w4a4_gemm(xq, xs, ga, wq, ws, gw, out_dtype=torch.float16)
+        assert_y16_close(host(y16).astype(np.float64), Y, T, "Y fp16")
+    m0, mc, n0, nc = window if window else (0, M, 0, N)
+    part = host(o.w4a4_gemm_debug_partials(xq, xs, ga, wq, ws, gw, m0, mc, n0, nc))
+    g = min(ga, gw)
+    for b, P in oracle.w4a4_block_partials(qa[m0:m0 + mc], qw[n0:n0 + nc], g):
+        assert np.array_equal(part[b], P), f"partials differ in block {b}"
+    return ratio
+
+
+def test_tiny_config():
+    run_case(16, 256, 256, 128, 128, dist="normal", check_fp16=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (130, 200, 512), (300, 392, 1024), (257, 129, 384)])
+def test_ragged_shapes(M, N, K):
+    run_case(M, N, K, 128, 128, seed=M)
+
+
+@pytest.mark.parametrize("ga,gw", [(64, 128), (128, 64), (256, 128), (512, 128), (1024, 128), (128, 1024), (64, 64)])
+def test_mixed_granularity(ga, gw):
+    run_case(200, 160, 1024, ga, gw, seed=ga + gw, window=(60, 100, 20, 130))
+
+
+def test_fp16_output_and_strided_y():
+    import torch
+    M, N, K = 64, 96, 512
+    x = synth.activations(M, K, seed=3)
+    w = synth.weights(N, K, seed=3)
+    o = ops()
+    xq, xs = o.w4a4_quantize_act(dev(x), 128)
+    wq, ws = o.w4a4_pack_weight(dev(w), 128)
+    big = torch.full((M, N + 40), 7.0, dtype=torch.float32, device="cuda")
+    o.w4a4_gemm(xq, xs, 128, wq, ws, 128, out=big[:, :N])
+    Y, T = oracle.w4a4_gemm(*oracle.int4_quantize(x, 128), 128, *oracle.int4_quantize(w, 128), 128)
+    yb = host(big)
+    assert_y_close(yb[:, :N], Y, T, "strided y")
+    assert np.all(yb[:, N:] == 7.0), "wrote outside the output window"
+    y16 = o.w4a4_gemm(xq, xs, 128, wq, ws, 128, out_dtype=torch.float16)
+    assert_y16_close(host(y16).astype(np.float64), Y, T, "fp16")
+
+
+def test_empty_is_noop():
+    import torch
+    o = ops()
+    xq = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
+    xs = torch.zeros((0, 2), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((8, 2), dtype=torch.float32, device="cuda")
+    y = o.w4a4_gemm(xq, xs, 128, wq, ws, 128)
+    assert y.shape == (0, 8)
+
+
+def test_zero_scales_give_zero():
+    M, N, K = 40, 72, 256
+    x = np.zeros((M, K), np.float16)
+    x[::3, :128] = 1.5
+    w = synth.weights(N, K, seed=1)
+    o = ops()
+    xq, xs = o.w4a4_quantize_act(dev(x), 128)
+    wq, ws = o.w4a4_pack_weight(dev(w), 128)
+    y = host(o.w4a4_gemm(xq, xs, 128, wq, ws, 128))
+    Y, T = oracle.w4a4_gemm(*oracle.int4_quantize(x, 128), 128, *oracle.int4_quantize(w, 128), 128)
+    assert_y_close(y, Y, T, "zero groups")
+    assert np.all(y[1::3] == 0)
+
+
+# --------------------------------------------------------------- full size
+_cache = {}
+
+
+def _weights_dev(N, K, gw):
+    key = ("w", N, K, gw)
+    if key not in _cache:
+        _cache.clear()
+        w = synth.weights(N, K, seed=0)
+        wq, ws = ops().w4a4_pack_weight(dev(w), gw)
+        _cache[key] = (wq, ws)
+    return _cache[key]
+
+
+def sampled_case(M, N, K, ga, gw, n_rows=8, n_cols=384, window=16):
+    o = ops()
+    wq, ws = _weights_dev(N, K, gw)
+    x = synth.activations(M, K, dist="t3", seed=0)
+    xq, xs = o.w4a4_quantize_act(dev(x), ga)
+    y = o.w4a4_gemm(xq, xs, ga, wq, ws, gw)
+    rows = synth.sample_rows(M, n_rows, seed=2)
+    cols = synth.sample_rows(N, n_cols, seed=3)
+    qa, sa = oracle.int4_quantize(x[rows], ga)
+    qw, sw = oracle.int4_quantize(synth.weights(N, K, seed=0, rows=cols), gw)
+    Y, T = oracle.w4a4_gemm(qa, sa, ga, qw, sw, gw)
+    yh = host(y)
+    ratio = assert_y_close(yh[np.ix_(rows, cols)], Y, T, f"M={M} N={N} K={K} ga={ga}")
+    # bit-exact partials on a window that straddles a tile corner
+    m0 = max(0, min(M - window, M // 2 - window // 2))
+    mc = min(window, M)
+    n0, nc = N // 2 - window // 2, window
+    part = host(o.w4a4_gemm_debug_partials(xq, xs, ga, wq, ws, gw, m0, mc, n0, nc))
+    qa2, _ = oracle.int4_quantize(x[m0:m0 + mc], ga)
+    qw2, _ = oracle.int4_quantize(synth.weights(N, K, seed=0, rows=np.arange(n0, n0 + nc)), gw)
+    for b, P in oracle.w4a4_block_partials(qa2, qw2, min(ga, gw)):
+        assert np.array_equal(part[b], P), f"partials block {b}"
+    return ratio
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_w13", "llama2_7b_w2"])
+def test_llama7b_shapes(name):
+    wl = synth.WORKLOADS[name]
+    sampled_case(wl["M"], wl["N"], wl["K"], 128, 128)
+
+
+@pytest.mark.parametrize("M", [1, 16, 256, 4096])
+def test_llama70b_w13(M):
+    sampled_case(M, 28672, 8192, 128, 128)
+
+
+@pytest.mark.parametrize("M", [1, 16, 256, 4096])
+def test_llama70b_w2(M):
+    sampled_case(M, 8192, 28672, 128, 128)
+
+
+@pytest.mark.parametrize("ga", [64, 128, 256, 512, 8192])
+def test_granularity_sweep(ga):
+    sampled_case(4096, 8192, 8192, ga, 128)

@@ -1,0 +1,133 @@
+"""GPU parity of the quantization kernels against the oracle: codes and scales
+must match bit for bit (INT4 and MXFP4), on the workload shapes, ragged and
+strided inputs, every supported group size, and exhaustive fp16 sweeps."""
+import numpy as np
+import pytest
+
+import oracle
+from w4a4_quantized_gemm_quantize_amd import synth
+from helpers import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from w4a4_quantized_gemm_quantize_amd import ops as o
+    return o
+
+
+def int4_check(x16, group, ldx_pad=0):
+    M, K = x16.shape
+    if ldx_pad:
+        buf = np.zeros((M, K + ldx_pad), np.float16)
+        buf[:, :K] = x16
+        xt = dev(buf)[:, :K]
+    else:
+        xt = dev(x16)
+    q, s = ops().w4a4_quantize_act(xt, group)
+    codes, scales = oracle.int4_quantize(x16, group)
+    assert np.array_equal(host(q), oracle.pack_nibbles(codes)), f"codes differ (M={M} K={K} g={group})"
+    gs = host(s)
+    assert np.array_equal(gs.view(np.uint32), scales.view(np.uint32)), f"scales differ (M={M} K={K} g={group})"
+
+
+def test_int4_tiny_config():
+    int4_check(synth.activations(16, 256, dist="normal", seed=0), 128)
+
+
+@pytest.mark.parametrize("group", [64, 128, 256, 512, "K"])
+def test_int4_groups_ragged_rows(group):
+    M, K = 37, 2048
+    g = K if group == "K" else group
+    int4_check(synth.activations(M, K, dist="t3", seed=1), g)
+
+
+def test_int4_strided_rows_and_per_token_long_rows():
+    int4_check(synth.activations(9, 1024, dist="t3", seed=2), 128, ldx_pad=64)
+    int4_check(synth.activations(5, 28672, dist="t3", seed=3), 28672)
+    int4_check(synth.activations(3, 1000, dist="t3", seed=3), 1000)     # per token, K % 128 != 0
+
+
+def test_int4_zero_rows_and_groups():
+    x = synth.activations(8, 512, dist="t3", seed=4)
+    x[2] = 0
+    x[5, 128:256] = 0
+    x[6, :] = np.float16(-0.0)
+    int4_check(x, 128)
+    int4_check(x, 512)
+
+
+def test_int4_exhaustive_fp16():
+    """Every finite fp16 value against 64 absmax anchors, groups of 128."""
+    rng = np.random.default_rng(0)
+    allf = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    allv = np.concatenate([allf, -allf[1:]])
+    anchors = np.concatenate([
+        np.array([65504, 1, 2.0 ** -24, 2.0 ** -14, 7, 0.5, 3.140625, 1000], np.float16),
+        rng.choice(allf[1:], 56)]).astype(np.float16)
+    rows = []
+    for a in anchors:
+        vals = allv[np.abs(allv.astype(np.float32)) <= np.float32(a)]
+        n = (vals.size + 126) // 127
+        pad = np.zeros(n * 127, np.float16)
+        pad[:vals.size] = vals
+        rows.append(np.concatenate([np.full((n, 1), a, np.float16), pad.reshape(n, 127)], axis=1))
+    x = np.concatenate(rows)                 # one group of 128 per row
+    n8 = x.shape[0] - x.shape[0] % 8         # 8 groups per 1024-wide row
+    int4_check(x[:n8].reshape(-1, 1024), 128)
+    if x.shape[0] > n8:
+        int4_check(x[n8:], 128)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_w13", "llama2_7b_w2", "llama2_70b_w13", "llama2_70b_w2"])
+def test_int4_workload_activations_sampled(name):
+    """Full-size activation quantization; bit-exact on a seeded row sample."""
+    wl = synth.WORKLOADS[name]
+    M, K = wl["M"], wl["K"]
+    x = synth.activations(M, K, dist=wl["dist"], seed=0)
+    q, s = ops().w4a4_quantize_act(dev(x), 128)
+    rows = synth.sample_rows(M, 64, seed=1)
+    codes, scales = oracle.int4_quantize(x[rows], 128)
+    assert np.array_equal(host(q)[rows], oracle.pack_nibbles(codes))
+    assert np.array_equal(host(s)[rows].view(np.uint32), scales.view(np.uint32))
+
+
+# ------------------------------------------------------------------ MXFP4
+def mx_check(x16, ldx_pad=0):
+    R, K = x16.shape
+    if ldx_pad:
+        buf = np.zeros((R, K + ldx_pad), np.float16)
+        buf[:, :K] = x16
+        xt = dev(buf)[:, :K]
+    else:
+        xt = dev(x16)
+    q, e = ops().mxfp4_quantize(xt)
+    codes, e8 = oracle.mxfp4_quantize(x16)
+    assert np.array_equal(host(e), e8), f"E8M0 differ (R={R} K={K})"
+    gq = host(q)
+    want = oracle.pack_nibbles(codes)
+    bad = np.argwhere(gq != want)
+    assert bad.size == 0, f"codes differ at {bad[:5].tolist()} (R={R} K={K})"
+
+
+def test_mxfp4_exhaustive_fp16():
+    rng = np.random.default_rng(1)
+    allf = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    allv = np.concatenate([allf, -allf])
+    perm = rng.permutation(allv)
+    perm = np.concatenate([perm, np.zeros((-perm.size) % 31, np.float16)])
+    blocks = perm.reshape(-1, 31)
+    anchors = np.abs(blocks.astype(np.float32)).max(axis=1) * rng.choice([1, 1.5, 3, 1000], size=blocks.shape[0])
+    anchors = np.clip(anchors, 0, 65504).astype(np.float16)
+    x = np.concatenate([anchors[:, None], blocks], axis=1).reshape(-1)
+    x = np.concatenate([x, np.zeros((-x.size) % 1024, np.float16)]).reshape(-1, 1024)
+    mx_check(x)
+
+
+def test_mxfp4_shapes():
+    mx_check(synth.activations(16, 256, dist="normal", seed=0))
+    mx_check(synth.activations(33, 3584, dist="t3", seed=5), ldx_pad=32)
+    x = synth.activations(7, 18944, dist="t3", seed=6)
+    x[3, :64] = 0
+    mx_check(x)
+    mx_check(synth.weights(40, 3584, seed=7))

@@ -1,5 +1,18 @@
 """W4A4 group-quantized GEMM and MXFP4 GEMM for MI355X (gfx950).
 
 The compute lives in ``libw4a4.so`` (hand-written HIP kernels behind a C ABI,
-declared in ``include/w4a4.h``). The Python side only marshals arguments.
+declared in ``include/w4a4.h``). The Python side only marshals arguments; the
+tensor-level entry points (same names as the C ABI) are in :mod:`.ops` and are
+re-exported here on first use.
 """
+_OPS = (
+    "w4a4_quantize_act", "w4a4_pack_weight", "w4a4_gemm", "w4a4_gemm_debug_partials",
+    "mxfp4_quantize", "mxfp4_gemm", "mxfp4_gemm_debug_partials",
+)
+
+
+def __getattr__(name):
+    if name in _OPS:
+        from . import ops
+        return getattr(ops, name)
+    raise AttributeError(name)

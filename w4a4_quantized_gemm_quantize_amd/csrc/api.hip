@@ -1,0 +1,181 @@
+// C ABI of libw4a4: argument validation, then one kernel launch per call.
+// The contract of each entry point is documented in include/w4a4.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "w4a4.h"
+
+using w4a4::GemmArgs;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+w4a4_status_t launched() {
+  return hipGetLastError() == hipSuccess ? W4A4_OK : W4A4_E_HIP;
+}
+
+// Quantizer groups: 64/128/256/512 or the whole row.
+bool quant_group_ok(int64_t K, int32_t group) {
+  if (group == K) return true;
+  if (group != 64 && group != 128 && group != 256 && group != 512) return false;
+  return K % group == 0;
+}
+
+// GEMM groups: multiples of 64 dividing K, nested.
+bool gemm_groups_ok(int64_t K, int32_t ga, int32_t gw) {
+  if (ga <= 0 || gw <= 0 || ga % 64 || gw % 64) return false;
+  if (K % ga || K % gw) return false;
+  const int32_t lo = ga < gw ? ga : gw, hi = ga < gw ? gw : ga;
+  return hi % lo == 0;
+}
+
+w4a4_status_t check_y(void* y, int32_t ydt, int64_t N, int64_t ldy) {
+  if (ydt != W4A4_Y_F32 && ydt != W4A4_Y_F16) return W4A4_E_DTYPE;
+  if (ldy < N) return W4A4_E_SHAPE;
+  if (!y) return W4A4_E_NULL;
+  if (!aligned(y, ydt == W4A4_Y_F32 ? 4 : 2)) return W4A4_E_ALIGN;
+  return W4A4_OK;
+}
+
+w4a4_status_t check_window(int64_t M, int64_t N, int64_t m0, int64_t mc, int64_t n0, int64_t nc) {
+  if (mc <= 0 || nc <= 0 || m0 < 0 || n0 < 0 || m0 + mc > M || n0 + nc > N) return W4A4_E_SHAPE;
+  return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a4_status_str(int status) {
+  switch (status) {
+    case W4A4_OK: return "ok";
+    case W4A4_E_NULL: return "null pointer";
+    case W4A4_E_SHAPE: return "unsupported shape or leading dimension";
+    case W4A4_E_GROUP: return "unsupported or non-nesting group size";
+    case W4A4_E_ALIGN: return "misaligned pointer or leading dimension";
+    case W4A4_E_DTYPE: return "unknown output dtype";
+    case W4A4_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+w4a4_status_t w4a4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group,
+                                uint8_t* xq, float* xs, void* stream) {
+  if (M < 0 || K <= 0 || K % 8 || ldx < K) return W4A4_E_SHAPE;
+  if (!quant_group_ok(K, group)) return W4A4_E_GROUP;
+  if (ldx % 8) return W4A4_E_ALIGN;
+  if (M == 0) return W4A4_OK;
+  if (!x || !xq || !xs) return W4A4_E_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xs, 4)) return W4A4_E_ALIGN;
+  w4a4::launch_int4_quant(x, M, K, ldx, group, xq, xs, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t group,
+                               uint8_t* wq, float* ws, void* stream) {
+  return w4a4_quantize_act(w, N, K, K, group, wq, ws, stream);
+}
+
+static w4a4_status_t gemm_common(const uint8_t* xq, const float* xs, int32_t ga,
+                                 const uint8_t* wq, const float* ws, int32_t gw,
+                                 int64_t M, int64_t N, int64_t K, GemmArgs& g) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128) return W4A4_E_SHAPE;
+  if (!gemm_groups_ok(K, ga, gw)) return W4A4_E_GROUP;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !xs || !wq || !ws) return W4A4_E_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xs, 4) || !aligned(ws, 4)) return W4A4_E_ALIGN;
+  g.a = xq; g.sa = xs; g.w = wq; g.sw = ws;
+  g.ga = ga; g.gw = gw;
+  g.M = M; g.N = N; g.K = K;
+  return W4A4_OK;
+}
+
+w4a4_status_t w4a4_gemm(const uint8_t* xq, const float* xs, int32_t group_a,
+                        const uint8_t* wq, const float* ws, int32_t group_w,
+                        int64_t M, int64_t N, int64_t K,
+                        void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = gemm_common(xq, xs, group_a, wq, ws, group_w, M, N, K, g);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if ((st = check_y(y, y_dtype, N, ldy)) != W4A4_OK) return st;
+  g.y = y; g.ydtype = y_dtype; g.ldy = ldy;
+  g.m0 = 0; g.mc = M; g.n0 = 0; g.nc = N; g.partials = nullptr;
+  w4a4::launch_w4a4_gemm(g, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t w4a4_gemm_debug_partials(const uint8_t* xq, const float* xs, int32_t group_a,
+                                       const uint8_t* wq, const float* ws, int32_t group_w,
+                                       int64_t M, int64_t N, int64_t K,
+                                       int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                                       int32_t* partials, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = gemm_common(xq, xs, group_a, wq, ws, group_w, M, N, K, g);
+  if (st != W4A4_OK) return st;
+  if ((st = check_window(M, N, m0, mc, n0, nc)) != W4A4_OK) return st;
+  if (!partials) return W4A4_E_NULL;
+  if (!aligned(partials, 4)) return W4A4_E_ALIGN;
+  g.y = nullptr; g.ydtype = 0; g.ldy = 0;
+  g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc; g.partials = partials;
+  w4a4::launch_w4a4_gemm(g, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                             uint8_t* q, uint8_t* e8m0, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 || ldx < K) return W4A4_E_SHAPE;
+  if (ldx % 8) return W4A4_E_ALIGN;
+  if (rows == 0) return W4A4_OK;
+  if (!x || !q || !e8m0) return W4A4_E_NULL;
+  if (!aligned(x, 16) || !aligned(q, 4)) return W4A4_E_ALIGN;
+  w4a4::launch_mxfp4_quant(x, rows, K, ldx, q, e8m0, as_stream(stream));
+  return launched();
+}
+
+static w4a4_status_t mx_common(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
+                               int64_t M, int64_t N, int64_t K, GemmArgs& g) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128) return W4A4_E_SHAPE;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !xe || !wq || !we) return W4A4_E_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xe, 4) || !aligned(we, 4)) return W4A4_E_ALIGN;
+  g.a = xq; g.sa = xe; g.w = wq; g.sw = we;
+  g.ga = 32; g.gw = 32;
+  g.M = M; g.N = N; g.K = K;
+  return W4A4_OK;
+}
+
+w4a4_status_t mxfp4_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
+                         int64_t M, int64_t N, int64_t K,
+                         void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = mx_common(xq, xe, wq, we, M, N, K, g);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if ((st = check_y(y, y_dtype, N, ldy)) != W4A4_OK) return st;
+  g.y = y; g.ydtype = y_dtype; g.ldy = ldy;
+  g.m0 = 0; g.mc = M; g.n0 = 0; g.nc = N; g.partials = nullptr;
+  w4a4::launch_mxfp4_gemm(g, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t mxfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xe,
+                                        const uint8_t* wq, const uint8_t* we,
+                                        int64_t M, int64_t N, int64_t K,
+                                        int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                                        int32_t* partials, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = mx_common(xq, xe, wq, we, M, N, K, g);
+  if (st != W4A4_OK) return st;
+  if ((st = check_window(M, N, m0, mc, n0, nc)) != W4A4_OK) return st;
+  if (!partials) return W4A4_E_NULL;
+  if (!aligned(partials, 4)) return W4A4_E_ALIGN;
+  g.y = nullptr; g.ydtype = 0; g.ldy = 0;
+  g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc; g.partials = partials;
+  w4a4::launch_mxfp4_gemm(g, as_stream(stream));
+  return launched();
+}
+
+}  // extern "C"

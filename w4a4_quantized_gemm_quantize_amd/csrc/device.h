@@ -1,0 +1,49 @@
+// Device-side helpers shared by the gfx950 kernels of libw4a4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace w4a4 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// DPP-permuted copy of v (same-row lane exchange, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int DPP_QUAD_1032 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;   // lane i <-> 15-i within a row of 16
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within each half row
+
+// Max over aligned groups of LANES consecutive lanes (LANES in {4,8,16,32,64}).
+// Every lane of a group must be active; the result is in every lane.
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64, "lanes");
+  if constexpr (LANES >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
+  if constexpr (LANES >= 16) v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+  if constexpr (LANES >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if constexpr (LANES >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Eight fp16 values from one 16-byte load, widened exactly to fp32.
+__device__ __forceinline__ void halves_to_float8(uint4 raw, float f[8]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xFFFFu)));
+    f[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
+  }
+}
+
+}  // namespace w4a4

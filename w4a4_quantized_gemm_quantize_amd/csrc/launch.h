@@ -1,0 +1,35 @@
+// Internal launchers behind the C ABI. Arguments are validated by the caller
+// (api.hip); these only pick a kernel configuration and enqueue it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a4 {
+
+void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int group,
+                       uint8_t* q, float* s, hipStream_t stream);
+
+void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                        uint8_t* q, uint8_t* e8m0, hipStream_t stream);
+
+// Window [m0, m0+mc) x [n0, n0+nc); for the plain GEMM the window is the whole
+// output and partials == nullptr.
+struct GemmArgs {
+  const uint8_t* a;
+  const void* sa;      // float* (INT4) or uint8_t* (MXFP4)
+  const uint8_t* w;
+  const void* sw;
+  int ga, gw;          // INT4 group sizes (unused for MXFP4)
+  int64_t M, N, K;
+  void* y;
+  int ydtype;
+  int64_t ldy;
+  int64_t m0, mc, n0, nc;
+  int32_t* partials;
+};
+
+void launch_w4a4_gemm(const GemmArgs& a, hipStream_t stream);
+void launch_mxfp4_gemm(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace w4a4

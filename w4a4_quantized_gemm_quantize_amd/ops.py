@@ -1,0 +1,129 @@
+"""Tensor-level wrappers over the C ABI (same names as include/w4a4.h).
+
+Each wrapper checks dtypes/devices, allocates outputs with torch on the input's
+device and calls the library on torch's current stream. Nothing is computed
+here.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import Y_F16, Y_F32, call
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ydtype(dtype) -> int:
+    if dtype == torch.float32:
+        return Y_F32
+    if dtype == torch.float16:
+        return Y_F16
+    raise TypeError("output dtype must be torch.float32 or torch.float16")
+
+
+def w4a4_quantize_act(x: torch.Tensor, group: int = 128, out=None):
+    """INT4 group quantization of fp16 X[M, K] (row stride may exceed K).
+
+    Returns ``(xq uint8 [M, K/2], xs float32 [M, K/group])``.
+    """
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    if out is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        xs = torch.empty((M, max(K // max(group, 1), 0)), dtype=torch.float32, device=x.device)
+    else:
+        xq, xs = out
+    call("w4a4_quantize_act", x.data_ptr(), M, K, x.stride(0), group,
+         xq.data_ptr(), xs.data_ptr(), _stream(x))
+    return xq, xs
+
+
+def w4a4_pack_weight(w: torch.Tensor, group: int = 128, out=None):
+    """Offline INT4 group quantization of fp16 W[N, K] (contiguous)."""
+    _need(w, torch.float16, "w")
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    N, K = w.shape
+    if out is None:
+        wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+        ws = torch.empty((N, max(K // max(group, 1), 0)), dtype=torch.float32, device=w.device)
+    else:
+        wq, ws = out
+    call("w4a4_pack_weight", w.data_ptr(), N, K, group, wq.data_ptr(), ws.data_ptr(), _stream(w))
+    return wq, ws
+
+
+def w4a4_gemm(xq, xs, group_a: int, wq, ws, group_w: int, out_dtype=torch.float32, out=None):
+    """Y[M, N] = group-dequantized INT4 GEMM of packed X and W."""
+    for t, dt, n in ((xq, torch.uint8, "xq"), (wq, torch.uint8, "wq"),
+                     (xs, torch.float32, "xs"), (ws, torch.float32, "ws")):
+        _need(t, dt, n)
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("K of xq and wq differ")
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    call("w4a4_gemm", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(), group_w,
+         M, N, K, y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
+    return y
+
+
+def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int, mc: int, n0: int, nc: int):
+    """Exact int32 group partials P_b for the window; shape [K/g, mc, nc]."""
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = wq.shape[0]
+    g = min(group_a, group_w)
+    part = torch.empty((K // g, mc, nc), dtype=torch.int32, device=xq.device)
+    call("w4a4_gemm_debug_partials", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(),
+         group_w, M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
+    return part
+
+
+def mxfp4_quantize(x: torch.Tensor, out=None):
+    """MXFP4 quantization of fp16 X[rows, K]: ``(codes uint8 [rows, K/2], e8m0 uint8 [rows, K/32])``."""
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    R, K = x.shape
+    if out is None:
+        q = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+        e = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, e = out
+    call("mxfp4_quantize", x.data_ptr(), R, K, x.stride(0), q.data_ptr(), e.data_ptr(), _stream(x))
+    return q, e
+
+
+def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
+    """Y[M, N] = block-scaled FP4 GEMM of MXFP4 X and W."""
+    for t, n in ((xq, "xq"), (xe, "xe"), (wq, "wq"), (we, "we")):
+        _need(t, torch.uint8, n)
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("K of xq and wq differ")
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    call("mxfp4_gemm", xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(), M, N, K,
+         y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
+    return y
+
+
+def mxfp4_gemm_debug_partials(xq, xe, wq, we, m0: int, mc: int, n0: int, nc: int):
+    """Exact int32 block integers I_b = sum (2va)(2vw) for the window; [K/32, mc, nc]."""
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = wq.shape[0]
+    part = torch.empty((K // 32, mc, nc), dtype=torch.int32, device=xq.device)
+    call("mxfp4_gemm_debug_partials", xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(),
+         M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
+    return part

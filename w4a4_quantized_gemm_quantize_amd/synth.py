@@ -23,6 +23,9 @@ large shapes get their rows.
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
+
 import numpy as np
 
 FP16_MAX = 65504.0
@@ -55,6 +58,23 @@ def _to_fp16(a: np.ndarray) -> np.ndarray:
     return np.clip(a, -FP16_MAX, FP16_MAX).astype(np.float16)
 
 
+def _fill_rows(out: np.ndarray, row_ids: np.ndarray, make_row) -> None:
+    """out[i] = make_row(row_ids[i]); rows are independent, so large fills are
+    spread over a thread pool (numpy's generators release the GIL)."""
+    def fill(span):
+        for i in range(*span):
+            out[i] = make_row(row_ids[i])
+    n = row_ids.size
+    workers = min(16, os.cpu_count() or 1)
+    if n < 256 or workers == 1:
+        fill((0, n))
+        return
+    step = (n + workers * 4 - 1) // (workers * 4)
+    spans = [(a, min(a + step, n)) for a in range(0, n, step)]
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, spans))
+
+
 def activations(M: int, K: int, *, dist: str = "t3", seed: int = 0,
                 n_outliers: int | None = None, outlier_scale: float | None = None,
                 rows=None) -> np.ndarray:
@@ -78,13 +98,12 @@ def activations(M: int, K: int, *, dist: str = "t3", seed: int = 0,
     gain = np.ones(K, dtype=np.float64)
     gain[ch] = scale
     out = np.empty((row_ids.size, K), dtype=np.float16)
-    for i, r in enumerate(row_ids):
+
+    def make_row(r):
         g = _rng(seed, STREAM_X, r)
-        if dist == "normal":
-            v = g.standard_normal(K)
-        else:
-            v = 0.5 * g.standard_t(3, K)
-        out[i] = _to_fp16(v * gain)
+        v = g.standard_normal(K) if dist == "normal" else 0.5 * g.standard_t(3, K)
+        return _to_fp16(v * gain)
+    _fill_rows(out, row_ids, make_row)
     return out
 
 
@@ -94,8 +113,7 @@ def weights(N: int, K: int, *, std: float = 0.02, seed: int = 0, rows=None) -> n
     if row_ids.size and (row_ids.min() < 0 or row_ids.max() >= N):
         raise IndexError("row index out of range")
     out = np.empty((row_ids.size, K), dtype=np.float16)
-    for i, r in enumerate(row_ids):
-        out[i] = _to_fp16(_rng(seed, STREAM_W, r).normal(0.0, std, K))
+    _fill_rows(out, row_ids, lambda r: _to_fp16(_rng(seed, STREAM_W, r).normal(0.0, std, K)))
     return out
 
 

@@ -93,8 +93,9 @@ w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t grou
  *
  *   xq, xs          packed activation codes [M][K/2] and scales [M][K/group_a]
  *   wq, ws          packed weight codes [N][K/2] and scales [N][K/group_w]
- *   group_a/group_w each a multiple of 64 dividing K (64, 128, 256, 512, ..., K);
- *                   the larger must be a multiple of the smaller
+ *   group_a/group_w each a power of two >= 64 dividing K (64, 128, 256, 512, ...)
+ *                   or K itself (per token); the larger must be a multiple of
+ *                   the smaller
  *   M, N, K         M, N >= 0; K > 0 and K % 128 == 0
  *   y               out: [M][ldy] fp32 or fp16 (y_dtype), ldy >= N,
  *                   aligned to its element size

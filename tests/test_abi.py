@@ -85,7 +85,8 @@ def test_gemm_validation(lib):
     assert g(P, P, 128, P, P, 128, M, N, 200, P, 0, N, None) == E_SHAPE       # K % 128
     assert g(P, P, 128, P, P, 128, -1, N, K, P, 0, N, None) == E_SHAPE
     assert g(P, P, 96, P, P, 128, M, N, K, P, 0, N, None) == E_GROUP
-    assert g(P, P, 128, P, P, 192, M, N, 384, P, 0, N, None) == E_GROUP       # not nested
+    assert g(P, P, 128, P, P, 192, M, N, 384, P, 0, N, None) == E_GROUP       # 192 not a power of two
+    assert g(P, P, 256, P, P, 384, M, N, 768, P, 0, N, None) == E_GROUP       # not nested
     assert g(P, P, 512, P, P, 128, M, N, K, P, 0, N, None) == E_GROUP         # 512 !| 256
     assert g(P, P, 128, P, P, 128, 0, N, K, None, 0, N, None) == OK           # empty
     assert g(P, P, 128, P, P, 128, M, 0, K, None, 0, 0, None) == OK

@@ -131,3 +131,40 @@ def test_mxfp4_shapes():
     x[3, :64] = 0
     mx_check(x)
     mx_check(synth.weights(40, 3584, seed=7))
+
+
+def _anchor_groups(lo, hi):
+    """Groups [a, x_1..x_127] covering, for each anchor bit pattern i in [lo, hi),
+    every fp16 x with |x| <= a (a = the fp16 with bits i), zero-padded."""
+    parts = []
+    for i in range(lo, hi):
+        xs = np.concatenate([np.arange(0, i + 1, dtype=np.uint16),
+                             np.arange(1, i + 1, dtype=np.uint16) | np.uint16(0x8000)])
+        n = -(-xs.size // 127)
+        pad = np.zeros(n * 127, np.uint16)
+        pad[:xs.size] = xs
+        g = np.empty((n, 128), np.uint16)
+        g[:, 0] = i
+        g[:, 1:] = pad.reshape(n, 127)
+        parts.append(g)
+    g = np.concatenate(parts)
+    g = np.concatenate([g, np.zeros(((-g.shape[0]) % 8, 128), np.uint16)])
+    return g.reshape(-1, 1024).view(np.float16)
+
+
+def test_int4_exhaustive_every_absmax_x_pair():
+    """Every pair (a, x) of finite fp16 values with |x| <= a, a > 0: the scale
+    depends only on a and the code only on (x, scale), so this covers every
+    scale the quantizer can produce against every input it can see."""
+    top = 0x7C00                           # bit patterns 1 .. 0x7BFF are the positive finite fp16
+    bounds = [1]
+    acc = 0
+    for i in range(1, top):                # chunks of ~48M elements
+        acc += 2 * i + 1
+        if acc > 48_000_000:
+            bounds.append(i + 1)
+            acc = 0
+    bounds.append(top)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        x = _anchor_groups(lo, hi)
+        int4_check(x, 128)

@@ -25,10 +25,14 @@ bool quant_group_ok(int64_t K, int32_t group) {
   return K % group == 0;
 }
 
-// GEMM groups: multiples of 64 dividing K, nested.
+// GEMM groups: a power of two >= 64 dividing K, or K itself (per token); nested.
+bool gemm_group_ok(int64_t K, int32_t g) {
+  if (g == K) return true;
+  return g >= 64 && (g & (g - 1)) == 0 && K % g == 0;
+}
+
 bool gemm_groups_ok(int64_t K, int32_t ga, int32_t gw) {
-  if (ga <= 0 || gw <= 0 || ga % 64 || gw % 64) return false;
-  if (K % ga || K % gw) return false;
+  if (!gemm_group_ok(K, ga) || !gemm_group_ok(K, gw)) return false;
   const int32_t lo = ga < gw ? ga : gw, hi = ga < gw ? gw : ga;
   return hi % lo == 0;
 }

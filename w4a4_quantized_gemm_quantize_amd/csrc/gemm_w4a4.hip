@@ -4,30 +4,34 @@
 // Rebalancing", abstract): a pure INT4 GEMM on the matrix units, with the
 // per-group dequantization done by the vector units -- the cost it identifies
 // as the W4A4 bottleneck (its "rho", matrix-unit : vector-unit throughput).
-// gfx950 has no INT4 matrix instruction, so packed int4 tiles are staged in LDS
-// and widened in registers to int8 for v_mfma_i32_32x32x32_i8:
-//   * a packed dword holds 8 codes; (d << 4) & 0xF0F0F0F0 puts the even codes,
-//     and d & 0xF0F0F0F0 the odd codes, in the high nibble of each byte, i.e.
-//     int8 bytes equal to 16*q (two's complement is preserved). A and W are
-//     widened the same way, so every product carries a factor 256 that is
-//     folded exactly into the fp32 scale (a power of two) and the k order
-//     permutation is the same on both sides.
-//   * per block of g = min(group_a, group_w) k values the int32 result is
-//     256 * P_b; the epilogue does acc += float(P) * (s_a * s_w / 256) -- one
-//     convert, one multiply, one fma per output per group -- then clears P.
-//     That is the whole vector-unit cost per output per group; everything
-//     else (LDS reads, unpacking) is amortized over a 64 x 64 wave tile.
+// On gfx950 the vector unit does 64 fp32 lane-ops per clock per CU against
+// 4096 int8 MACs on the matrix cores (packed fp32 math is not used), so every
+// vector op per output per group matters. Design:
+//
+//   * gfx950 has no INT4 matrix instruction. Packed int4 tiles are fetched
+//     from HBM/L2 and widened ONCE per workgroup, by the threads that stage
+//     them, into int8 operands in LDS: for a packed dword d (8 codes),
+//     (d << 4) & 0xF0F0F0F0 puts the even codes and d & 0xF0F0F0F0 the odd
+//     codes in the high nibble of each byte, i.e. int8 bytes equal to 16*q
+//     (two's complement preserved). A and W are widened the same way, so each
+//     product carries a factor 256, folded exactly into the fp32 scale (a power
+//     of two), and the k permutation is the same on both sides.
+//   * The waves read MFMA-ready 16-byte operands from LDS and run
+//     v_mfma_i32_32x32x32_i8. A group's partial P_b (times 256) starts from an
+//     inline zero accumulator, so clearing it costs nothing.
+//   * Epilogue per output per group: acc += float(P) * (s_a * s_w / 256) --
+//     one convert, one multiply, one fma, the minimum for an int32 partial
+//     and two fp32 scales.
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; tile 128 x 128 outputs,
-// K stage 128 (64 packed bytes per row), double-buffered LDS (45 KB), two
-// workgroups per CU (2 waves per SIMD) so one wave's epilogue overlaps the
-// other's matrix work. Tiles are ordered XCD-contiguous, then in groups of 8
-// tile-rows, so workgroups running together on one XCD share A and W slices
-// in that XCD's L2.
+// K stage 128, double-buffered LDS (76 KB), two workgroups per CU (2 waves per
+// SIMD) so one wave's epilogue overlaps the other's matrix work. Tiles are
+// ordered XCD-contiguous, then in groups of 8 tile-rows, so workgroups running
+// together on one XCD share A and W slices in that XCD's L2.
 //
 // v_mfma_i32_32x32x32_i8 lane layout: A/B operand lane l holds row (col) l%32
-// and 16 consecutive k of chunk l/32; D element r of lane l is
-// row 8*(r/4) + 4*(l/32) + r%4, col l%32.
+// and 16 k of chunk l/32; D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+// col l%32.
 #include "device.h"
 #include "launch.h"
 
@@ -40,17 +44,21 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int ROW_BYTES = BK / 2;   // packed bytes per row per stage
-constexpr int PITCH = 80;           // LDS row pitch: +16 B keeps 16-byte reads conflict-free
+constexpr int PITCH = 144;          // LDS bytes per row: 128 int8 + 16 pad (conflict-free 16 B reads)
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;       // tile-rows per raster group
+
+// Group modes: epilogue after every 64-k half (g = 64), after every stage
+// (g = 128), or after several stages (g > 128).
+enum { G64 = 0, G128 = 1, GBIG = 2 };
 
 struct Params {
   const uint8_t* a;
   const float* sa;
   const uint8_t* w;
   const float* sw;
-  int ga64, gw64;             // group sizes in units of 64 k
-  int gmin;                   // min(ga, gw)
+  int sha, shw;               // scale column of 64-k half h = h >> sh (31: one column)
+  int stages_per_group;       // GBIG only
   int M, N, K;
   int ksa, ksw;               // scale columns per row (K / group)
   void* y;
@@ -62,12 +70,18 @@ struct Params {
   int32_t* partials;
 };
 
-__device__ __forceinline__ v4i widen_x16(uint32_t d0, uint32_t d1) {
-  return v4i{(int)((d0 << 4) & 0xF0F0F0F0u), (int)(d0 & 0xF0F0F0F0u),
-             (int)((d1 << 4) & 0xF0F0F0F0u), (int)(d1 & 0xF0F0F0F0u)};
+__device__ __forceinline__ uint32_t even16(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t odd16(uint32_t d) { return d & 0xF0F0F0F0u; }
+
+// 32 packed codes (16 B) -> two 16-byte int8 operand pieces in LDS.
+__device__ __forceinline__ void widen_store(uint8_t* dst, uint4 v) {
+  *reinterpret_cast<uint4*>(dst) = uint4{even16(v.x), odd16(v.x), even16(v.y), odd16(v.y)};
+  *reinterpret_cast<uint4*>(dst + 16) = uint4{even16(v.z), odd16(v.z), even16(v.w), odd16(v.w)};
 }
 
-template <bool PARTIALS>
+__device__ __forceinline__ v4i as_v4i(uint4 v) { return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
+
+template <bool PARTIALS, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_w4a4_gemm(Params p) {
   __shared__ __align__(16) uint8_t sA[2][BM * PITCH];
@@ -80,14 +94,12 @@ void k_w4a4_gemm(Params p) {
   int bid = blockIdx.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int per_group = kGroupRows * p.tiles_n;
-  const int g = bid / per_group;
-  const int first_m = g * kGroupRows;
+  const int grp = bid / per_group;
+  const int first_m = grp * kGroupRows;
   const int gsize = min(p.tiles_m - first_m, kGroupRows);
-  const int rem = bid - g * per_group;
-  const int tm = first_m + rem % gsize;
-  const int tn = rem / gsize;
-  const int tile_m = (p.tile_m0 + tm) * BM;
-  const int tile_n = (p.tile_n0 + tn) * BN;
+  const int rem = bid - grp * per_group;
+  const int tile_m = (p.tile_m0 + first_m + rem % gsize) * BM;
+  const int tile_n = (p.tile_n0 + rem / gsize) * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,71 +108,61 @@ void k_w4a4_gemm(Params p) {
   const int row_bytes = p.K >> 1;
   const int nk = p.K / BK;
 
-  // ---- global -> LDS staging: 2 x 16 B of A and of W per thread per stage
-  const uint8_t* gA[2];
-  const uint8_t* gW[2];
-  int ldsoff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + kThreads * i;
-    const int r = idx >> 2, seg = idx & 3;
-    gA[i] = p.a + (int64_t)min(tile_m + r, p.M - 1) * row_bytes + seg * 16;
-    gW[i] = p.w + (int64_t)min(tile_n + r, p.N - 1) * row_bytes + seg * 16;
-    ldsoff[i] = r * PITCH + seg * 16;
-  }
+  // ---- staging: each thread fetches 2 x 16 B of A and of W per stage
+  const uint8_t* gA0 = p.a + (int64_t)min(tile_m + (tid >> 2), p.M - 1) * row_bytes + (tid & 3) * 16;
+  const uint8_t* gA1 = p.a + (int64_t)min(tile_m + 64 + (tid >> 2), p.M - 1) * row_bytes + (tid & 3) * 16;
+  const uint8_t* gW0 = p.w + (int64_t)min(tile_n + (tid >> 2), p.N - 1) * row_bytes + (tid & 3) * 16;
+  const uint8_t* gW1 = p.w + (int64_t)min(tile_n + 64 + (tid >> 2), p.N - 1) * row_bytes + (tid & 3) * 16;
+  const int st0 = (tid >> 2) * PITCH + (tid & 3) * 32;
+  const int st1 = st0 + 64 * PITCH;
   // scales: threads 0..127 stage A-row scales, 128..255 W-row scales
   const bool s_is_a = tid < BM;
   const int srow = s_is_a ? tid : tid - BM;
   const float* gS = s_is_a ? p.sa + (int64_t)min(tile_m + srow, p.M - 1) * p.ksa
                            : p.sw + (int64_t)min(tile_n + srow, p.N - 1) * p.ksw;
-  const int s_g64 = s_is_a ? p.ga64 : p.gw64;
-  float* sS0 = s_is_a ? &sSA[0][0][srow] : &sSW[0][0][srow];   // [stage][half] stride BM
+  const int ssh = s_is_a ? p.sha : p.shw;
+  float* sS = s_is_a ? &sSA[0][0][srow] : &sSW[0][0][srow];
 
   uint4 ra0, ra1, rw0, rw1;
   float rs0, rs1;
-#define GLOAD(KT)                                                               \
-  {                                                                             \
-    const int off_ = (KT) * ROW_BYTES;                                          \
-    ra0 = *reinterpret_cast<const uint4*>(gA[0] + off_);                        \
-    ra1 = *reinterpret_cast<const uint4*>(gA[1] + off_);                        \
-    rw0 = *reinterpret_cast<const uint4*>(gW[0] + off_);                        \
-    rw1 = *reinterpret_cast<const uint4*>(gW[1] + off_);                        \
-    rs0 = gS[(unsigned)(2 * (KT)) / (unsigned)s_g64];                           \
-    rs1 = gS[(unsigned)(2 * (KT) + 1) / (unsigned)s_g64];                       \
+#define GLOAD(KT)                                                     \
+  {                                                                   \
+    const int off_ = (KT) * ROW_BYTES;                                \
+    ra0 = *reinterpret_cast<const uint4*>(gA0 + off_);                \
+    ra1 = *reinterpret_cast<const uint4*>(gA1 + off_);                \
+    rw0 = *reinterpret_cast<const uint4*>(gW0 + off_);                \
+    rw1 = *reinterpret_cast<const uint4*>(gW1 + off_);                \
+    rs0 = gS[(2 * (KT)) >> ssh];                                      \
+    rs1 = gS[(2 * (KT) + 1) >> ssh];                                  \
   }
-#define LSTORE(BUF)                                                             \
-  {                                                                             \
-    *reinterpret_cast<uint4*>(&sA[BUF][ldsoff[0]]) = ra0;                       \
-    *reinterpret_cast<uint4*>(&sA[BUF][ldsoff[1]]) = ra1;                       \
-    *reinterpret_cast<uint4*>(&sW[BUF][ldsoff[0]]) = rw0;                       \
-    *reinterpret_cast<uint4*>(&sW[BUF][ldsoff[1]]) = rw1;                       \
-    sS0[(BUF) * 2 * BM] = rs0;                                                  \
-    sS0[(BUF) * 2 * BM + BM] = rs1;                                             \
+#define LSTORE(BUF)                                                   \
+  {                                                                   \
+    widen_store(&sA[BUF][st0], ra0);                                  \
+    widen_store(&sA[BUF][st1], ra1);                                  \
+    widen_store(&sW[BUF][st0], rw0);                                  \
+    widen_store(&sW[BUF][st1], rw1);                                  \
+    sS[(BUF) * 2 * BM] = rs0;                                         \
+    sS[(BUF) * 2 * BM + BM] = rs1;                                    \
   }
 
   v16f acc[2][2];
   v16i P[2][2];
+  const v16i zero16 = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      P[i][j] = zero16;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[i][j][r] = 0.0f;
-        P[i][j][r] = 0;
-      }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     }
 
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-  // LDS read offsets (bytes) of this lane's operand rows, without the stage base
-  const int offA0 = (wm * 64 + l32) * PITCH + 16 * lhi;
-  const int offA1 = offA0 + 32 * PITCH;
-  const int offW0 = (wn * 64 + l32) * PITCH + 16 * lhi;
-  const int offW1 = offW0 + 32 * PITCH;
-  const int k_per_group = p.gmin / BK;    // stages per group when gmin >= 128
-  int gcount = 0;                         // stages since the last epilogue
-  int gidx = 0;                           // index of the next group to finish
+  const int rdA = (wm * 64 + l32) * PITCH + 16 * lhi;   // + i*32*PITCH + 32*s
+  const int rdW = (wn * 64 + l32) * PITCH + 16 * lhi;
+  int gcount = 0;     // GBIG: stages accumulated into P since the last epilogue
+  int gidx = 0;       // index of the next group to finish (partials export)
 
   GLOAD(0);
   LSTORE(0);
@@ -170,31 +172,30 @@ void k_w4a4_gemm(Params p) {
     const int buf = kt & 1;
     if (kt + 1 < nk) GLOAD(kt + 1);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][offA0 + 32 * s2]);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(&sA[buf][offA1 + 32 * s2]);
-      const uint4 w0 = *reinterpret_cast<const uint4*>(&sW[buf][offW0 + 32 * s2]);
-      const uint4 w1 = *reinterpret_cast<const uint4*>(&sW[buf][offW1 + 32 * s2]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const v4i av0 = u ? widen_x16(a0.z, a0.w) : widen_x16(a0.x, a0.y);
-        const v4i av1 = u ? widen_x16(a1.z, a1.w) : widen_x16(a1.x, a1.y);
-        const v4i wv0 = u ? widen_x16(w0.z, w0.w) : widen_x16(w0.x, w0.y);
-        const v4i wv1 = u ? widen_x16(w1.z, w1.w) : widen_x16(w1.x, w1.y);
-        P[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av0, wv0, P[0][0], 0, 0, 0);
-        P[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av0, wv1, P[0][1], 0, 0, 0);
-        P[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av1, wv0, P[1][0], 0, 0, 0);
-        P[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av1, wv1, P[1][1], 0, 0, 0);
-      }
-      // A group ends after this 64-k half when gmin == 64, or after the
-      // whole stage when the stage completes a group of gmin >= 128.
-      bool flush;
-      if (p.gmin == 64) {
-        flush = true;
+    for (int s = 0; s < 4; ++s) {
+      const v4i a0 = as_v4i(*reinterpret_cast<const uint4*>(&sA[buf][rdA + 32 * s]));
+      const v4i a1 = as_v4i(*reinterpret_cast<const uint4*>(&sA[buf][rdA + 32 * PITCH + 32 * s]));
+      const v4i w0 = as_v4i(*reinterpret_cast<const uint4*>(&sW[buf][rdW + 32 * s]));
+      const v4i w1 = as_v4i(*reinterpret_cast<const uint4*>(&sW[buf][rdW + 32 * PITCH + 32 * s]));
+      // first k-step of a group starts from an inline zero accumulator
+      const bool fresh = (MODE == G64) ? (s == 0 || s == 2) : (MODE == G128) ? (s == 0) : false;
+      if (fresh) {
+        P[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w0, zero16, 0, 0, 0);
+        P[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w1, zero16, 0, 0, 0);
+        P[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w0, zero16, 0, 0, 0);
+        P[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w1, zero16, 0, 0, 0);
       } else {
-        flush = (s2 == 1) && (gcount + 1 == k_per_group);
+        P[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w0, P[0][0], 0, 0, 0);
+        P[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w1, P[0][1], 0, 0, 0);
+        P[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w0, P[1][0], 0, 0, 0);
+        P[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w1, P[1][1], 0, 0, 0);
       }
+      bool flush;
+      if (MODE == G64) flush = (s == 1 || s == 3);
+      else if (MODE == G128) flush = (s == 3);
+      else flush = (s == 3) && (gcount + 1 == p.stages_per_group);
       if (flush) {
+        const int h = s >> 1;   // 64-k half whose scales apply
         if constexpr (PARTIALS) {
 #pragma unroll
           for (int i = 0; i < 2; ++i)
@@ -208,8 +209,8 @@ void k_w4a4_gemm(Params p) {
                   p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = P[i][j][r] >> 8;
               }
         } else {
-          const float* sa_h = &sSA[buf][s2][wm * 64 + 4 * lhi];
-          const float* sw_h = &sSW[buf][s2][wn * 64 + l32];
+          const float* sa_h = &sSA[buf][h][wm * 64 + 4 * lhi];
+          const float* sw_h = &sSW[buf][h][wn * 64 + l32];
           const float swj0 = sw_h[0] * (1.0f / 256.0f);
           const float swj1 = sw_h[32] * (1.0f / 256.0f);
 #pragma unroll
@@ -227,16 +228,16 @@ void k_w4a4_gemm(Params p) {
             }
           }
         }
+        if (MODE == GBIG) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) P[i][j][r] = 0;
+            for (int j = 0; j < 2; ++j) P[i][j] = zero16;
+        }
         ++gidx;
       }
     }
-    if (p.gmin != 64) gcount = (gcount + 1 == k_per_group) ? 0 : gcount + 1;
+    if (MODE == GBIG) gcount = (gcount + 1 == p.stages_per_group) ? 0 : gcount + 1;
     if (kt + 1 < nk) LSTORE(buf ^ 1);
     __syncthreads();
   }
@@ -262,6 +263,23 @@ void k_w4a4_gemm(Params p) {
   }
 }
 
+// log2(group / 64) for a power-of-two group, 31 (a single column) for group == K.
+int scale_shift(int64_t group, int64_t K) {
+  if (group == K && (group & (group - 1))) return 31;
+  int s = 0;
+  while ((64LL << s) < group) ++s;
+  return s;
+}
+
+template <bool PARTIALS>
+void launch_mode(int mode, const Params& p, dim3 grid, hipStream_t stream) {
+  switch (mode) {
+    case G64: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G64>), grid, dim3(kThreads), 0, stream, p); return;
+    case G128: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G128>), grid, dim3(kThreads), 0, stream, p); return;
+    default: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, GBIG>), grid, dim3(kThreads), 0, stream, p); return;
+  }
+}
+
 }  // namespace
 
 void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
@@ -270,9 +288,11 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.sa = static_cast<const float*>(g.sa);
   p.w = g.w;
   p.sw = static_cast<const float*>(g.sw);
-  p.ga64 = g.ga / 64;
-  p.gw64 = g.gw / 64;
-  p.gmin = g.ga < g.gw ? g.ga : g.gw;
+  p.sha = scale_shift(g.ga, g.K);
+  p.shw = scale_shift(g.gw, g.K);
+  const int64_t gmin = g.ga < g.gw ? g.ga : g.gw;
+  const int mode = gmin == 64 ? G64 : gmin == 128 ? G128 : GBIG;
+  p.stages_per_group = (int)(gmin / BK);
   p.M = (int)g.M;
   p.N = (int)g.N;
   p.K = (int)g.K;
@@ -292,9 +312,9 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   if (g.partials)
-    hipLaunchKernelGGL(k_w4a4_gemm<true>, grid, dim3(kThreads), 0, stream, p);
+    launch_mode<true>(mode, p, grid, stream);
   else
-    hipLaunchKernelGGL(k_w4a4_gemm<false>, grid, dim3(kThreads), 0, stream, p);
+    launch_mode<false>(mode, p, grid, stream);
 }
 
 }  // namespace w4a4

@@ -8,9 +8,21 @@
 // rule): per 32 elements E = floor(log2 a) - 2, codes = E2M1(x / 2^E) with
 // ties to even and saturation at 6, E8M0 byte E + 127.
 //
-// Both kernels are HBM-bound streams: each lane loads 8 fp16 (one 128-bit load),
-// a group's absmax is reduced across the lanes that hold it with DPP row
-// permutes (no LDS), and each lane writes its 8 codes as one 32-bit store.
+// Both kernels stream HBM: each lane loads 8 fp16 (one 128-bit load) per row
+// it covers, a group's absmax is reduced across the lanes that hold it with DPP
+// row permutes (no LDS), and each lane writes its 8 codes as one 32-bit store.
+// The grid is 2-D (chunk column x row block), so no lane divides to find its row.
+//
+// Vector-ALU economy for the INT4 rule (the stream must not become ALU-bound):
+//   * x / s is computed as q0 = x*r, e = fma(-q0, s, x), q1 = fma(e, r, q0) with
+//     r = RN(1/s) computed once per group; with r correctly rounded and q0 within
+//     an ulp this Markstein-style correction yields RN(x/s) (P. Markstein, IBM
+//     J. Res. Dev. 34(1), 1990). The GPU parity tests check it against the
+//     oracle's IEEE divisions over every (absmax, x) pair of fp16 values.
+//   * s = RN(a/7) the same way with r7 = RN(1/7).
+//   * rne + clamp: t is clamped to [-8, 7] and 2^23 + 8 is added; binary32
+//     spacing is 1 on [2^23, 2^24), so the add rounds half-to-even and the low
+//     4 bits hold q + 8; XOR 8 turns that into the two's complement nibble.
 #include "device.h"
 #include "launch.h"
 
@@ -19,53 +31,91 @@ namespace w4a4 {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kChunksPerThread = 4;  // independent 16-byte loads in flight per lane
+constexpr int kRowsPerThread = 4;   // independent 16-byte loads in flight per lane
+constexpr float kMagic = 8388616.0f;    // 2^23 + 8
 
-// Quantize 8 values with scale s (s > 0) or to zero (s == 0); pack 8 nibbles.
-__device__ __forceinline__ uint32_t int4_codes8(const float f[8], float s) {
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float t = f[i] / s;                       // correctly rounded binary32 division
-    float r = fminf(fmaxf(rintf(t), -8.0f), 7.0f);
-    int q = (s == 0.0f) ? 0 : (int)r;
-    word |= (uint32_t)(q & 0xF) << (4 * i);
-  }
-  return word;
+// Correctly rounded x / d given r = RN(1/d) (d normal, no overflow/underflow).
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+  const float q0 = x * r;
+  const float e = fmaf(-q0, d, x);
+  return fmaf(e, r, q0);
 }
 
-// One group of G elements spans G/8 consecutive lanes.
+// (q + 8) in the low 4 bits of the returned word, q = clamp(rne(t), -8, 7).
+__device__ __forceinline__ uint32_t biased_code(float t) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(t, -8.0f, 7.0f) + kMagic);
+}
+
+// 8 biased codes -> one packed dword of two's complement nibbles (low nibble first).
+__device__ __forceinline__ uint32_t pack8(const uint32_t u[8]) {
+  const uint32_t p01 = (u[1] << 4) | (u[0] & 0xFFu);
+  const uint32_t p23 = (u[3] << 4) | (u[2] & 0xFFu);
+  const uint32_t p45 = (u[5] << 4) | (u[4] & 0xFFu);
+  const uint32_t p67 = (u[7] << 4) | (u[6] & 0xFFu);
+  const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);   // [p01.b0, p23.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p67, p45, 0x04000C0Cu);   // [0, 0, p45.b0, p67.b0]
+  return lo ^ hi ^ 0x88888888u;
+}
+
+// Group scale and its reciprocal (r = 0 for an all-zero group so every code is 0).
+__device__ __forceinline__ void group_scale(float a, float& s, float& r) {
+  constexpr float r7 = 1.0f / 7.0f;      // RN(1/7), folded at compile time
+  s = div_rn(a, 7.0f, r7);
+  r = (s == 0.0f) ? 0.0f : 1.0f / s;     // correctly rounded division
+}
+
+__device__ __forceinline__ uint32_t int4_codes8(const float f[8], float s, float r) {
+  uint32_t u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = biased_code(div_rn(f[i], s, r));
+  return pack8(u);
+}
+
+// Lane mapping of the 2-D grid: a block is kQuantThreads lanes = (256 / W) row
+// slots x W chunk columns, W in {64, 128, 256}; each lane covers kRowsPerThread
+// rows spaced (256 / W) apart.
+struct Map {
+  int col;       // 8-element chunk index within the row
+  int row0;      // first row
+  int rstep;     // row spacing between a lane's rows
+};
+
+__device__ __forceinline__ Map lane_map(int wshift) {
+  const int W = 1 << wshift;
+  Map m;
+  m.col = blockIdx.x * W + (threadIdx.x & (W - 1));
+  m.rstep = kQuantThreads >> wshift;
+  m.row0 = blockIdx.y * m.rstep * kRowsPerThread + (threadIdx.x >> wshift);
+  return m;
+}
+
+// One group of G elements spans G/8 consecutive lanes of one row.
 template <int G>
 __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t M, int64_t K,
+    const uint16_t* __restrict__ x, int64_t ldx, int M, int cpr, int wshift,
     uint32_t* __restrict__ q, float* __restrict__ s) {
   constexpr int LPG = G / 8;
-  const int64_t cpr = K / 8;                  // 8-element chunks per row
-  const int64_t total = M * cpr;
-  const int64_t base = (int64_t)blockIdx.x * (kQuantThreads * kChunksPerThread) + threadIdx.x;
-  uint4 raw[kChunksPerThread];
+  const Map mp = lane_map(wshift);
+  if (mp.col >= cpr) return;                  // whole lane groups drop out together
+  uint4 raw[kRowsPerThread];
 #pragma unroll
-  for (int u = 0; u < kChunksPerThread; ++u) {
-    const int64_t c = base + u * kQuantThreads;
-    if (c < total) {
-      const int64_t row = c / cpr, col = c - row * cpr;
-      raw[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col * 8);
-    }
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int row = mp.row0 + u * mp.rstep;
+    if (row < M) raw[u] = *reinterpret_cast<const uint4*>(x + row * ldx + mp.col * 8);
   }
 #pragma unroll
-  for (int u = 0; u < kChunksPerThread; ++u) {
-    const int64_t c = base + u * kQuantThreads;
-    if (c < total) {                          // uniform across each lane group
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int row = mp.row0 + u * mp.rstep;
+    if (row < M) {                            // uniform across each lane group
       float f[8];
       halves_to_float8(raw[u], f);
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+      float a = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
+      a = fmaxf(a, fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));
       a = group_max<LPG>(a);
-      const float sc = a / 7.0f;
-      const int64_t row = c / cpr, col = c - row * cpr;
-      q[row * (K / 8) + col] = int4_codes8(f, sc);
-      if ((threadIdx.x & (LPG - 1)) == 0) s[row * (K / G) + (col * 8) / G] = sc;
+      float sc, rc;
+      group_scale(a, sc, rc);
+      q[(int64_t)row * cpr + mp.col] = int4_codes8(f, sc, rc);
+      if ((threadIdx.x & (LPG - 1)) == 0) s[(int64_t)row * (cpr / LPG) + mp.col / LPG] = sc;
     }
   }
 }
@@ -73,14 +123,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
 // Per-token quantization (one group spans the whole row): one block per row,
 // absmax reduced across the block, then the row is read again from cache.
 __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t K,
+    const uint16_t* __restrict__ x, int64_t ldx, int cpr,
     uint32_t* __restrict__ q, float* __restrict__ s) {
   __shared__ float wave_max[kQuantThreads / 64];
-  const int64_t row = blockIdx.x;
+  const int row = blockIdx.x;
   const uint16_t* xr = x + row * ldx;
-  const int64_t cpr = K / 8;
   float a = 0.0f;
-  for (int64_t c = threadIdx.x; c < cpr; c += kQuantThreads) {
+  for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
     float f[8];
     halves_to_float8(*reinterpret_cast<const uint4*>(xr + c * 8), f);
 #pragma unroll
@@ -91,43 +140,45 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kQuantThreads / 64; ++w) a = fmaxf(a, wave_max[w]);
-  const float sc = a / 7.0f;
-  for (int64_t c = threadIdx.x; c < cpr; c += kQuantThreads) {
+  float sc, rc;
+  group_scale(a, sc, rc);
+  for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
     float f[8];
     halves_to_float8(*reinterpret_cast<const uint4*>(xr + c * 8), f);
-    q[row * cpr + c] = int4_codes8(f, sc);
+    q[(int64_t)row * cpr + c] = int4_codes8(f, sc, rc);
   }
   if (threadIdx.x == 0) s[row] = sc;
 }
 
-// Round |v| (already divided by 2^E) to an E2M1 magnitude index 0..7:
-// nearest of {0,0.5,1,1.5,2,3,4,6}, ties to the even index, saturating at 6.
-__device__ __forceinline__ uint32_t e2m1_index(float m) {
-  uint32_t i = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) +
-               (m > 2.5f) + (m >= 3.5f) + (m > 5.0f);
-  return i;
+// E2M1 conversion of 8 values already divided by 2^E, two per instruction:
+// v_cvt_scalef32_pk_fp4_f32 (unit scale) rounds to nearest of
+// {0,0.5,1,1.5,2,3,4,6}, ties to even, saturates at 6 and keeps the sign of
+// zero -- the OCP MX rule; the parity tests check it over every fp16 input.
+__device__ __forceinline__ uint32_t e2m1_codes8(const float v[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
 }
 
 // 32-element block = 4 lanes x 8 values.
 __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
-    const uint16_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t K,
+    const uint16_t* __restrict__ x, int64_t ldx, int rows, int cpr, int wshift,
     uint32_t* __restrict__ q, uint8_t* __restrict__ e8m0) {
-  const int64_t cpr = K / 8;
-  const int64_t total = rows * cpr;
-  const int64_t base = (int64_t)blockIdx.x * (kQuantThreads * kChunksPerThread) + threadIdx.x;
-  uint4 raw[kChunksPerThread];
+  const Map mp = lane_map(wshift);
+  if (mp.col >= cpr) return;
+  uint4 raw[kRowsPerThread];
 #pragma unroll
-  for (int u = 0; u < kChunksPerThread; ++u) {
-    const int64_t c = base + u * kQuantThreads;
-    if (c < total) {
-      const int64_t row = c / cpr, col = c - row * cpr;
-      raw[u] = *reinterpret_cast<const uint4*>(x + row * ldx + col * 8);
-    }
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int row = mp.row0 + u * mp.rstep;
+    if (row < rows) raw[u] = *reinterpret_cast<const uint4*>(x + row * ldx + mp.col * 8);
   }
 #pragma unroll
-  for (int u = 0; u < kChunksPerThread; ++u) {
-    const int64_t c = base + u * kQuantThreads;
-    if (c < total) {
+  for (int u = 0; u < kRowsPerThread; ++u) {
+    const int row = mp.row0 + u * mp.rstep;
+    if (row < rows) {
       float f[8];
       halves_to_float8(raw[u], f);
       float a = 0.0f;
@@ -138,18 +189,21 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
       // biased exponent field is floor(log2 a) + 127.
       const int biased = (int)((__float_as_uint(a) >> 23) & 0xFF);
       const int E = (a == 0.0f) ? -127 : biased - 127 - 2;
-      uint32_t word = 0;
+      float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = ldexpf(f[i], -E);      // exact power-of-two scaling
-        const uint32_t sign = (__float_as_uint(f[i]) >> 31) & 1u;
-        word |= ((sign << 3) | e2m1_index(fabsf(v))) << (4 * i);
-      }
-      const int64_t row = c / cpr, col = c - row * cpr;
-      q[row * cpr + col] = word;
-      if ((threadIdx.x & 3) == 0) e8m0[row * (K / 32) + col / 4] = (uint8_t)(E + 127);
+      for (int i = 0; i < 8; ++i) v[i] = ldexpf(f[i], -E);   // exact power-of-two scaling
+      q[(int64_t)row * cpr + mp.col] = e2m1_codes8(v);
+      if ((threadIdx.x & 3) == 0) e8m0[(int64_t)row * (cpr / 4) + mp.col / 4] = (uint8_t)(E + 127);
     }
   }
+}
+
+int width_shift(int cpr) { return cpr <= 64 ? 6 : cpr <= 128 ? 7 : 8; }
+
+dim3 grid_for(int rows, int cpr, int wshift) {
+  const int W = 1 << wshift;
+  const int rows_per_block = (kQuantThreads >> wshift) * kRowsPerThread;
+  return dim3((unsigned)((cpr + W - 1) / W), (unsigned)((rows + rows_per_block - 1) / rows_per_block));
 }
 
 }  // namespace
@@ -158,27 +212,28 @@ void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int gro
                        uint8_t* q, float* s, hipStream_t stream) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint32_t* qp = reinterpret_cast<uint32_t*>(q);
-  const int64_t total = M * (K / 8);
-  const int64_t per_block = kQuantThreads * kChunksPerThread;
-  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
-  switch (group) {
-    case 64: hipLaunchKernelGGL(k_int4_quant_groups<64>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, M, K, qp, s); return;
-    case 128: hipLaunchKernelGGL(k_int4_quant_groups<128>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, M, K, qp, s); return;
-    case 256: hipLaunchKernelGGL(k_int4_quant_groups<256>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, M, K, qp, s); return;
-    case 512: hipLaunchKernelGGL(k_int4_quant_groups<512>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, M, K, qp, s); return;
-    default:  // group == K, validated by the caller
-      hipLaunchKernelGGL(k_int4_quant_rows, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, xp, ldx, K, qp, s);
+  const int cpr = (int)(K / 8);
+  const int ws = width_shift(cpr);
+  const dim3 grid = grid_for((int)M, cpr, ws);
+  const int m = (int)M;
+  switch (group == K && group > 512 ? 0 : group) {
+    case 64: hipLaunchKernelGGL(k_int4_quant_groups<64>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
+    case 128: hipLaunchKernelGGL(k_int4_quant_groups<128>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
+    case 256: hipLaunchKernelGGL(k_int4_quant_groups<256>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
+    case 512: hipLaunchKernelGGL(k_int4_quant_groups<512>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
+    default:  // group == K (per token), validated by the caller
+      hipLaunchKernelGGL(k_int4_quant_rows, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, xp, ldx, cpr, qp, s);
       return;
   }
 }
 
 void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
                         uint8_t* q, uint8_t* e8m0, hipStream_t stream) {
-  const int64_t total = rows * (K / 8);
-  const int64_t per_block = kQuantThreads * kChunksPerThread;
-  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
-  hipLaunchKernelGGL(k_mxfp4_quant, grid, dim3(kQuantThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), ldx, rows, K, reinterpret_cast<uint32_t*>(q), e8m0);
+  const int cpr = (int)(K / 8);
+  const int ws = width_shift(cpr);
+  hipLaunchKernelGGL(k_mxfp4_quant, grid_for((int)rows, cpr, ws), dim3(kQuantThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), ldx, (int)rows, cpr, ws,
+                     reinterpret_cast<uint32_t*>(q), e8m0);
 }
 
 }  // namespace w4a4

@@ -2,14 +2,22 @@
 //
 // MXFP4 = FP4 E2M1 elements with one E8M0 scale per 32 along K (the
 // "open-standard MXFP4" of the FP4 RL abstract; block rule of OCP MX v1.0).
-// v_mfma_scale_f32_16x16x128_f8f6f4 with both operand formats set to FP4
-// multiplies a 16 x 128 A tile by a 128 x 16 B tile; each lane supplies 32
-// consecutive K codes of one row (16 bytes) and the E8M0 byte of exactly that
-// 32-block, so the block scales are applied inside the instruction and the
-// accumulation is fp32 with no vector-unit epilogue.
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operand formats set to FP4
+// multiplies a 32 x 64 A tile by a 64 x 32 B tile; lane l supplies the 32
+// consecutive K codes (16 bytes) of row l%32, 32-block l/32, and the E8M0 byte
+// of exactly that block, so the block scales are applied inside the
+// instruction and accumulation is fp32 with no vector-unit epilogue. The kernel
+// is therefore matrix-core bound, and is tiled for that: each wave owns a
+// (BM/WM) x (BN/WN) output tile; the launch uses 128 x 128 workgroup tiles of
+// 2 x 2 waves, two workgroups per CU (2 waves per SIMD).
 //
-// Tile: 128 x 128 per 256-thread workgroup (2 x 2 waves of 64 x 64), K step
-// 128 (one MFMA per 16 x 16 block per step), double-buffered LDS.
+// K stage 128 (64 packed bytes per row), fed through a 3-stage LDS ring by
+// direct global->LDS loads (no staging registers), so two stages of loads are
+// in flight behind the matrix work. The debug-partials variant runs
+// the same instruction one 32-block at a time with unit scales.
+//
+// 32x32 MFMA output layout: D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+// col l%32.
 #include "device.h"
 #include "launch.h"
 
@@ -17,24 +25,27 @@ namespace w4a4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 128;
 constexpr int ROW_BYTES = BK / 2;
-constexpr int LDS_STRIDE = ROW_BYTES + 16;
 constexpr int kThreads = 256;
 constexpr int kFmtFp4 = 4;       // cbsz / blgp operand format code for FP4 E2M1
 constexpr int kUnitScale = 127;  // E8M0 byte of 2^0
+constexpr int kGroupRows = 4;    // tile-rows per raster group
 
 struct Params {
   const uint8_t* a;
   const uint8_t* ea;
   const uint8_t* w;
   const uint8_t* ew;
-  int64_t M, N, K;
+  int M, N, K;
   void* y;
   int ydtype;
   int64_t ldy;
-  int64_t tile_m0, tile_n0;
-  int64_t m0, mc, n0, nc;
+  int tiles_m, tiles_n;
+  int tile_m0, tile_n0;
+  int m0, mc, n0, nc;
   int32_t* partials;
 };
 
@@ -42,142 +53,242 @@ __device__ __forceinline__ v8i as_operand(uint4 v) {
   return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 }
 
-template <bool PARTIALS>
-__global__ __launch_bounds__(kThreads) void k_mxfp4_gemm(Params p) {
-  __shared__ __align__(16) uint8_t sA[2][BM * LDS_STRIDE];
-  __shared__ __align__(16) uint8_t sW[2][BN * LDS_STRIDE];
-  __shared__ uint32_t sEA[2][BM];   // 4 scale bytes (the 4 blocks of a K step)
-  __shared__ uint32_t sEW[2][BN];
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(1))) void* glb_vptr;
+
+// Direct global -> LDS copies: lane l's 16 (4) bytes land at lds + 16 l (4 l).
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((glb_vptr)(const_cast<void*>(g)), (lds_vptr)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((glb_vptr)(const_cast<void*>(g)), (lds_vptr)lds, 4, 0, 0);
+}
+
+// s_waitcnt on vmcnt only (expcnt/lgkmcnt left at their maxima), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup tile BM x BN; waves in a 2 x 2 grid, each (BM/2) x (BN/2) = TI x TJ
+// blocks of 32 x 32. S-stage LDS ring filled by direct global->LDS loads: stage
+// kt+S-1 is in flight while stage kt is computed. A stage holds BM + BN rows of
+// 64 bytes (row-major, no pad: each 16-row chunk is one wave-wide 1 KB load)
+// and one E8M0 dword per row. The 16-byte slot of a row is XOR-swizzled with
+// (row >> 3) & 3 so the 32 lanes of each half-wave that read one slot of 32
+// consecutive rows hit 32 distinct bank groups.
+template <int BM, int BN, int WM, int WN, bool PARTIALS>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_mxfp4_gemm(Params p) {
+  constexpr int S = 3;                              // ring depth
+  constexpr int NWAVE = WM * WN;
+  constexpr int TI = BM / WM / 32, TJ = BN / WN / 32;   // 32x32 blocks per wave
+  constexpr int NA = BM / 16 / NWAVE, NW = BN / 16 / NWAVE;   // 1 KB loads per wave per stage
+  constexpr int NE = (BM + BN + 64 * NWAVE - 1) / (64 * NWAVE); // scale-dword loads per wave
+  constexpr int W_OFF = BM * ROW_BYTES;
+  constexpr int E_OFF = (BM + BN) * ROW_BYTES;
+  constexpr int STAGE = E_OFF + NE * NWAVE * 64 * 4;
+  constexpr int PER_STAGE = NA + NW + NE;           // load instructions per wave per stage
+  static_assert(NA * 16 * NWAVE == BM && NW * 16 * NWAVE == BN, "tile rows per wave");
+  // One array per ring slot (the loop is unrolled by S, so every access names
+  // its slot): the compiler can then tell an in-flight load into one slot from
+  // LDS reads of another and does not wait for it.
+  __shared__ __align__(16) uint8_t sm0[STAGE];
+  __shared__ __align__(16) uint8_t sm1[STAGE];
+  __shared__ __align__(16) uint8_t sm2[STAGE];
+
+  const int nblk = p.tiles_m * p.tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int per_group = kGroupRows * p.tiles_n;
+  const int grp = bid / per_group;
+  const int first_m = grp * kGroupRows;
+  const int gsize = min(p.tiles_m - first_m, kGroupRows);
+  const int rem = bid - grp * per_group;
+  const int tile_m = (p.tile_m0 + first_m + rem % gsize) * BM;
+  const int tile_n = (p.tile_n0 + rem / gsize) * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tile_m = (p.tile_m0 + blockIdx.y) * BM;
-  const int64_t tile_n = (p.tile_n0 + blockIdx.x) * BN;
-  const int64_t row_bytes = p.K / 2;
-  const int64_t row_scales = p.K / 32;
-  const int nk = (int)(p.K / BK);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int row_bytes = p.K >> 1;
+  const int row_scales = p.K >> 5;
+  const int nk = p.K / BK;
 
-  const uint8_t* ga_ptr[2];
-  const uint8_t* gw_ptr[2];
-  int lds_off[2];
+  // ---- per-lane sources of this wave's loads (stage 0); LDS offsets are per wave
+  const uint8_t* srcA[NA];
+  const uint8_t* srcW[NW];
+  const uint8_t* srcE[NE];
+  const int lrow = lane >> 2, lslot = lane & 3;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + kThreads * i;
-    const int r = idx >> 2, seg = idx & 3;
-    ga_ptr[i] = p.a + min(tile_m + r, p.M - 1) * row_bytes + seg * 16;
-    gw_ptr[i] = p.w + min(tile_n + r, p.N - 1) * row_bytes + seg * 16;
-    lds_off[i] = r * LDS_STRIDE + seg * 16;
+  for (int i = 0; i < NA; ++i) {
+    const int row = 16 * (wave + NWAVE * i) + lrow;
+    const int seg = lslot ^ ((row >> 3) & 3);
+    srcA[i] = p.a + (int64_t)min(tile_m + row, p.M - 1) * row_bytes + 16 * seg;
   }
-  const bool scale_is_a = tid < BM;
-  const int srow = scale_is_a ? tid : tid - BM;
-  const uint8_t* sptr = scale_is_a ? p.ea + min(tile_m + srow, p.M - 1) * row_scales
-                                   : p.ew + min(tile_n + srow, p.N - 1) * row_scales;
-
-  uint4 ra[2], rw[2];
-  uint32_t rs;
-  auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(ga_ptr[i] + (int64_t)kt * ROW_BYTES);
-      rw[i] = *reinterpret_cast<const uint4*>(gw_ptr[i] + (int64_t)kt * ROW_BYTES);
-    }
-    rs = *reinterpret_cast<const uint32_t*>(sptr + (int64_t)kt * 4);
-  };
-  auto lstore = [&](int buf) {
+  for (int i = 0; i < NW; ++i) {
+    const int row = 16 * (wave + NWAVE * i) + lrow;
+    const int seg = lslot ^ ((row >> 3) & 3);
+    srcW[i] = p.w + (int64_t)min(tile_n + row, p.N - 1) * row_bytes + 16 * seg;
+  }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&sA[buf][lds_off[i]]) = ra[i];
-      *reinterpret_cast<uint4*>(&sW[buf][lds_off[i]]) = rw[i];
-    }
-    if (scale_is_a) sEA[buf][srow] = rs;
-    else sEW[buf][srow] = rs;
-  };
+  for (int j = 0; j < NE; ++j) {
+    const int slot = 64 * (NE * wave + j) + lane;
+    srcE[j] = slot < BM ? p.ea + (int64_t)min(tile_m + slot, p.M - 1) * row_scales
+            : slot < BM + BN ? p.ew + (int64_t)min(tile_n + slot - BM, p.N - 1) * row_scales
+                             : p.ea;   // unused slot: a harmless in-bounds read
+  }
+#define ISSUE(KT, SM)                                                                \
+  {                                                                                  \
+    uint8_t* base_ = (SM);                                                           \
+    _Pragma("unroll") for (int i = 0; i < NA; ++i)                                   \
+        dma16(srcA[i] + (KT) * ROW_BYTES, base_ + (wave + NWAVE * i) * 1024);      \
+    _Pragma("unroll") for (int i = 0; i < NW; ++i)                                   \
+        dma16(srcW[i] + (KT) * ROW_BYTES, base_ + W_OFF + (wave + NWAVE * i) * 1024); \
+    _Pragma("unroll") for (int j = 0; j < NE; ++j)                                   \
+        dma4(srcE[j] + (KT) * 4, base_ + E_OFF + (NE * wave + j) * 256);           \
+  }
 
-  v4f acc[4][4];
+  v16f acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int lrow = lane & 15;
-  const int lblk = lane >> 4;     // which 32-block of the K step this lane holds
-  const int orow = (lane >> 4) * 4;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  const int rowA = wm * (BM / WM) + l32;
+  const int rowW = wn * (BN / WN) + l32;
+  int offA[2], offW[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    offA[u] = rowA * ROW_BYTES + 16 * ((2 * u + lhi) ^ ((rowA >> 3) & 3));
+    offW[u] = rowW * ROW_BYTES + 16 * ((2 * u + lhi) ^ ((rowW >> 3) & 3));
+  }
+  uint4 av[TI], wv[TJ];     // one 64-k step's operands (FP4: 16 bytes per lane)
+  int ea[TI], ew[TJ];
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+// Operands of one 64-k MFMA step U from ring slot SM: lane l feeds 32-block
+// 2U + l/32 of its row and that block's E8M0 byte. (row + 32 i) >> 3 & 3 equals
+// row >> 3 & 3, so one swizzled base per step serves every row block i.
+#define LOAD_OPS(SM, U)                                                               \
+  {                                                                                  \
+    const uint8_t* st_ = (SM);                                                       \
+    const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF);            \
+    _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                 \
+      av[i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 2048 * i);            \
+      ea[i] = (int)((se_[rowA + 32 * i] >> (8 * (2 * (U) + lhi))) & 0xFFu);          \
+    }                                                                                \
+    _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                 \
+      wv[j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 2048 * j);    \
+      ew[j] = (int)((se_[BM + rowW + 32 * j] >> (8 * (2 * (U) + lhi))) & 0xFFu);     \
+    }                                                                                \
+  }
+// Matrix work of step U of stage KT. The partials variant runs one 32-block at
+// a time with unit scales, so D = sum va*vw over that block exactly.
+#define MMA_STEP(KT, U)                                                              \
+  {                                                                                  \
+    if constexpr (PARTIALS) {                                                        \
+      const v8i zero_ = v8i{0, 0, 0, 0, 0, 0, 0, 0};                                 \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                \
+        const int gblk = 4 * (KT) + 2 * (U) + h;                                     \
+        _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
+        _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                             \
+          v16f zacc;                                                                 \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) zacc[r] = 0.0f;             \
+          const v16f d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(            \
+              lhi == h ? as_operand(av[i]) : zero_, lhi == h ? as_operand(wv[j]) : zero_, zacc, \
+              kFmtFp4, kFmtFp4, 0, kUnitScale, 0, kUnitScale);                       \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) {                           \
+            const int m = tile_m + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3); \
+            const int n = tile_n + wn * (BN / WN) + 32 * j + l32;                     \
+            if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)        \
+              p.partials[((int64_t)gblk * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = (int32_t)(d[r] * 4.0f); \
+          }                                                                          \
+        }                                                                            \
+      }                                                                              \
+    } else {                                                                         \
+      _Pragma("unroll") for (int i = 0; i < TI; ++i)                                 \
+      _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                 \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
+            as_operand(av[i]), as_operand(wv[j]), acc[i][j], kFmtFp4, kFmtFp4, 0, ea[i], 0, ew[j]); \
+    }                                                                                \
+  }
+// Barrier between ring stages. Each wave has already waited for its own
+// direct loads of the stage (vmcnt), so after the barrier every wave's part of
+// the stage is in LDS, and every wave has finished reading the slot about to be
+// refilled. No memory fence: a fence would also drain the loads still in
+// flight for later stages. The scheduling barrier keeps the compiler from
+// moving LDS accesses across it.
+#define STAGE_BARRIER()                                                 \
+  {                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    __builtin_amdgcn_s_barrier();                                       \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+  }
+// Iteration for stage KT held in slot CUR; stage KT+2 is issued into slot NXT
+// (the slot stage KT-1 used, free once every wave has passed the barrier) after
+// the first step's operand reads, so those reads never wait behind the new loads.
+#define ITER(KT, CUR, NXT)                                              \
+  {                                                                     \
+    if ((KT) + 1 < nk) wait_vmcnt<PER_STAGE>();                         \
+    else wait_vmcnt<0>();                                               \
+    STAGE_BARRIER();                                                    \
+    LOAD_OPS(CUR, 0);                                                   \
+    if ((KT) + 2 < nk) ISSUE((KT) + 2, NXT);                            \
+    MMA_STEP(KT, 0);                                                    \
+    LOAD_OPS(CUR, 1);                                                   \
+    MMA_STEP(KT, 1);                                                    \
+  }
 
+  ISSUE(0, sm0);
+  if (nk > 1) ISSUE(1, sm1);
+  int slot = 0;      // kt % S
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    v8i a[4], b[4];
-    int ea[4], eb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + i * 16 + lrow;
-      a[i] = as_operand(*reinterpret_cast<const uint4*>(&sA[buf][r * LDS_STRIDE + lblk * 16]));
-      ea[i] = (int)((sEA[buf][r] >> (8 * lblk)) & 0xFFu);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 64 + j * 16 + lrow;
-      b[j] = as_operand(*reinterpret_cast<const uint4*>(&sW[buf][r * LDS_STRIDE + lblk * 16]));
-      eb[j] = (int)((sEW[buf][r] >> (8 * lblk)) & 0xFFu);
-    }
-    if constexpr (PARTIALS) {
-      // One 32-block at a time: only the lanes holding block q keep their
-      // codes, scales are 2^0, and D = sum va*vw over that block exactly.
-      const v8i zero = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t blk = (int64_t)kt * 4 + q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                lblk == q ? a[i] : zero, lblk == q ? b[j] : zero, v4f{0.f, 0.f, 0.f, 0.f},
-                kFmtFp4, kFmtFp4, 0, kUnitScale, 0, kUnitScale);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t m = tile_m + wm * 64 + i * 16 + orow + r;
-              const int64_t n = tile_n + wn * 64 + j * 16 + lrow;
-              if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)
-                p.partials[(blk * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = (int32_t)(d[r] * 4.0f);
-            }
-          }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              a[i], b[j], acc[i][j], kFmtFp4, kFmtFp4, 0, ea[i], 0, eb[j]);
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    // a uniform branch picks the slot, so each path names its arrays statically
+    if (slot == 0) ITER(kt, sm0, sm2)
+    else if (slot == 1) ITER(kt, sm1, sm0)
+    else ITER(kt, sm2, sm1)
+    slot = (slot == S - 1) ? 0 : slot + 1;
   }
+#undef ITER
+#undef STAGE_BARRIER
+#undef MMA_STEP
+#undef LOAD_OPS
+#undef ISSUE
 
   if constexpr (!PARTIALS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t m = tile_m + wm * 64 + i * 16 + orow + r;
-          const int64_t n = tile_n + wn * 64 + j * 16 + lrow;
+        for (int r = 0; r < 16; ++r) {
+          const int m = tile_m + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
+          const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
           if (m < p.M && n < p.N) {
             if (p.ydtype == 0)
-              static_cast<float*>(p.y)[m * p.ldy + n] = acc[i][j][r];
+              static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i][j][r];
             else
-              static_cast<__half*>(p.y)[m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
+              static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
           }
         }
   }
+}
+
+template <int BM, int BN, int WM, int WN, bool PARTIALS>
+void launch_cfg(Params p, const GemmArgs& g, hipStream_t stream) {
+  p.tile_m0 = (int)(g.m0 / BM);
+  p.tile_n0 = (int)(g.n0 / BN);
+  p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
+  p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
+  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, PARTIALS>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                     dim3(64 * WM * WN), 0, stream, p);
 }
 
 }  // namespace
@@ -188,26 +299,22 @@ void launch_mxfp4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.ea = static_cast<const uint8_t*>(g.sa);
   p.w = g.w;
   p.ew = static_cast<const uint8_t*>(g.sw);
-  p.M = g.M;
-  p.N = g.N;
-  p.K = g.K;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
   p.y = g.y;
   p.ydtype = g.ydtype;
   p.ldy = g.ldy;
-  p.m0 = g.m0;
-  p.mc = g.mc;
-  p.n0 = g.n0;
-  p.nc = g.nc;
+  p.m0 = (int)g.m0;
+  p.mc = (int)g.mc;
+  p.n0 = (int)g.n0;
+  p.nc = (int)g.nc;
   p.partials = g.partials;
-  p.tile_m0 = g.m0 / BM;
-  p.tile_n0 = g.n0 / BN;
-  const int64_t tiles_m = (g.m0 + g.mc - 1) / BM - p.tile_m0 + 1;
-  const int64_t tiles_n = (g.n0 + g.nc - 1) / BN - p.tile_n0 + 1;
-  const dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
-  if (g.partials)
-    hipLaunchKernelGGL(k_mxfp4_gemm<true>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(k_mxfp4_gemm<false>, grid, dim3(kThreads), 0, stream, p);
+  if (g.partials) {
+    launch_cfg<128, 128, 2, 2, true>(p, g, stream);
+    return;
+  }
+  launch_cfg<128, 128, 2, 2, false>(p, g, stream);
 }
 
 }  // namespace w4a4

@@ -19,6 +19,7 @@ workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -41,8 +42,44 @@ WORKLOADS = {
 }
 
 
+GEMM_SOURCES = {"int4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_w4a4.hip",
+                "mxfp4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip"}
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha256(fmt: str) -> str:
+    with open(os.path.join(ROOT, GEMM_SOURCES[fmt]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(fmt: str, workload: str, tokens: int):
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, scaled by the copy-kernel calibration; None when there is
+    no record for this workload or the kernel source changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))[f"{fmt}:{workload}:{tokens}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != source_sha256(fmt):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> int:
+    """A plain device copy of known size, run under rocprofv3 to scale the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) of the GEMM runs."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+    return 0
 
 
 def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
@@ -92,6 +129,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--cpu-cols", type=int, default=4096)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -99,6 +138,9 @@ def main() -> int:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import numpy as np
     import torch
@@ -216,7 +258,7 @@ def main() -> int:
         },
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": None,
+            "frac": achieved / peak, "traffic": measured_traffic(fmt, args.workload, M),
         },
         "act_quant": {"GB/s": quant_gbs, "frac_hbm": quant_gbs / PEAK_HBM_GBS},
         "per_linear": per_linear,

@@ -41,6 +41,7 @@ namespace {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int ROW_BYTES = BK / 2;   // packed bytes per row per stage
@@ -148,6 +149,7 @@ void k_w4a4_gemm(Params p) {
   v16f acc[2][2];
   v16i P[2][2];
   const v16i zero16 = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const v32f zero32 = {};
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -209,22 +211,20 @@ void k_w4a4_gemm(Params p) {
                   p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = P[i][j][r] >> 8;
               }
         } else {
-          const float* sa_h = &sSA[buf][h][wm * 64 + 4 * lhi];
-          const float* sw_h = &sSW[buf][h][wn * 64 + l32];
-          const float swj0 = sw_h[0] * (1.0f / 256.0f);
-          const float swj1 = sw_h[32] * (1.0f / 256.0f);
+          // Scale products t[m][n] = s_a[m] * s_w[n] / 256 as a rank-1 matrix
+          // product on the matrix cores: one two-block 32x32x1 fp32 MFMA gives
+          // the 32x32 tiles (i = 0, j) and (i = 1, j), in the same lane/register
+          // layout as the int32 partials. Lane l supplies row l of the wave's 64
+          // A rows (block l / 32) and column 32 j + l % 32 of its W columns.
+          const float av = sSA[buf][h][wm * 64 + lane];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
+          for (int j = 0; j < 2; ++j) {
+            const float bv = sSW[buf][h][wn * 64 + 32 * j + l32] * (1.0f / 256.0f);
+            const v32f T = __builtin_amdgcn_mfma_f32_32x32x1f32(av, bv, zero32, 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 sa4 = *reinterpret_cast<const float4*>(sa_h + i * 32 + 8 * q);
-              const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q + e;
-                acc[i][0][r] = fmaf((float)P[i][0][r], sa[e] * swj0, acc[i][0][r]);
-                acc[i][1][r] = fmaf((float)P[i][1][r], sa[e] * swj1, acc[i][1][r]);
-              }
+            for (int r = 0; r < 16; ++r) {
+              acc[0][j][r] = fmaf((float)P[0][j][r], T[r], acc[0][j][r]);
+              acc[1][j][r] = fmaf((float)P[1][j][r], T[16 + r], acc[1][j][r]);
             }
           }
         }

@@ -25,10 +25,18 @@
  *   - Extents are int64_t element counts. A zero extent (M, N or rows == 0) is a
  *     valid no-op; pointers whose extent is zero may then be NULL.
  *   - Buffers must not overlap. Results are deterministic (no atomics).
- *   - Packed 4-bit layout (INT4 and MXFP4 alike): row-major [rows][K/2] bytes,
- *     K contiguous, two codes per byte, the even k in the LOW nibble.
- *     INT4 codes are two's complement in [-8, 7]; MXFP4 codes are E2M1
- *     (sign<<3 | magnitude index into {0,0.5,1,1.5,2,3,4,6}).
+ *   - Packed 4-bit codes are row-major [rows][K/2] bytes, K contiguous, two
+ *     codes per byte.
+ *     MXFP4: E2M1 codes (sign<<3 | magnitude index into {0,0.5,1,1.5,2,3,4,6}),
+ *     the even k in the LOW nibble.
+ *     INT4: sign-magnitude (the symmetric rule below only yields codes in
+ *     [-7, 7]), the sign bit being that of the input value (a negative input
+ *     that rounds to 0 is stored as -0). Each little-endian 32-bit word holds
+ *     the codes c0..c7 of 8 consecutive k; its byte b (0..3) holds sign(c_b) in
+ *     bit 7, |c_b| in bits 2..0, |c_(4+b)| in bits 6..4 and sign(c_(4+(b+3)%4))
+ *     in bit 3. The arrangement lets the GEMM form the 8 FP8 E4M3 operand bytes
+ *     [sign 0000 |c|] (value +-|c| * 2^-9, exact) as word & 0x87878787 and
+ *     rotr(word, 4) & 0x87878787.
  */
 #ifndef W4A4_H
 #define W4A4_H
@@ -64,6 +72,7 @@ const char* w4a4_status_str(int status);
  * Per group: a = max|x|; s = fl32(a / 7); q = clamp(rne(fl32(x / s)), -8, 7)
  * with correctly rounded binary32 divisions; an all-zero group gives s = 0 and
  * codes 0. (The pages give no formula: this is the plain symmetric reading.)
+ * |x| <= a makes |q| <= 7, so the codes fit the sign-magnitude layout above.
  *
  *   x     fp16 [M][ldx] row-major, 16-byte aligned, ldx >= K, ldx % 8 == 0
  *   M, K  K > 0, K % 8 == 0 (K % group == 0 required as well)
@@ -88,14 +97,15 @@ w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t grou
  * W4A4 group-dequantized GEMM (APEX4 abstract: pure INT4 matrix products, with
  * the per-group dequantization -- the vector-unit bottleneck it studies -- folded
  * into the accumulation). With g = min(group_a, group_w):
- *   P_b[m,n] = sum_{k in block b of g} qa[m,k] * qw[n,k]          (exact int32)
+ *   P_b[m,n] = sum_{k in block b of g} qa[m,k] * qw[n,k]     (exact, |P_b| <= 49 g)
  *   Y[m,n]   = sum_b s_a[m, b*g/group_a] * s_w[n, b*g/group_w] * P_b[m,n]  (fp32)
  *
  *   xq, xs          packed activation codes [M][K/2] and scales [M][K/group_a]
  *   wq, ws          packed weight codes [N][K/2] and scales [N][K/group_w]
  *   group_a/group_w each a power of two >= 64 dividing K (64, 128, 256, 512, ...)
  *                   or K itself (per token); the larger must be a multiple of
- *                   the smaller
+ *                   the smaller, and g <= 262144 (P_b stays an exact integer in
+ *                   the fp32 matrix-core accumulator: 49 g < 2^24)
  *   M, N, K         M, N >= 0; K > 0 and K % 128 == 0
  *   y               out: [M][ldy] fp32 or fp16 (y_dtype), ldy >= N,
  *                   aligned to its element size

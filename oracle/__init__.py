@@ -19,8 +19,10 @@ from .int4 import (  # noqa: F401
     int4_quantize,
     int4_dequantize,
     pack_nibbles,
-    unpack_nibbles_signed,
     unpack_nibbles_unsigned,
+    pack_int4,
+    unpack_int4,
+    int4_sign_bits,
     w4a4_block_partials,
     w4a4_gemm,
     w4a4_gemm_rows,

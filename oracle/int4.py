@@ -16,8 +16,16 @@ taken here:
   -8, 7)``; an all-zero group has ``s = 0`` and codes 0;
 * scales are IEEE binary32; divisions are correctly rounded binary32 (the
   precision the kernel makes the integer decision in); ties round to even;
-* packed layout: row-major, K contiguous, two codes per byte, the even k in the
-  low nibble, two's complement;
+* packed layout (the pages give none): row-major, K contiguous, two codes per
+  byte, sign-magnitude. The symmetric rule only yields codes in [-7, 7] (the
+  clamp at -8 never fires), so a sign bit and a 3-bit magnitude hold every code.
+  A code's sign bit is the sign bit of its input value (so a negative input that
+  rounds to 0 is stored as -0). Each little-endian 32-bit word holds the 8 codes
+  c0..c7 of k = 8j .. 8j+7; its byte b (b = 0..3) holds the sign of c_b in bit 7,
+  |c_b| in bits 2..0, |c_(4+b)| in bits 6..4 and the sign of c_(4+(b+3) mod 4)
+  in bit 3. (With that arrangement ``word & 0x87878787`` and
+  ``rotr(word, 4) & 0x87878787`` are the OCP FP8 E4M3 bytes [sign 0000 mag] of
+  c0..c3 and c4..c7, whose values are exactly +-|c| * 2^-9.);
 * the GEMM is ``Y = X W^T`` (a linear layer), A = activations [M, K] and
   W = weights [N, K]; with ``g = min(g_a, g_w)`` (nested groups) the per-block
   integer partial is ``P_b[m, n] = sum_{k in block b} qa[m,k] qw[n,k]`` and
@@ -70,7 +78,10 @@ def int4_dequantize(codes: np.ndarray, scales: np.ndarray, group: int) -> np.nda
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
-    """Two 4-bit codes per byte, even k in the low nibble (two's complement)."""
+    """Generic 4-bit field packing: two fields per byte, even k in the low nibble.
+
+    Used for MXFP4 E2M1 codes (fields 0..15); INT4 codes use :func:`pack_int4`.
+    """
     c = np.asarray(codes)
     if c.ndim != 2 or c.shape[1] % 2:
         raise ValueError("codes must be 2-D with an even number of columns")
@@ -87,10 +98,52 @@ def unpack_nibbles_unsigned(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def unpack_nibbles_signed(packed: np.ndarray) -> np.ndarray:
-    """Inverse of :func:`pack_nibbles` giving two's complement codes -8..7."""
-    u = unpack_nibbles_unsigned(packed).astype(np.int8)
-    return np.where(u >= 8, u - 16, u).astype(np.int8)
+def pack_int4(codes: np.ndarray, negative: np.ndarray) -> np.ndarray:
+    """Sign-magnitude INT4 packing (layout in the module docstring).
+
+    ``codes``: int [R, K] in [-7, 7], K a multiple of 8; ``negative``: bool
+    [R, K], the sign bit of each code (must agree with the code where it is not
+    zero). Returns uint8 [R, K/2].
+    """
+    c = np.asarray(codes).astype(np.int16)
+    neg = np.asarray(negative, dtype=bool)
+    if c.ndim != 2 or c.shape[1] % 8 or neg.shape != c.shape:
+        raise ValueError("codes and signs must be 2-D, equal shapes, K a multiple of 8")
+    if np.abs(c).max(initial=0) > 7:
+        raise ValueError("sign-magnitude INT4 holds codes in [-7, 7]")
+    if np.any((c != 0) & (neg != (c < 0))):
+        raise ValueError("sign bits disagree with nonzero codes")
+    R, K = c.shape
+    m = np.abs(c).astype(np.uint8).reshape(R, K // 8, 8)
+    sg = neg.astype(np.uint8).reshape(R, K // 8, 8)
+    out = np.empty((R, K // 8, 4), dtype=np.uint8)
+    for b in range(4):
+        out[..., b] = ((sg[..., b] << 7) | (m[..., 4 + b] << 4)
+                       | (sg[..., 4 + (b + 3) % 4] << 3) | m[..., b])
+    return out.reshape(R, K // 2)
+
+
+def unpack_int4(packed: np.ndarray):
+    """Inverse of :func:`pack_int4`: ``(codes int8 [R, K], negative bool [R, K])``."""
+    p = np.asarray(packed, dtype=np.uint8)
+    if p.ndim != 2 or p.shape[1] % 4:
+        raise ValueError("packed rows must hold whole 32-bit words")
+    R, H = p.shape
+    w = p.reshape(R, H // 4, 4)
+    m = np.empty((R, H // 4, 8), dtype=np.int16)
+    sg = np.empty((R, H // 4, 8), dtype=bool)
+    for b in range(4):
+        m[..., b] = w[..., b] & 7
+        sg[..., b] = (w[..., b] >> 7) & 1
+        m[..., 4 + b] = (w[..., b] >> 4) & 7
+        sg[..., 4 + (b + 3) % 4] = (w[..., b] >> 3) & 1
+    codes = np.where(sg, -m, m).astype(np.int8)
+    return codes.reshape(R, 2 * H), sg.reshape(R, 2 * H)
+
+
+def int4_sign_bits(x: np.ndarray) -> np.ndarray:
+    """Sign bit stored with each INT4 code: the sign bit of the fp16 input."""
+    return np.signbit(np.asarray(x))
 
 
 def _nested_groups(K: int, g_a: int, g_w: int) -> int:

@@ -26,7 +26,9 @@ def int4_check(x16, group, ldx_pad=0):
         xt = dev(x16)
     q, s = ops().w4a4_quantize_act(xt, group)
     codes, scales = oracle.int4_quantize(x16, group)
-    assert np.array_equal(host(q), oracle.pack_nibbles(codes)), f"codes differ (M={M} K={K} g={group})"
+    want = oracle.pack_int4(codes, oracle.int4_sign_bits(x16))
+    bad = np.argwhere(host(q) != want)
+    assert bad.size == 0, f"codes differ at {bad[:5].tolist()} (M={M} K={K} g={group})"
     gs = host(s)
     assert np.array_equal(gs.view(np.uint32), scales.view(np.uint32)), f"scales differ (M={M} K={K} g={group})"
 
@@ -88,7 +90,7 @@ def test_int4_workload_activations_sampled(name):
     q, s = ops().w4a4_quantize_act(dev(x), 128)
     rows = synth.sample_rows(M, 64, seed=1)
     codes, scales = oracle.int4_quantize(x[rows], 128)
-    assert np.array_equal(host(q)[rows], oracle.pack_nibbles(codes))
+    assert np.array_equal(host(q)[rows], oracle.pack_int4(codes, oracle.int4_sign_bits(x[rows])))
     assert np.array_equal(host(s)[rows].view(np.uint32), scales.view(np.uint32))
 
 
@@ -105,7 +107,7 @@ def mx_check(x16, ldx_pad=0):
     codes, e8 = oracle.mxfp4_quantize(x16)
     assert np.array_equal(host(e), e8), f"E8M0 differ (R={R} K={K})"
     gq = host(q)
-    want = oracle.pack_nibbles(codes)
+    want = oracle.pack_nibbles(codes)   # E2M1 fields, even k low
     bad = np.argwhere(gq != want)
     assert bad.size == 0, f"codes differ at {bad[:5].tolist()} (R={R} K={K})"
 

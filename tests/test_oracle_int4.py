@@ -158,20 +158,77 @@ def test_rejects_bad_input():
 
 
 # ---------------------------------------------------------------- packing
-def test_pack_layout_examples():
-    c = np.array([[1, -1, -8, 7, 0, -7, 3, 4]], dtype=np.int8)
-    p = oracle.pack_nibbles(c)
-    assert p.tolist() == [[0xF1, 0x78, 0x90, 0x43]]
-    assert np.array_equal(oracle.unpack_nibbles_signed(p), c)
+def test_pack_nibbles_generic_layout():
     u = np.array([[0, 15, 8, 9]], dtype=np.uint8)
     assert oracle.pack_nibbles(u).tolist() == [[0xF0, 0x98]]
     assert np.array_equal(oracle.unpack_nibbles_unsigned(oracle.pack_nibbles(u)), u)
 
 
-def test_pack_round_trip_random():
+def test_pack_int4_hand_computed_word():
+    """c = [1, -2, 3, -4, 5, -6, 7, -7], worked out bit by bit from the layout:
+    byte0 = s0<<7 | |c4|<<4 | s7<<3 | |c0| = 0 | 0x50 | 0x08 | 1 = 0x59,
+    byte1 = s1<<7 | |c5|<<4 | s4<<3 | |c1| = 0x80 | 0x60 | 0 | 2 = 0xE2,
+    byte2 = s2<<7 | |c6|<<4 | s5<<3 | |c2| = 0 | 0x70 | 0x08 | 3 = 0x7B,
+    byte3 = s3<<7 | |c7|<<4 | s6<<3 | |c3| = 0x80 | 0x70 | 0 | 4 = 0xF4."""
+    c = np.array([[1, -2, 3, -4, 5, -6, 7, -7]], dtype=np.int8)
+    p = oracle.pack_int4(c, c < 0)
+    assert p.tolist() == [[0x59, 0xE2, 0x7B, 0xF4]]
+    codes, neg = oracle.unpack_int4(p)
+    assert np.array_equal(codes, c) and np.array_equal(neg, c < 0)
+    # negative zero: c5 is a high code, so its sign is bit 3 of byte (5 - 4 + 1) % 4 = 2;
+    # c2 is a low code, its sign is bit 7 of byte 2
+    z = np.zeros((1, 8), np.int8)
+    negz = np.zeros((1, 8), bool)
+    negz[0, 5] = True
+    assert oracle.pack_int4(z, negz).tolist() == [[0, 0, 0x08, 0]]
+    negz[0, 5] = False
+    negz[0, 2] = True
+    assert oracle.pack_int4(z, negz).tolist() == [[0, 0, 0x80, 0]]
+
+
+def test_pack_int4_words_decode_to_fp8_e4m3():
+    """Design property of the layout: masking a word with 0x87878787, and its
+    4-bit rotation with the same mask, gives the OCP FP8 E4M3 bytes of
+    c0..c3 and c4..c7; an E4M3 byte [s 0000 mmm] is the subnormal
+    (-1)^s * 2^(1-7) * m/8 = +-m * 2^-9 (OCP 8-bit floating point, E4M3)."""
     rng = np.random.default_rng(0)
-    c = rng.integers(-8, 8, size=(7, 64)).astype(np.int8)
-    assert np.array_equal(oracle.unpack_nibbles_signed(oracle.pack_nibbles(c)), c)
+    c = rng.integers(-7, 8, size=(5, 64)).astype(np.int8)
+    neg = (c < 0) | ((c == 0) & (rng.random(c.shape) < 0.5))
+    p = oracle.pack_int4(c, neg)
+    words = p.view("<u4")
+
+    def e4m3(byte):
+        s, e, m = byte >> 7, (byte >> 3) & 15, byte & 7
+        v = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        return -v if s else v
+
+    for r in range(c.shape[0]):
+        for j in range(words.shape[1]):
+            wd = int(words[r, j])
+            lo = wd & 0x87878787
+            hi = (((wd >> 4) | (wd << 28)) & 0xFFFFFFFF) & 0x87878787
+            got = [e4m3((lo >> (8 * b)) & 0xFF) for b in range(4)] + \
+                  [e4m3((hi >> (8 * b)) & 0xFF) for b in range(4)]
+            assert got == [float(v) * 2.0 ** -9 for v in c[r, 8 * j:8 * j + 8]]
+
+
+def test_pack_int4_round_trip_and_rejects():
+    rng = np.random.default_rng(1)
+    c = rng.integers(-7, 8, size=(7, 128)).astype(np.int8)
+    neg = (c < 0) | ((c == 0) & (rng.random(c.shape) < 0.3))
+    codes, n2 = oracle.unpack_int4(oracle.pack_int4(c, neg))
+    assert np.array_equal(codes, c) and np.array_equal(n2, neg)
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.full((1, 8), -8, np.int8), np.ones((1, 8), bool))
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.ones((1, 8), np.int8), np.ones((1, 8), bool))
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.ones((1, 12), np.int8), np.zeros((1, 12), bool))
+
+
+def test_sign_bits_follow_input():
+    x = np.array([[0.0, -0.0, 1.0, -1.0, -1e-8, 1e-8, 3.0, -3.0]], np.float16)
+    assert oracle.int4_sign_bits(x).tolist() == [[False, True, False, True, True, False, False, True]]
 
 
 # ---------------------------------------------------------------- GEMM

@@ -31,10 +31,14 @@ bool gemm_group_ok(int64_t K, int32_t g) {
   return g >= 64 && (g & (g - 1)) == 0 && K % g == 0;
 }
 
+// The finer group bounds the fp32 partials: |P_b| <= 49 g must stay below 2^24
+// for them to be exact integers.
+constexpr int32_t kMaxPartialGroup = 1 << 18;
+
 bool gemm_groups_ok(int64_t K, int32_t ga, int32_t gw) {
   if (!gemm_group_ok(K, ga) || !gemm_group_ok(K, gw)) return false;
   const int32_t lo = ga < gw ? ga : gw, hi = ga < gw ? gw : ga;
-  return hi % lo == 0;
+  return hi % lo == 0 && lo <= kMaxPartialGroup;
 }
 
 w4a4_status_t check_y(void* y, int32_t ydt, int64_t N, int64_t ldy) {

@@ -5,33 +5,41 @@
 // per-group dequantization done by the vector units -- the cost it identifies
 // as the W4A4 bottleneck (its "rho", matrix-unit : vector-unit throughput).
 // On gfx950 the vector unit does 64 fp32 lane-ops per clock per CU against
-// 4096 int8 MACs on the matrix cores (packed fp32 math is not used), so every
-// vector op per output per group matters. Design:
+// 4096 8-bit MACs on the matrix cores (packed fp32 math is not used), so the
+// design moves every piece of the dequantization it can onto the matrix cores
+// and keeps the vector work per output per group at ONE fma:
 //
-//   * gfx950 has no INT4 matrix instruction. Packed int4 tiles are fetched
-//     from HBM/L2 and widened ONCE per workgroup, by the threads that stage
-//     them, into int8 operands in LDS: for a packed dword d (8 codes),
-//     (d << 4) & 0xF0F0F0F0 puts the even codes and d & 0xF0F0F0F0 the odd
-//     codes in the high nibble of each byte, i.e. int8 bytes equal to 16*q
-//     (two's complement preserved). A and W are widened the same way, so each
-//     product carries a factor 256, folded exactly into the fp32 scale (a power
-//     of two), and the k permutation is the same on both sides.
-//   * The waves read MFMA-ready 16-byte operands from LDS and run
-//     v_mfma_i32_32x32x32_i8. A group's partial P_b (times 256) starts from an
-//     inline zero accumulator, so clearing it costs nothing.
-//   * Epilogue per output per group: acc += float(P) * (s_a * s_w / 256) --
-//     one convert, one multiply, one fma, the minimum for an int32 partial
-//     and two fp32 scales.
+//   * gfx950 has no INT4 matrix instruction, but FP8 E4M3 holds every INT4
+//     code exactly: the byte [sign 0000 m] is the subnormal +-m * 2^-9. The
+//     codes are stored sign-magnitude in a layout where a packed word d gives
+//     the 8 operand bytes of its 8 codes as d & 0x87878787 (codes 0..3) and
+//     rotr(d, 4) & 0x87878787 (codes 4..7), in k order. The threads that stage
+//     a tile unpack it ONCE per workgroup into LDS.
+//   * v_mfma_scale_f32_32x32x64_f8f6f4 multiplies them with an E8M0 scale of
+//     2^9 per operand, so each partial P_b = sum qa*qw comes out as an exact
+//     integer in fp32 (|P_b| <= 49 g < 2^24) -- no int->float convert.
+//   * The scale product t[m][n] = s_a[m] * s_w[n] is a rank-1 matrix: one
+//     two-block 32x32x1 fp32 MFMA gives it for two 32x32 tiles, in the lane
+//     layout of the partials.
+//   * Epilogue per output per group: acc = fma(P, t, acc).
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; tile 128 x 128 outputs,
-// K stage 128, double-buffered LDS (76 KB), two workgroups per CU (2 waves per
-// SIMD) so one wave's epilogue overlaps the other's matrix work. Tiles are
-// ordered XCD-contiguous, then in groups of 8 tile-rows, so workgroups running
-// together on one XCD share A and W slices in that XCD's L2.
+// K stage 128 (two MFMA k-steps), double-buffered LDS (76 KB), two workgroups
+// per CU (two waves per SIMD). The staging threads fetch stage kt+2 while
+// stage kt is computed and stage kt+1 is unpacked (two register sets), and the
+// stage barrier orders LDS only, so no wait drains those loads. Within a stage
+// each wave streams its four 32x32 tiles in the order (0,0) (1,0) (1,1) (0,1),
+// issuing a tile's epilogue next to the following tile's MFMAs; with groups of
+// <= 128 only two tiles' partials are live at once. (Measured on gfx950: a wave
+// overlaps little of its own vector work with its own MFMAs; the overlap comes
+// from the other wave on the SIMD.) Tiles are ordered XCD-contiguous, then in
+// groups of 8 tile-rows, so workgroups running together on one XCD share A and
+// W slices in that XCD's L2.
 //
-// v_mfma_i32_32x32x32_i8 lane layout: A/B operand lane l holds row (col) l%32
-// and 16 k of chunk l/32; D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-// col l%32.
+// 32x32 MFMA lane layout: operand lane l holds row (col) l%32 and the k-chunk
+// l/32 (32 consecutive k for FP8); result register r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, col l%32 (block b of the two-block fp32 MFMA in
+// registers 16b .. 16b+15, with operand lanes 32b .. 32b+31).
 #include "device.h"
 #include "launch.h"
 
@@ -39,17 +47,17 @@ namespace w4a4 {
 
 namespace {
 
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int ROW_BYTES = BK / 2;   // packed bytes per row per stage
-constexpr int PITCH = 144;          // LDS bytes per row: 128 int8 + 16 pad (conflict-free 16 B reads)
+constexpr int PITCH = 144;          // LDS bytes per row: 128 FP8 + 16 pad (conflict-free 16 B reads)
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;       // tile-rows per raster group
+constexpr int kUnitScale = 127 + 9; // E8M0 2^9: FP8 [s 0000 m] * 2^9 = +-m
 
-// Group modes: epilogue after every 64-k half (g = 64), after every stage
+// Group modes: epilogue after every 64-k step (g = 64), after every stage
 // (g = 128), or after several stages (g > 128).
 enum { G64 = 0, G128 = 1, GBIG = 2 };
 
@@ -71,16 +79,33 @@ struct Params {
   int32_t* partials;
 };
 
-__device__ __forceinline__ uint32_t even16(uint32_t d) { return (d << 4) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t odd16(uint32_t d) { return d & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t fp8_lo(uint32_t d) { return d & 0x87878787u; }
+__device__ __forceinline__ uint32_t fp8_hi(uint32_t d) { return __builtin_amdgcn_alignbit(d, d, 4) & 0x87878787u; }
 
-// 32 packed codes (16 B) -> two 16-byte int8 operand pieces in LDS.
-__device__ __forceinline__ void widen_store(uint8_t* dst, uint4 v) {
-  *reinterpret_cast<uint4*>(dst) = uint4{even16(v.x), odd16(v.x), even16(v.y), odd16(v.y)};
-  *reinterpret_cast<uint4*>(dst + 16) = uint4{even16(v.z), odd16(v.z), even16(v.w), odd16(v.w)};
+// 32 packed codes (16 B) -> 32 FP8 operand bytes in LDS, k order.
+__device__ __forceinline__ void unpack_store(uint8_t* dst, uint4 v) {
+  *reinterpret_cast<uint4*>(dst) = uint4{fp8_lo(v.x), fp8_hi(v.x), fp8_lo(v.y), fp8_hi(v.y)};
+  *reinterpret_cast<uint4*>(dst + 16) = uint4{fp8_lo(v.z), fp8_hi(v.z), fp8_lo(v.w), fp8_hi(v.w)};
 }
 
-__device__ __forceinline__ v4i as_v4i(uint4 v) { return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}; }
+// 32 FP8 bytes of one lane's operand (row l%32, k-chunk l/32) from LDS.
+__device__ __forceinline__ v8i load_op(const uint8_t* p) {
+  const uint4 x = *reinterpret_cast<const uint4*>(p);
+  const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
+  return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+}
+
+// Workgroup barrier that orders LDS only: __syncthreads() would also wait for
+// every global load in flight, i.e. for the prefetch of later stages.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
 
 template <bool PARTIALS, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -124,125 +149,175 @@ void k_w4a4_gemm(Params p) {
   const int ssh = s_is_a ? p.sha : p.shw;
   float* sS = s_is_a ? &sSA[0][0][srow] : &sSW[0][0][srow];
 
-  uint4 ra0, ra1, rw0, rw1;
-  float rs0, rs1;
-#define GLOAD(KT)                                                     \
+  // Two register sets of staged global data: stage kt+2 is fetched while
+  // stage kt is computed and stage kt+1 (fetched one stage earlier) is
+  // unpacked into LDS, so every load has two stages to land. The g = 64 mode
+  // and the partials export keep one set (one stage ahead) to stay in registers.
+  constexpr int kAhead = (MODE == G64 || PARTIALS) ? 1 : 2;
+  struct Staged {
+    uint4 a0, a1, w0, w1;
+    float s0, s1;
+  };
+#define GLOAD(R, KT)                                                  \
   {                                                                   \
     const int off_ = (KT) * ROW_BYTES;                                \
-    ra0 = *reinterpret_cast<const uint4*>(gA0 + off_);                \
-    ra1 = *reinterpret_cast<const uint4*>(gA1 + off_);                \
-    rw0 = *reinterpret_cast<const uint4*>(gW0 + off_);                \
-    rw1 = *reinterpret_cast<const uint4*>(gW1 + off_);                \
-    rs0 = gS[(2 * (KT)) >> ssh];                                      \
-    rs1 = gS[(2 * (KT) + 1) >> ssh];                                  \
+    R.a0 = *reinterpret_cast<const uint4*>(gA0 + off_);               \
+    R.a1 = *reinterpret_cast<const uint4*>(gA1 + off_);               \
+    R.w0 = *reinterpret_cast<const uint4*>(gW0 + off_);               \
+    R.w1 = *reinterpret_cast<const uint4*>(gW1 + off_);               \
+    R.s0 = gS[(2 * (KT)) >> ssh];                                     \
+    R.s1 = gS[(2 * (KT) + 1) >> ssh];                                 \
   }
-#define LSTORE(BUF)                                                   \
+#define LSTORE(BUF, R)                                                \
   {                                                                   \
-    widen_store(&sA[BUF][st0], ra0);                                  \
-    widen_store(&sA[BUF][st1], ra1);                                  \
-    widen_store(&sW[BUF][st0], rw0);                                  \
-    widen_store(&sW[BUF][st1], rw1);                                  \
-    sS[(BUF) * 2 * BM] = rs0;                                         \
-    sS[(BUF) * 2 * BM + BM] = rs1;                                    \
+    unpack_store(&sA[BUF][st0], R.a0);                                \
+    unpack_store(&sA[BUF][st1], R.a1);                                \
+    unpack_store(&sW[BUF][st0], R.w0);                                \
+    unpack_store(&sW[BUF][st1], R.w1);                                \
+    sS[(BUF) * 2 * BM] = R.s0;                                        \
+    sS[(BUF) * 2 * BM + BM] = R.s1;                                   \
   }
 
-  v16f acc[2][2];
-  v16i P[2][2];
-  const v16i zero16 = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  const v16f zero16 = {};
   const v32f zero32 = {};
+  v16f acc[2][2];
+  v16f P[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      acc[i][j] = zero16;
       P[i][j] = zero16;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     }
 
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-  const int rdA = (wm * 64 + l32) * PITCH + 16 * lhi;   // + i*32*PITCH + 32*s
-  const int rdW = (wn * 64 + l32) * PITCH + 16 * lhi;
+  const int rdA = (wm * 64 + l32) * PITCH + 32 * lhi;   // + i*32*PITCH + 64*s
+  const int rdW = (wn * 64 + l32) * PITCH + 32 * lhi;
   int gcount = 0;     // GBIG: stages accumulated into P since the last epilogue
   int gidx = 0;       // index of the next group to finish (partials export)
 
-  GLOAD(0);
-  LSTORE(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) GLOAD(kt + 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v4i a0 = as_v4i(*reinterpret_cast<const uint4*>(&sA[buf][rdA + 32 * s]));
-      const v4i a1 = as_v4i(*reinterpret_cast<const uint4*>(&sA[buf][rdA + 32 * PITCH + 32 * s]));
-      const v4i w0 = as_v4i(*reinterpret_cast<const uint4*>(&sW[buf][rdW + 32 * s]));
-      const v4i w1 = as_v4i(*reinterpret_cast<const uint4*>(&sW[buf][rdW + 32 * PITCH + 32 * s]));
-      // first k-step of a group starts from an inline zero accumulator
-      const bool fresh = (MODE == G64) ? (s == 0 || s == 2) : (MODE == G128) ? (s == 0) : false;
-      if (fresh) {
-        P[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w0, zero16, 0, 0, 0);
-        P[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w1, zero16, 0, 0, 0);
-        P[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w0, zero16, 0, 0, 0);
-        P[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w1, zero16, 0, 0, 0);
-      } else {
-        P[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w0, P[0][0], 0, 0, 0);
-        P[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, w1, P[0][1], 0, 0, 0);
-        P[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w0, P[1][0], 0, 0, 0);
-        P[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, w1, P[1][1], 0, 0, 0);
-      }
-      bool flush;
-      if (MODE == G64) flush = (s == 1 || s == 3);
-      else if (MODE == G128) flush = (s == 3);
-      else flush = (s == 3) && (gcount + 1 == p.stages_per_group);
-      if (flush) {
-        const int h = s >> 1;   // 64-k half whose scales apply
-        if constexpr (PARTIALS) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int m = tile_m + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-                const int n = tile_n + wn * 64 + j * 32 + l32;
-                if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)
-                  p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = P[i][j][r] >> 8;
-              }
-        } else {
-          // Scale products t[m][n] = s_a[m] * s_w[n] / 256 as a rank-1 matrix
-          // product on the matrix cores: one two-block 32x32x1 fp32 MFMA gives
-          // the 32x32 tiles (i = 0, j) and (i = 1, j), in the same lane/register
-          // layout as the int32 partials. Lane l supplies row l of the wave's 64
-          // A rows (block l / 32) and column 32 j + l % 32 of its W columns.
-          const float av = sSA[buf][h][wm * 64 + lane];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float bv = sSW[buf][h][wn * 64 + 32 * j + l32] * (1.0f / 256.0f);
-            const v32f T = __builtin_amdgcn_mfma_f32_32x32x1f32(av, bv, zero32, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              acc[0][j][r] = fmaf((float)P[0][j][r], T[r], acc[0][j][r]);
-              acc[1][j][r] = fmaf((float)P[1][j][r], T[16 + r], acc[1][j][r]);
-            }
-          }
-        }
-        if (MODE == GBIG) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) P[i][j] = zero16;
-        }
-        ++gidx;
-      }
-    }
-    if (MODE == GBIG) gcount = (gcount + 1 == p.stages_per_group) ? 0 : gcount + 1;
-    if (kt + 1 < nk) LSTORE(buf ^ 1);
-    __syncthreads();
+  // Epilogue of tile (i, j) for group scales T (two-block product, block i).
+#define EPI(I, J, T)                                                                     \
+  {                                                                                      \
+    if constexpr (PARTIALS) {                                                            \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                   \
+        const int m = tile_m + wm * 64 + (I) * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);    \
+        const int n = tile_n + wn * 64 + (J) * 32 + l32;                                 \
+        if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)                \
+          p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] =          \
+              (int32_t)P[I][J][r];                                                       \
+      }                                                                                  \
+    } else {                                                                             \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r)                                     \
+        acc[I][J][r] = fmaf(P[I][J][r], (T)[16 * (I) + r], acc[I][J][r]);                \
+    }                                                                                    \
   }
+  // Scale products for tiles (0, J) and (1, J) from 64-k half H of stage buffer B.
+#define TPROD(B, H, J)                                                                   \
+  __builtin_amdgcn_mfma_f32_32x32x1f32(sSA[B][H][wm * 64 + lane],                        \
+                                       sSW[B][H][wn * 64 + 32 * (J) + l32], zero32, 0, 0, 0)
+
+  // One K stage from LDS buffer BUF: fetch stage min(KT+kAhead, nk-1) into
+  // register set RL, compute, unpack register set RS (stage KT+1) into buffer
+  // BUF^1. The
+  // fetch and the store are unconditional (at the end they repeat the final
+  // stage into the idle buffer): a branch would let the compiler sink the MFMAs
+  // below the store. Phase order is pinned with scheduling barriers: each
+  // tile's epilogue is issued next to the following tile's MFMAs, the unpack
+  // next to the last MFMAs, and the two scale-product blocks are never live
+  // together.
+#define STAGE(KT, BUF, RL, RS)                                                           \
+  {                                                                                      \
+    GLOAD(RL, min((KT) + kAhead, nk - 1));                                               \
+    const uint8_t* bA = &sA[BUF][rdA];                                                   \
+    const uint8_t* bW = &sW[BUF][rdW];                                                   \
+    v8i a[2][2], b[2][2];   /* [tile row i / col j][k-step s] */                         \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                        \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                      \
+      a[i][s] = load_op(bA + i * 32 * PITCH + 64 * s);                                   \
+      b[i][s] = load_op(bW + i * 32 * PITCH + 64 * s);                                   \
+    }                                                                                    \
+    if constexpr (MODE == G64) {                                                         \
+      _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
+        const v32f T0 = TPROD(BUF, s, 0);                                                \
+        P[0][0] = mma(a[0][s], b[0][s], zero16);                                         \
+        P[1][0] = mma(a[1][s], b[0][s], zero16);                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        EPI(0, 0, T0);                                                                   \
+        P[1][1] = mma(a[1][s], b[1][s], zero16);                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        EPI(1, 0, T0);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        const v32f T1 = TPROD(BUF, s, 1);                                                \
+        P[0][1] = mma(a[0][s], b[1][s], zero16);                                         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        EPI(1, 1, T1);                                                                   \
+        if (s == 1) LSTORE((BUF) ^ 1, RS);                                               \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        EPI(0, 1, T1);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        ++gidx;                                                                          \
+      }                                                                                  \
+    } else if constexpr (MODE == G128) {                                                 \
+      const v32f T0 = TPROD(BUF, 0, 0);                                                  \
+      P[0][0] = mma(a[0][1], b[0][1], mma(a[0][0], b[0][0], zero16));                    \
+      P[1][0] = mma(a[1][1], b[0][1], mma(a[1][0], b[0][0], zero16));                    \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      EPI(0, 0, T0);                                                                     \
+      P[1][1] = mma(a[1][1], b[1][1], mma(a[1][0], b[1][0], zero16));                    \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      EPI(1, 0, T0);                                                                     \
+      const v32f T1 = TPROD(BUF, 0, 1);                                                  \
+      P[0][1] = mma(a[0][1], b[1][1], mma(a[0][0], b[1][0], zero16));                    \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      EPI(1, 1, T1);                                                                     \
+      LSTORE((BUF) ^ 1, RS);                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      EPI(0, 1, T1);                                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      ++gidx;                                                                            \
+    } else {                                                                             \
+      /* partials accumulate over stages_per_group stages, then one epilogue */          \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                      \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                      \
+        P[i][j] = mma(a[i][1], b[j][1], mma(a[i][0], b[j][0], P[i][j]));                 \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      LSTORE((BUF) ^ 1, RS);                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      if (++gcount == p.stages_per_group) {                                              \
+        const v32f T0 = TPROD(BUF, 0, 0);                                                \
+        EPI(0, 0, T0);                                                                   \
+        EPI(1, 0, T0);                                                                   \
+        const v32f T1 = TPROD(BUF, 0, 1);                                                \
+        EPI(0, 1, T1);                                                                   \
+        EPI(1, 1, T1);                                                                   \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                    \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) P[i][j] = zero16;                  \
+        gcount = 0;                                                                      \
+        ++gidx;                                                                          \
+      }                                                                                  \
+    }                                                                                    \
+    lds_barrier();                                                                       \
+  }
+
+  Staged R0, R1;
+  Staged& RX = (kAhead == 2) ? R1 : R0;
+  GLOAD(R0, 0);
+  LSTORE(0, R0);
+  if constexpr (kAhead == 2) GLOAD(R1, min(1, nk - 1));
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    STAGE(kt, 0, R0, RX);
+    STAGE(kt + 1, 1, RX, R0);
+  }
+  if (kt < nk) STAGE(kt, 0, R0, RX);
 #undef GLOAD
 #undef LSTORE
+#undef EPI
+#undef TPROD
+#undef STAGE
 
   if constexpr (!PARTIALS) {
 #pragma unroll

@@ -3,7 +3,12 @@
 // INT4 (APEX4, abstract: W4A4-g128 activations quantized per group of 128 along
 // K; other group sizes for its mixed-granularity mode). Per group:
 //   a = max|x|, s = fl32(a / 7), q = clamp(rne(fl32(x / s)), -8, 7), s = 0 and
-//   q = 0 for an all-zero group; two codes per byte, even k in the low nibble.
+//   q = 0 for an all-zero group. The rule only yields q in [-7, 7], stored
+//   sign-magnitude: each 32-bit word holds the codes c0..c7 of 8 consecutive k;
+//   byte b holds sign(c_b) in bit 7, |c_b| in bits 2..0, |c_(4+b)| in bits 6..4
+//   and sign(c_(4+(b+3)%4)) in bit 3, the sign bit being that of the input value.
+//   The GEMM turns a word into 8 FP8 E4M3 operand bytes with two masks and one
+//   rotate.
 // MXFP4 (the open-standard MXFP4 of the FP4 RL abstract; OCP MX v1.0 block
 // rule): per 32 elements E = floor(log2 a) - 2, codes = E2M1(x / 2^E) with
 // ties to even and saturation at 6, E8M0 byte E + 127.
@@ -20,9 +25,9 @@
 //     J. Res. Dev. 34(1), 1990). The GPU parity tests check it against the
 //     oracle's IEEE divisions over every (absmax, x) pair of fp16 values.
 //   * s = RN(a/7) the same way with r7 = RN(1/7).
-//   * rne + clamp: t is clamped to [-8, 7] and 2^23 + 8 is added; binary32
-//     spacing is 1 on [2^23, 2^24), so the add rounds half-to-even and the low
-//     4 bits hold q + 8; XOR 8 turns that into the two's complement nibble.
+//   * rne + clamp on the magnitude: RNE is symmetric, so |q| = rne(|x| / s);
+//     t = |x|/s is clamped to [0, 7] and 2^23 is added (binary32 spacing is 1 on
+//     [2^23, 2^24), so the add rounds half-to-even) leaving |q| in the low bits.
 #include "device.h"
 #include "launch.h"
 
@@ -32,7 +37,7 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 constexpr int kRowsPerThread = 4;   // independent 16-byte loads in flight per lane
-constexpr float kMagic = 8388616.0f;    // 2^23 + 8
+constexpr float kMagic = 8388608.0f;    // 2^23
 
 // Correctly rounded x / d given r = RN(1/d) (d normal, no overflow/underflow).
 __device__ __forceinline__ float div_rn(float x, float d, float r) {
@@ -41,20 +46,25 @@ __device__ __forceinline__ float div_rn(float x, float d, float r) {
   return fmaf(e, r, q0);
 }
 
-// (q + 8) in the low 4 bits of the returned word, q = clamp(rne(t), -8, 7).
-__device__ __forceinline__ uint32_t biased_code(float t) {
-  return __float_as_uint(__builtin_amdgcn_fmed3f(t, -8.0f, 7.0f) + kMagic);
+// |q| = min(rne(t), 7) for t >= 0, in the low 3 bits of the returned word.
+__device__ __forceinline__ uint32_t mag_code(float t) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(t, 0.0f, 7.0f) + kMagic);
 }
 
-// 8 biased codes -> one packed dword of two's complement nibbles (low nibble first).
-__device__ __forceinline__ uint32_t pack8(const uint32_t u[8]) {
-  const uint32_t p01 = (u[1] << 4) | (u[0] & 0xFFu);
-  const uint32_t p23 = (u[3] << 4) | (u[2] & 0xFFu);
-  const uint32_t p45 = (u[5] << 4) | (u[4] & 0xFFu);
-  const uint32_t p67 = (u[7] << 4) | (u[6] & 0xFFu);
-  const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x0C0C0400u);   // [p01.b0, p23.b0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(p67, p45, 0x04000C0Cu);   // [0, 0, p45.b0, p67.b0]
-  return lo ^ hi ^ 0x88888888u;
+// 8 magnitudes (low bits of m[]) and the 8 fp16 inputs they came from -> one
+// sign-magnitude word (layout in the file header).
+__device__ __forceinline__ uint32_t pack8(const uint32_t m[8], uint4 raw) {
+  const uint32_t p0 = (m[4] << 4) | m[0];     // byte 0 = |c0| | |c4| << 4
+  const uint32_t p1 = (m[5] << 4) | m[1];
+  const uint32_t p2 = (m[6] << 4) | m[2];
+  const uint32_t p3 = (m[7] << 4) | m[3];
+  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);    // [p0.b0, p1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);    // [0, 0, p2.b0, p3.b0]
+  // high byte of each fp16 input: bit 7 = its sign
+  const uint32_t s_lo = __builtin_amdgcn_perm(raw.y, raw.x, 0x07050301u);   // x0..x3
+  const uint32_t s_hi = __builtin_amdgcn_perm(raw.w, raw.z, 0x07050301u);   // x4..x7
+  const uint32_t s_hi_rot = __builtin_amdgcn_alignbit(s_hi, s_hi, 28);      // rotl 4: byte b bit 7 -> byte b+1 bit 3
+  return (lo | hi) | (s_lo & 0x80808080u) | (s_hi_rot & 0x08080808u);
 }
 
 // Group scale and its reciprocal (r = 0 for an all-zero group so every code is 0).
@@ -64,11 +74,11 @@ __device__ __forceinline__ void group_scale(float a, float& s, float& r) {
   r = (s == 0.0f) ? 0.0f : 1.0f / s;     // correctly rounded division
 }
 
-__device__ __forceinline__ uint32_t int4_codes8(const float f[8], float s, float r) {
-  uint32_t u[8];
+__device__ __forceinline__ uint32_t int4_codes8(const float f[8], uint4 raw, float s, float r) {
+  uint32_t m[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = biased_code(div_rn(f[i], s, r));
-  return pack8(u);
+  for (int i = 0; i < 8; ++i) m[i] = mag_code(div_rn(fabsf(f[i]), s, r));
+  return pack8(m, raw);
 }
 
 // Lane mapping of the 2-D grid: a block is kQuantThreads lanes = (256 / W) row
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
       a = group_max<LPG>(a);
       float sc, rc;
       group_scale(a, sc, rc);
-      q[(int64_t)row * cpr + mp.col] = int4_codes8(f, sc, rc);
+      q[(int64_t)row * cpr + mp.col] = int4_codes8(f, raw[u], sc, rc);
       if ((threadIdx.x & (LPG - 1)) == 0) s[(int64_t)row * (cpr / LPG) + mp.col / LPG] = sc;
     }
   }
@@ -143,9 +153,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
   float sc, rc;
   group_scale(a, sc, rc);
   for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(xr + c * 8);
     float f[8];
-    halves_to_float8(*reinterpret_cast<const uint4*>(xr + c * 8), f);
-    q[(int64_t)row * cpr + c] = int4_codes8(f, sc, rc);
+    halves_to_float8(raw, f);
+    q[(int64_t)row * cpr + c] = int4_codes8(f, raw, sc, rc);
   }
   if (threadIdx.x == 0) s[row] = sc;
 }

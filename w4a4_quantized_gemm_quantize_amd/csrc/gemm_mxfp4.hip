@@ -7,13 +7,16 @@
 // consecutive K codes (16 bytes) of row l%32, 32-block l/32, and the E8M0 byte
 // of exactly that block, so the block scales are applied inside the
 // instruction and accumulation is fp32 with no vector-unit epilogue. The kernel
-// is therefore matrix-core bound, and is tiled for that: each wave owns a
-// (BM/WM) x (BN/WN) output tile; the launch uses 128 x 128 workgroup tiles of
-// 2 x 2 waves, two workgroups per CU (2 waves per SIMD).
+// is tiled for the matrix cores: each wave owns a (BM/WM) x (BN/WN) output
+// tile. The launch uses 256 x 128 workgroup tiles of 4 x 2 waves with 256-deep
+// K stages (one workgroup per CU, 2 waves per SIMD) when K % 256 == 0, else
+// 128 x 128 tiles of 2 x 2 waves with 128-deep stages. Measured on gfx950 the
+// kernel is bound by L2 request traffic (L2 busy ~96 %); the larger tile and
+// the line-sized row pieces of the deeper stage cut requests per flop.
 //
-// K stage 128 (64 packed bytes per row), fed through a 3-stage LDS ring by
-// direct global->LDS loads (no staging registers), so two stages of loads are
-// in flight behind the matrix work. The debug-partials variant runs
+// Stages are fed through a 3-stage LDS ring by direct global->LDS loads (no
+// staging registers), so two stages of loads are in flight behind the matrix
+// work. The debug-partials variant runs
 // the same instruction one 32-block at a time with unit scales.
 //
 // 32x32 MFMA output layout: D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
@@ -27,8 +30,6 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 128;
-constexpr int ROW_BYTES = BK / 2;
 constexpr int kThreads = 256;
 constexpr int kFmtFp4 = 4;       // cbsz / blgp operand format code for FP4 E2M1
 constexpr int kUnitScale = 127;  // E8M0 byte of 2^0
@@ -71,26 +72,36 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Workgroup tile BM x BN; waves in a 2 x 2 grid, each (BM/2) x (BN/2) = TI x TJ
-// blocks of 32 x 32. S-stage LDS ring filled by direct global->LDS loads: stage
-// kt+S-1 is in flight while stage kt is computed. A stage holds BM + BN rows of
-// 64 bytes (row-major, no pad: each 16-row chunk is one wave-wide 1 KB load)
-// and one E8M0 dword per row. The 16-byte slot of a row is XOR-swizzled with
-// (row >> 3) & 3 so the 32 lanes of each half-wave that read one slot of 32
-// consecutive rows hit 32 distinct bank groups.
-template <int BM, int BN, int WM, int WN, bool PARTIALS>
+// Workgroup tile BM x BN; waves in a WM x WN grid, each (BM/WM) x (BN/WN) =
+// TI x TJ blocks of 32 x 32; K stage KB (128 or 256). S-stage LDS ring filled by
+// direct global->LDS loads: stage kt+S-1 is in flight while stage kt is
+// computed. A stage holds BM + BN rows of RB = KB/2 packed bytes (row-major, no
+// pad: each wave-wide 1 KB load covers 1024/RB rows) and KB/128 E8M0 dwords per
+// row. A 256-deep stage makes each row's piece a whole 128-byte line, so the L2
+// serves line-sized requests instead of 64-byte halves. The SL = RB/16 slots of
+// a row are XOR-swizzled with (row >> log2(32/SL)) & (SL-1) so the 32 lanes of a
+// half-wave that read one slot of 32 consecutive rows hit 32 distinct bank
+// groups.
+template <int BM, int BN, int WM, int WN, int KB, bool PARTIALS>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_mxfp4_gemm(Params p) {
   constexpr int S = 3;                              // ring depth
   constexpr int NWAVE = WM * WN;
+  constexpr int RB = KB / 2;                        // packed bytes per row per stage
+  constexpr int SL = RB / 16;                       // 16-byte slots per row
+  constexpr int RPK = 1024 / RB;                    // rows per 1 KB load
+  constexpr int SWS = SL == 4 ? 3 : 2;              // log2(32 / SL)
+  constexpr int NSTEP = KB / 64;                    // MFMA k-steps per stage
+  constexpr int NEW = KB / 128;                     // E8M0 dwords per row per stage
   constexpr int TI = BM / WM / 32, TJ = BN / WN / 32;   // 32x32 blocks per wave
-  constexpr int NA = BM / 16 / NWAVE, NW = BN / 16 / NWAVE;   // 1 KB loads per wave per stage
-  constexpr int NE = (BM + BN + 64 * NWAVE - 1) / (64 * NWAVE); // scale-dword loads per wave
-  constexpr int W_OFF = BM * ROW_BYTES;
-  constexpr int E_OFF = (BM + BN) * ROW_BYTES;
+  constexpr int NA = BM / RPK / NWAVE, NW = BN / RPK / NWAVE;   // 1 KB loads per wave per stage
+  constexpr int NE = (NEW * (BM + BN) + 64 * NWAVE - 1) / (64 * NWAVE); // scale-dword loads per wave
+  constexpr int W_OFF = BM * RB;
+  constexpr int E_OFF = (BM + BN) * RB;
   constexpr int STAGE = E_OFF + NE * NWAVE * 64 * 4;
   constexpr int PER_STAGE = NA + NW + NE;           // load instructions per wave per stage
-  static_assert(NA * 16 * NWAVE == BM && NW * 16 * NWAVE == BN, "tile rows per wave");
+  static_assert(KB == 128 || KB == 256, "stage depth");
+  static_assert(NA * RPK * NWAVE == BM && NW * RPK * NWAVE == BN, "tile rows per wave");
   // One array per ring slot (the loop is unrolled by S, so every access names
   // its slot): the compiler can then tell an in-flight load into one slot from
   // LDS reads of another and does not wait for it.
@@ -115,41 +126,44 @@ void k_mxfp4_gemm(Params p) {
   const int wm = wave / WN, wn = wave % WN;
   const int row_bytes = p.K >> 1;
   const int row_scales = p.K >> 5;
-  const int nk = p.K / BK;
+  const int nk = p.K / KB;
 
   // ---- per-lane sources of this wave's loads (stage 0); LDS offsets are per wave
   const uint8_t* srcA[NA];
   const uint8_t* srcW[NW];
   const uint8_t* srcE[NE];
-  const int lrow = lane >> 2, lslot = lane & 3;
+  const int lrow = lane / SL, lslot = lane % SL;
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int row = 16 * (wave + NWAVE * i) + lrow;
-    const int seg = lslot ^ ((row >> 3) & 3);
+    const int row = RPK * (wave + NWAVE * i) + lrow;
+    const int seg = lslot ^ ((row >> SWS) & (SL - 1));
     srcA[i] = p.a + (int64_t)min(tile_m + row, p.M - 1) * row_bytes + 16 * seg;
   }
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const int row = 16 * (wave + NWAVE * i) + lrow;
-    const int seg = lslot ^ ((row >> 3) & 3);
+    const int row = RPK * (wave + NWAVE * i) + lrow;
+    const int seg = lslot ^ ((row >> SWS) & (SL - 1));
     srcW[i] = p.w + (int64_t)min(tile_n + row, p.N - 1) * row_bytes + 16 * seg;
   }
+  // scale dword e = w * (BM + BN) + r: dword w of this stage's scales of A row r
+  // (r < BM) or W row r - BM
 #pragma unroll
   for (int j = 0; j < NE; ++j) {
-    const int slot = 64 * (NE * wave + j) + lane;
-    srcE[j] = slot < BM ? p.ea + (int64_t)min(tile_m + slot, p.M - 1) * row_scales
-            : slot < BM + BN ? p.ew + (int64_t)min(tile_n + slot - BM, p.N - 1) * row_scales
-                             : p.ea;   // unused slot: a harmless in-bounds read
+    const int e = 64 * (NE * wave + j) + lane;
+    const int w = e / (BM + BN), r = e % (BM + BN);
+    srcE[j] = e >= NEW * (BM + BN) ? p.ea   // unused slot: a harmless in-bounds read
+            : r < BM ? p.ea + (int64_t)min(tile_m + r, p.M - 1) * row_scales + 4 * w
+                     : p.ew + (int64_t)min(tile_n + r - BM, p.N - 1) * row_scales + 4 * w;
   }
 #define ISSUE(KT, SM)                                                                \
   {                                                                                  \
     uint8_t* base_ = (SM);                                                           \
     _Pragma("unroll") for (int i = 0; i < NA; ++i)                                   \
-        dma16(srcA[i] + (KT) * ROW_BYTES, base_ + (wave + NWAVE * i) * 1024);      \
+        dma16(srcA[i] + (KT) * RB, base_ + (wave + NWAVE * i) * 1024);             \
     _Pragma("unroll") for (int i = 0; i < NW; ++i)                                   \
-        dma16(srcW[i] + (KT) * ROW_BYTES, base_ + W_OFF + (wave + NWAVE * i) * 1024); \
+        dma16(srcW[i] + (KT) * RB, base_ + W_OFF + (wave + NWAVE * i) * 1024);     \
     _Pragma("unroll") for (int j = 0; j < NE; ++j)                                   \
-        dma4(srcE[j] + (KT) * 4, base_ + E_OFF + (NE * wave + j) * 256);           \
+        dma4(srcE[j] + (KT) * 4 * NEW, base_ + E_OFF + (NE * wave + j) * 256);     \
   }
 
   v16f acc[TI][TJ];
@@ -164,29 +178,30 @@ void k_mxfp4_gemm(Params p) {
   const int lhi = lane >> 5;
   const int rowA = wm * (BM / WM) + l32;
   const int rowW = wn * (BN / WN) + l32;
-  int offA[2], offW[2];
+  int offA[NSTEP], offW[NSTEP];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    offA[u] = rowA * ROW_BYTES + 16 * ((2 * u + lhi) ^ ((rowA >> 3) & 3));
-    offW[u] = rowW * ROW_BYTES + 16 * ((2 * u + lhi) ^ ((rowW >> 3) & 3));
+  for (int u = 0; u < NSTEP; ++u) {
+    offA[u] = rowA * RB + 16 * ((2 * u + lhi) ^ ((rowA >> SWS) & (SL - 1)));
+    offW[u] = rowW * RB + 16 * ((2 * u + lhi) ^ ((rowW >> SWS) & (SL - 1)));
   }
   uint4 av[TI], wv[TJ];     // one 64-k step's operands (FP4: 16 bytes per lane)
   int ea[TI], ew[TJ];
 
 // Operands of one 64-k MFMA step U from ring slot SM: lane l feeds 32-block
-// 2U + l/32 of its row and that block's E8M0 byte. (row + 32 i) >> 3 & 3 equals
-// row >> 3 & 3, so one swizzled base per step serves every row block i.
+// 2U + l/32 of the stage in its row and that block's E8M0 byte (byte
+// 2 (U % 2) + l/32 of the row's scale dword U / 2). The swizzle term of row
+// + 32 i equals that of row, so one base per step serves every row block i.
 #define LOAD_OPS(SM, U)                                                               \
   {                                                                                  \
     const uint8_t* st_ = (SM);                                                       \
-    const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF);            \
+    const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF) + ((U) / 2) * (BM + BN); \
     _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                 \
-      av[i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 2048 * i);            \
-      ea[i] = (int)((se_[rowA + 32 * i] >> (8 * (2 * (U) + lhi))) & 0xFFu);          \
+      av[i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 32 * RB * i);         \
+      ea[i] = (int)((se_[rowA + 32 * i] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu);    \
     }                                                                                \
     _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                 \
-      wv[j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 2048 * j);    \
-      ew[j] = (int)((se_[BM + rowW + 32 * j] >> (8 * (2 * (U) + lhi))) & 0xFFu);     \
+      wv[j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 32 * RB * j); \
+      ew[j] = (int)((se_[BM + rowW + 32 * j] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
   }
 // Matrix work of step U of stage KT. The partials variant runs one 32-block at
@@ -196,7 +211,7 @@ void k_mxfp4_gemm(Params p) {
     if constexpr (PARTIALS) {                                                        \
       const v8i zero_ = v8i{0, 0, 0, 0, 0, 0, 0, 0};                                 \
       _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                \
-        const int gblk = 4 * (KT) + 2 * (U) + h;                                     \
+        const int gblk = (KB / 32) * (KT) + 2 * (U) + h;                             \
         _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
         _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                             \
           v16f zacc;                                                                 \
@@ -242,8 +257,10 @@ void k_mxfp4_gemm(Params p) {
     LOAD_OPS(CUR, 0);                                                   \
     if ((KT) + 2 < nk) ISSUE((KT) + 2, NXT);                            \
     MMA_STEP(KT, 0);                                                    \
-    LOAD_OPS(CUR, 1);                                                   \
-    MMA_STEP(KT, 1);                                                    \
+    _Pragma("unroll") for (int u_ = 1; u_ < NSTEP; ++u_) {              \
+      LOAD_OPS(CUR, u_);                                                \
+      MMA_STEP(KT, u_);                                                 \
+    }                                                                   \
   }
 
   ISSUE(0, sm0);
@@ -281,14 +298,24 @@ void k_mxfp4_gemm(Params p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool PARTIALS>
+template <int BM, int BN, int WM, int WN, int KB, bool PARTIALS>
 void launch_cfg(Params p, const GemmArgs& g, hipStream_t stream) {
   p.tile_m0 = (int)(g.m0 / BM);
   p.tile_n0 = (int)(g.n0 / BN);
   p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
   p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
-  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, PARTIALS>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, KB, PARTIALS>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
                      dim3(64 * WM * WN), 0, stream, p);
+}
+
+// 256 x 128 tiles (8 waves) with 256-deep stages when K allows, else 128 x 128
+// with 128-deep stages.
+template <bool PARTIALS>
+void launch_for(Params p, const GemmArgs& g, hipStream_t stream) {
+  if (g.K % 256 == 0)
+    launch_cfg<256, 128, 4, 2, 256, PARTIALS>(p, g, stream);
+  else
+    launch_cfg<128, 128, 2, 2, 128, PARTIALS>(p, g, stream);
 }
 
 }  // namespace
@@ -310,11 +337,10 @@ void launch_mxfp4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.n0 = (int)g.n0;
   p.nc = (int)g.nc;
   p.partials = g.partials;
-  if (g.partials) {
-    launch_cfg<128, 128, 2, 2, true>(p, g, stream);
-    return;
-  }
-  launch_cfg<128, 128, 2, 2, false>(p, g, stream);
+  if (g.partials)
+    launch_for<true>(p, g, stream);
+  else
+    launch_for<false>(p, g, stream);
 }
 
 }  // namespace w4a4

@@ -103,11 +103,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+struct GroupScales {
+  v32f t;          // s_a x s_w for two 32x32 tiles (unused with per-row A scales)
+  float sw0, sw1;  // the lane's W scales of column blocks 0 and 1 (per-row A scales)
+};
+
 __device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
 }
 
-template <bool PARTIALS, int MODE>
+// ROWA: one activation scale per row (group_a == K, the per-token end of the
+// mixed-granularity mode). Then s_a[m] is common to every group and factors
+// out of the sum: the epilogue is acc = fma(P, s_w[n], acc) with s_w[n] a
+// per-lane constant (no scale-product MFMA) and the store multiplies by s_a[m].
+template <bool PARTIALS, int MODE, bool ROWA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_w4a4_gemm(Params p) {
   __shared__ __align__(16) uint8_t sA[2][BM * PITCH];
@@ -208,15 +217,22 @@ void k_w4a4_gemm(Params p) {
           p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] =          \
               (int32_t)P[I][J][r];                                                       \
       }                                                                                  \
+    } else if constexpr (ROWA) {                                                         \
+      const float swj_ = (J) == 0 ? (T).sw0 : (T).sw1;                                   \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r)                                     \
+        acc[I][J][r] = fmaf(P[I][J][r], swj_, acc[I][J][r]);                             \
     } else {                                                                             \
       _Pragma("unroll") for (int r = 0; r < 16; ++r)                                     \
-        acc[I][J][r] = fmaf(P[I][J][r], (T)[16 * (I) + r], acc[I][J][r]);                \
+        acc[I][J][r] = fmaf(P[I][J][r], (T).t[16 * (I) + r], acc[I][J][r]);              \
     }                                                                                    \
   }
-  // Scale products for tiles (0, J) and (1, J) from 64-k half H of stage buffer B.
+  // Group scales for tiles (0, J) and (1, J) from 64-k half H of stage buffer B:
+  // the two-block product s_a x s_w, or (ROWA) the lane's two W scales.
 #define TPROD(B, H, J)                                                                   \
-  __builtin_amdgcn_mfma_f32_32x32x1f32(sSA[B][H][wm * 64 + lane],                        \
-                                       sSW[B][H][wn * 64 + 32 * (J) + l32], zero32, 0, 0, 0)
+  GroupScales{ROWA ? zero32 : __builtin_amdgcn_mfma_f32_32x32x1f32(                      \
+                   sSA[B][H][wm * 64 + lane], sSW[B][H][wn * 64 + 32 * (J) + l32], zero32, 0, 0, 0), \
+               ROWA ? sSW[B][H][wn * 64 + l32] : 0.0f,                                   \
+               ROWA ? sSW[B][H][wn * 64 + 32 + l32] : 0.0f}
 
   // One K stage from LDS buffer BUF: fetch stage min(KT+kAhead, nk-1) into
   // register set RL, compute, unpack register set RS (stage KT+1) into buffer
@@ -240,7 +256,7 @@ void k_w4a4_gemm(Params p) {
     }                                                                                    \
     if constexpr (MODE == G64) {                                                         \
       _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
-        const v32f T0 = TPROD(BUF, s, 0);                                                \
+        const GroupScales T0 = TPROD(BUF, s, 0);                                         \
         P[0][0] = mma(a[0][s], b[0][s], zero16);                                         \
         P[1][0] = mma(a[1][s], b[0][s], zero16);                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
@@ -249,7 +265,7 @@ void k_w4a4_gemm(Params p) {
         __builtin_amdgcn_sched_barrier(0);                                               \
         EPI(1, 0, T0);                                                                   \
         __builtin_amdgcn_sched_barrier(0);                                               \
-        const v32f T1 = TPROD(BUF, s, 1);                                                \
+        const GroupScales T1 = TPROD(BUF, s, 1);                                         \
         P[0][1] = mma(a[0][s], b[1][s], zero16);                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         EPI(1, 1, T1);                                                                   \
@@ -260,7 +276,7 @@ void k_w4a4_gemm(Params p) {
         ++gidx;                                                                          \
       }                                                                                  \
     } else if constexpr (MODE == G128) {                                                 \
-      const v32f T0 = TPROD(BUF, 0, 0);                                                  \
+      const GroupScales T0 = TPROD(BUF, 0, 0);                                           \
       P[0][0] = mma(a[0][1], b[0][1], mma(a[0][0], b[0][0], zero16));                    \
       P[1][0] = mma(a[1][1], b[0][1], mma(a[1][0], b[0][0], zero16));                    \
       __builtin_amdgcn_sched_barrier(0);                                                 \
@@ -268,7 +284,7 @@ void k_w4a4_gemm(Params p) {
       P[1][1] = mma(a[1][1], b[1][1], mma(a[1][0], b[1][0], zero16));                    \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       EPI(1, 0, T0);                                                                     \
-      const v32f T1 = TPROD(BUF, 0, 1);                                                  \
+      const GroupScales T1 = TPROD(BUF, 0, 1);                                           \
       P[0][1] = mma(a[0][1], b[1][1], mma(a[0][0], b[1][0], zero16));                    \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       EPI(1, 1, T1);                                                                     \
@@ -286,10 +302,10 @@ void k_w4a4_gemm(Params p) {
       LSTORE((BUF) ^ 1, RS);                                                             \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       if (++gcount == p.stages_per_group) {                                              \
-        const v32f T0 = TPROD(BUF, 0, 0);                                                \
+        const GroupScales T0 = TPROD(BUF, 0, 0);                                         \
         EPI(0, 0, T0);                                                                   \
         EPI(1, 0, T0);                                                                   \
-        const v32f T1 = TPROD(BUF, 0, 1);                                                \
+        const GroupScales T1 = TPROD(BUF, 0, 1);                                         \
         EPI(0, 1, T1);                                                                   \
         EPI(1, 1, T1);                                                                   \
         _Pragma("unroll") for (int i = 0; i < 2; ++i)                                    \
@@ -329,10 +345,11 @@ void k_w4a4_gemm(Params p) {
           const int m = tile_m + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
           const int n = tile_n + wn * 64 + j * 32 + l32;
           if (m < p.M && n < p.N) {
+            const float v = ROWA ? acc[i][j][r] * p.sa[(int64_t)m * p.ksa] : acc[i][j][r];
             if (p.ydtype == 0)
-              static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i][j][r];
+              static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = v;
             else
-              static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
+              static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(v);
           }
         }
   }
@@ -346,12 +363,12 @@ int scale_shift(int64_t group, int64_t K) {
   return s;
 }
 
-template <bool PARTIALS>
+template <bool PARTIALS, bool ROWA>
 void launch_mode(int mode, const Params& p, dim3 grid, hipStream_t stream) {
   switch (mode) {
-    case G64: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G64>), grid, dim3(kThreads), 0, stream, p); return;
-    case G128: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G128>), grid, dim3(kThreads), 0, stream, p); return;
-    default: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, GBIG>), grid, dim3(kThreads), 0, stream, p); return;
+    case G64: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G64, ROWA>), grid, dim3(kThreads), 0, stream, p); return;
+    case G128: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G128, ROWA>), grid, dim3(kThreads), 0, stream, p); return;
+    default: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, GBIG, ROWA>), grid, dim3(kThreads), 0, stream, p); return;
   }
 }
 
@@ -387,9 +404,11 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   if (g.partials)
-    launch_mode<true>(mode, p, grid, stream);
+    launch_mode<true, false>(mode, p, grid, stream);
+  else if (g.ga == g.K)
+    launch_mode<false, true>(mode, p, grid, stream);
   else
-    launch_mode<false>(mode, p, grid, stream);
+    launch_mode<false, false>(mode, p, grid, stream);
 }
 
 }  // namespace w4a4

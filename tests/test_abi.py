@@ -88,6 +88,9 @@ def test_gemm_validation(lib):
     assert g(P, P, 128, P, P, 192, M, N, 384, P, 0, N, None) == E_GROUP       # 192 not a power of two
     assert g(P, P, 256, P, P, 384, M, N, 768, P, 0, N, None) == E_GROUP       # not nested
     assert g(P, P, 512, P, P, 128, M, N, K, P, 0, N, None) == E_GROUP         # 512 !| 256
+    # the finer group bounds the fp32 partials: 49 g must stay below 2^24
+    big = 1 << 19
+    assert g(P, P, big, P, P, big, M, N, big, P, 0, N, None) == E_GROUP       # per token, g = 2^19
     assert g(P, P, 128, P, P, 128, 0, N, K, None, 0, N, None) == OK           # empty
     assert g(P, P, 128, P, P, 128, M, 0, K, None, 0, 0, None) == OK
     assert g(None, P, 128, P, P, 128, M, N, K, P, 0, N, None) == E_NULL

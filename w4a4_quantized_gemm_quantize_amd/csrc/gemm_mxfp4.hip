@@ -265,13 +265,17 @@ void k_mxfp4_gemm(Params p) {
 
   ISSUE(0, sm0);
   if (nk > 1) ISSUE(1, sm1);
-  int slot = 0;      // kt % S
-  for (int kt = 0; kt < nk; ++kt) {
-    // a uniform branch picks the slot, so each path names its arrays statically
-    if (slot == 0) ITER(kt, sm0, sm2)
-    else if (slot == 1) ITER(kt, sm1, sm0)
-    else ITER(kt, sm2, sm1)
-    slot = (slot == S - 1) ? 0 : slot + 1;
+  // Unrolled by the ring depth, so every stage names its slot statically and
+  // the loop has one back edge: the accumulators stay in the registers the
+  // matrix instructions write, with no copies between stages.
+  static_assert(S == 3, "the unrolled loop below names three slots");
+  for (int kt = 0;; kt += S) {
+    ITER(kt, sm0, sm2)
+    if (kt + 1 >= nk) break;
+    ITER(kt + 1, sm1, sm0)
+    if (kt + 2 >= nk) break;
+    ITER(kt + 2, sm2, sm1)
+    if (kt + 3 >= nk) break;
   }
 #undef ITER
 #undef STAGE_BARRIER

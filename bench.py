@@ -167,7 +167,7 @@ def main() -> int:
         else:
             wq, ws = ops.mxfp4_quantize(w)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-            xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M * (K // 32),), dtype=torch.uint8, device=dev)
         del w
         y = torch.empty((M, N), dtype=ydt, device=dev)
         layers.append(dict(K=K, N=N, x=x, wq=wq, ws=ws, xq=xq, xs=xs, y=y))

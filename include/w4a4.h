@@ -137,7 +137,12 @@ w4a4_status_t w4a4_gemm_debug_partials(const uint8_t* xq, const float* xs, int32
  *
  *   x     fp16 [rows][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0; K % 32 == 0
  *   q     out: u8 [rows][K/2] packed E2M1 codes, 4-byte aligned
- *   e8m0  out: u8 [rows][K/32] scale bytes
+ *   e8m0  out: u8, rows * K/32 scale bytes in 256-k panels: with nb = K/32 and
+ *         w_p = min(8, nb - 8p), the scale of row r and block b (p = b / 8) is
+ *         at byte 8 * rows * p + w_p * r + b % 8. Panel p thus holds, row after
+ *         row, the w_p scale bytes of blocks 8p .. 8p + w_p - 1, and a GEMM
+ *         stage of 256 k reads one contiguous run per tile instead of one
+ *         small piece per row. (K % 256 == 0: every panel is rows x 8 bytes.)
  * Used for activations online and for weights offline.
  */
 w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
@@ -148,8 +153,9 @@ w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx
  *   Y[m,n] = sum_b 2^(Ea[m,b] + Ew[n,b]) * sum_{k in block b} va[m,k] * vw[n,k]
  * accumulated in fp32.
  *
- *   xq, xe   activation codes [M][K/2], scale bytes [M][K/32]
- *   wq, we   weight codes [N][K/2], scale bytes [N][K/32]
+ *   xq, xe   activation codes [M][K/2], M * K/32 scale bytes (panel layout
+ *            of mxfp4_quantize)
+ *   wq, we   weight codes [N][K/2], N * K/32 scale bytes (panel layout)
  *   K > 0, K % 128 == 0; y as for w4a4_gemm. xq, wq 16-byte aligned.
  */
 w4a4_status_t mxfp4_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,

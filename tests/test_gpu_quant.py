@@ -105,7 +105,7 @@ def mx_check(x16, ldx_pad=0):
         xt = dev(x16)
     q, e = ops().mxfp4_quantize(xt)
     codes, e8 = oracle.mxfp4_quantize(x16)
-    assert np.array_equal(host(e), e8), f"E8M0 differ (R={R} K={K})"
+    assert np.array_equal(ops().mxfp4_scales_to_rows(host(e), R, K), e8), f"E8M0 differ (R={R} K={K})"
     gq = host(q)
     want = oracle.pack_nibbles(codes)   # E2M1 fields, even k low
     bad = np.argwhere(gq != want)

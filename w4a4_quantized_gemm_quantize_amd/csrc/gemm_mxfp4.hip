@@ -125,13 +125,16 @@ void k_mxfp4_gemm(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int row_bytes = p.K >> 1;
-  const int row_scales = p.K >> 5;
   const int nk = p.K / KB;
 
   // ---- per-lane sources of this wave's loads (stage 0); LDS offsets are per wave
   const uint8_t* srcA[NA];
   const uint8_t* srcW[NW];
-  const uint8_t* srcE[NE];
+  const uint8_t* baseE[NE];   // the lane's scale matrix (unused slots: p.ea, offsets 0)
+  int64_t panE[NE];           // bytes per full panel of that matrix (8 per row)
+  int rowE[NE];               // byte offset of the lane's dword in an 8-byte-pitch panel
+  int rowE4[NE];              // the same in a 4-byte-pitch (last, 4-block) panel
+  int hE[NE];                 // 4 for used slots: offset of the second 128-k half
   const int lrow = lane / SL, lslot = lane % SL;
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
@@ -145,16 +148,37 @@ void k_mxfp4_gemm(Params p) {
     const int seg = lslot ^ ((row >> SWS) & (SL - 1));
     srcW[i] = p.w + (int64_t)min(tile_n + row, p.N - 1) * row_bytes + 16 * seg;
   }
-  // scale dword e = w * (BM + BN) + r: dword w of this stage's scales of A row r
-  // (r < BM) or W row r - BM
+  // Scales are stored in panels of 8 blocks (256 k): panel q holds, row after
+  // row, each row's 8 scale bytes of blocks 8q..8q+7 (a last panel of 4 blocks
+  // holds 4 bytes per row). Scale dword e = NEW * r + w of a stage is dword w of
+  // the stage's scales of A row r (r < BM) or W row r - BM, so consecutive lanes
+  // read consecutive dwords of one panel.
 #pragma unroll
   for (int j = 0; j < NE; ++j) {
     const int e = 64 * (NE * wave + j) + lane;
-    const int w = e / (BM + BN), r = e % (BM + BN);
-    srcE[j] = e >= NEW * (BM + BN) ? p.ea   // unused slot: a harmless in-bounds read
-            : r < BM ? p.ea + (int64_t)min(tile_m + r, p.M - 1) * row_scales + 4 * w
-                     : p.ew + (int64_t)min(tile_n + r - BM, p.N - 1) * row_scales + 4 * w;
+    const int r = e / NEW, w = e % NEW;
+    const bool used = e < NEW * (BM + BN);
+    const bool is_a = r < BM;
+    const int64_t row = is_a ? min(tile_m + r, p.M - 1) : min(tile_n + r - BM, p.N - 1);
+    baseE[j] = (used && !is_a) ? p.ew : p.ea;
+    panE[j] = used ? 8 * (int64_t)(is_a ? p.M : p.N) : 0;
+    rowE[j] = used ? (int)(8 * row + 4 * w) : 0;
+    rowE4[j] = used ? (int)(4 * row) : 0;
+    hE[j] = used ? 4 : 0;
   }
+  // a K that is 128 mod 256 ends in a 4-block panel (4 scale bytes per row)
+  const bool half_tail = (p.K & 255) != 0;
+  // Address of scale dword slot j for stage kt: panel kt (KB = 256) or half
+  // kt % 2 of panel kt / 2 (KB = 128), whose row pitch is 4 in a last 4-block panel.
+  auto scale_src = [&](int j, int kt) -> const uint8_t* {
+    if constexpr (KB == 256) {
+      return baseE[j] + kt * panE[j] + rowE[j];
+    } else {
+      const uint8_t* panel = baseE[j] + (kt >> 1) * panE[j];
+      if (half_tail && kt == nk - 1) return panel + rowE4[j];
+      return panel + rowE[j] + (kt & 1) * hE[j];
+    }
+  };
 #define ISSUE(KT, SM)                                                                \
   {                                                                                  \
     uint8_t* base_ = (SM);                                                           \
@@ -163,7 +187,7 @@ void k_mxfp4_gemm(Params p) {
     _Pragma("unroll") for (int i = 0; i < NW; ++i)                                   \
         dma16(srcW[i] + (KT) * RB, base_ + W_OFF + (wave + NWAVE * i) * 1024);     \
     _Pragma("unroll") for (int j = 0; j < NE; ++j)                                   \
-        dma4(srcE[j] + (KT) * 4 * NEW, base_ + E_OFF + (NE * wave + j) * 256);     \
+        dma4(scale_src(j, (KT)), base_ + E_OFF + (NE * wave + j) * 256);           \
   }
 
   v16f acc[TI][TJ];
@@ -194,14 +218,14 @@ void k_mxfp4_gemm(Params p) {
 #define LOAD_OPS(SM, U)                                                               \
   {                                                                                  \
     const uint8_t* st_ = (SM);                                                       \
-    const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF) + ((U) / 2) * (BM + BN); \
+    const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF) + (U) / 2;  \
     _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                 \
       av[i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 32 * RB * i);         \
-      ea[i] = (int)((se_[rowA + 32 * i] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu);    \
+      ea[i] = (int)((se_[NEW * (rowA + 32 * i)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
     _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                 \
       wv[j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 32 * RB * j); \
-      ew[j] = (int)((se_[BM + rowW + 32 * j] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
+      ew[j] = (int)((se_[NEW * (BM + rowW + 32 * j)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
   }
 // Matrix work of step U of stage KT. The partials variant runs one 32-block at

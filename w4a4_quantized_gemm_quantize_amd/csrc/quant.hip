@@ -11,7 +11,10 @@
 //   rotate.
 // MXFP4 (the open-standard MXFP4 of the FP4 RL abstract; OCP MX v1.0 block
 // rule): per 32 elements E = floor(log2 a) - 2, codes = E2M1(x / 2^E) with
-// ties to even and saturation at 6, E8M0 byte E + 127.
+// ties to even and saturation at 6, E8M0 byte E + 127. The scale bytes are
+// written in 256-k panels (panel q = blocks 8q..8q+7 of every row, row after
+// row, min(8, blocks left) bytes per row), so the GEMM reads one stage's scales
+// of a tile as one contiguous run.
 //
 // Both kernels stream HBM: each lane loads 8 fp16 (one 128-bit load) per row
 // it covers, a group's absmax is reduced across the lanes that hold it with DPP
@@ -204,7 +207,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = ldexpf(f[i], -E);   // exact power-of-two scaling
       q[(int64_t)row * cpr + mp.col] = e2m1_codes8(v);
-      if ((threadIdx.x & 3) == 0) e8m0[(int64_t)row * (cpr / 4) + mp.col / 4] = (uint8_t)(E + 127);
+      if ((threadIdx.x & 3) == 0) {
+        // panel layout: block b of the row goes to panel b / 8, whose rows hold
+        // min(8, blocks left) bytes each
+        const int b = mp.col >> 2, nb = cpr >> 2;
+        const int pq = b >> 3, pw = min(8, nb - 8 * pq);
+        e8m0[(int64_t)8 * rows * pq + (int64_t)row * pw + (b & 7)] = (uint8_t)(E + 127);
+      }
     }
   }
 }

@@ -90,17 +90,56 @@ def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int
     return part
 
 
+def mxfp4_scale_offsets(rows: int, K: int):
+    """Byte offset of the scale of (row r, block b) in the 256-k panel layout
+    of the C header: ``8*rows*p + w_p*r + b%8`` with ``p = b // 8`` and
+    ``w_p = min(8, K/32 - 8p)``. Returns an int64 tensor [rows, K/32]."""
+    nb = K // 32
+    b = torch.arange(nb, dtype=torch.int64)
+    p = b // 8
+    w = torch.clamp(nb - 8 * p, max=8)
+    r = torch.arange(rows, dtype=torch.int64)[:, None]
+    return 8 * rows * p[None, :] + w[None, :] * r + (b % 8)[None, :]
+
+
+def mxfp4_scales_to_rows(e, rows: int, K: int):
+    """Panel-layout scale bytes (flat, ``rows*K/32``) -> row-major [rows, K/32]
+    (torch tensor on its device, or numpy array)."""
+    idx = mxfp4_scale_offsets(rows, K)
+    if isinstance(e, torch.Tensor):
+        return e.reshape(-1)[idx.to(e.device)]
+    return e.reshape(-1)[idx.numpy()]
+
+
+def mxfp4_scales_to_panels(e_rows):
+    """Row-major [rows, K/32] scale bytes -> the flat panel layout."""
+    rows, nb = e_rows.shape
+    idx = mxfp4_scale_offsets(rows, 32 * nb).reshape(-1)
+    if isinstance(e_rows, torch.Tensor):
+        out = torch.empty(rows * nb, dtype=e_rows.dtype, device=e_rows.device)
+        out[idx.to(e_rows.device)] = e_rows.reshape(-1)
+        return out
+    import numpy as np
+    out = np.empty(rows * nb, dtype=e_rows.dtype)
+    out[idx.numpy()] = e_rows.reshape(-1)
+    return out
+
+
 def mxfp4_quantize(x: torch.Tensor, out=None):
-    """MXFP4 quantization of fp16 X[rows, K]: ``(codes uint8 [rows, K/2], e8m0 uint8 [rows, K/32])``."""
+    """MXFP4 quantization of fp16 X[rows, K]: ``(codes uint8 [rows, K/2],
+    e8m0 uint8 [rows*K/32] in the 256-k panel layout)``; see
+    :func:`mxfp4_scales_to_rows` for the row-major view."""
     _need(x, torch.float16, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     R, K = x.shape
     if out is None:
         q = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
-        e = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+        e = torch.empty((R * (K // 32),), dtype=torch.uint8, device=x.device)
     else:
         q, e = out
+    if e.numel() != R * (K // 32) or not e.is_contiguous():
+        raise ValueError("e8m0 must be contiguous with rows*K/32 bytes")
     call("mxfp4_quantize", x.data_ptr(), R, K, x.stride(0), q.data_ptr(), e.data_ptr(), _stream(x))
     return q, e
 
@@ -113,6 +152,8 @@ def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
     N = wq.shape[0]
     if wq.shape[1] * 2 != K:
         raise ValueError("K of xq and wq differ")
+    if xe.numel() != M * (K // 32) or we.numel() != N * (K // 32):
+        raise ValueError("scale tensors must hold rows*K/32 bytes (panel layout)")
     y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
     call("mxfp4_gemm", xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(), M, N, K,
          y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))

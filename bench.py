@@ -163,7 +163,7 @@ def main() -> int:
         if fmt == "int4":
             wq, ws = ops.w4a4_pack_weight(w, gw)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-            xs = torch.empty((M, K // ga), dtype=torch.float32, device=dev)
+            xs = torch.empty((K // ga, M), dtype=torch.float32, device=dev)
         else:
             wq, ws = ops.mxfp4_quantize(w)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)

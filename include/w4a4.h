@@ -78,7 +78,9 @@ const char* w4a4_status_str(int status);
  *   M, K  K > 0, K % 8 == 0 (K % group == 0 required as well)
  *   group 64, 128, 256, 512, or group == K ("per token")
  *   xq    out: u8 [M][K/2] packed codes (layout above), 4-byte aligned
- *   xs    out: f32 [M][K/group] scales, 4-byte aligned
+ *   xs    out: f32 [K/group][M] scales, group-major (the scale of row m and
+ *         group c is xs[c * M + m]), 4-byte aligned. One K stage of a GEMM tile
+ *         then reads its rows' scales as one contiguous run.
  */
 w4a4_status_t w4a4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group,
                                 uint8_t* xq, float* xs, void* stream);
@@ -88,7 +90,7 @@ w4a4_status_t w4a4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx
  * rule as w4a4_quantize_act applied to the rows of W[N][K] (ldw = K).
  *
  *   w     fp16 [N][K], 16-byte aligned
- *   wq    out: u8 [N][K/2];  ws  out: f32 [N][K/group]
+ *   wq    out: u8 [N][K/2];  ws  out: f32 [K/group][N] (group-major, as xs)
  */
 w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t group,
                                uint8_t* wq, float* ws, void* stream);
@@ -100,8 +102,9 @@ w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t grou
  *   P_b[m,n] = sum_{k in block b of g} qa[m,k] * qw[n,k]     (exact, |P_b| <= 49 g)
  *   Y[m,n]   = sum_b s_a[m, b*g/group_a] * s_w[n, b*g/group_w] * P_b[m,n]  (fp32)
  *
- *   xq, xs          packed activation codes [M][K/2] and scales [M][K/group_a]
- *   wq, ws          packed weight codes [N][K/2] and scales [N][K/group_w]
+ *   xq, xs          packed activation codes [M][K/2] and scales [K/group_a][M]
+ *   wq, ws          packed weight codes [N][K/2] and scales [K/group_w][N]
+ *                   (scales group-major, as written by the quantizers)
  *   group_a/group_w each a power of two >= 64 dividing K (64, 128, 256, 512, ...)
  *                   or K itself (per token); the larger must be a multiple of
  *                   the smaller, and g <= 262144 (P_b stays an exact integer in

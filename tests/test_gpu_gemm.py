@@ -79,9 +79,9 @@ def test_empty_is_noop():
     import torch
     o = ops()
     xq = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
-    xs = torch.zeros((0, 2), dtype=torch.float32, device="cuda")
+    xs = torch.zeros((2, 0), dtype=torch.float32, device="cuda")
     wq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
-    ws = torch.zeros((8, 2), dtype=torch.float32, device="cuda")
+    ws = torch.zeros((2, 8), dtype=torch.float32, device="cuda")
     y = o.w4a4_gemm(xq, xs, 128, wq, ws, 128)
     assert y.shape == (0, 8)
 

@@ -29,7 +29,7 @@ def int4_check(x16, group, ldx_pad=0):
     want = oracle.pack_int4(codes, oracle.int4_sign_bits(x16))
     bad = np.argwhere(host(q) != want)
     assert bad.size == 0, f"codes differ at {bad[:5].tolist()} (M={M} K={K} g={group})"
-    gs = host(s)
+    gs = np.ascontiguousarray(host(s).T)   # group-major on the device
     assert np.array_equal(gs.view(np.uint32), scales.view(np.uint32)), f"scales differ (M={M} K={K} g={group})"
 
 
@@ -91,7 +91,7 @@ def test_int4_workload_activations_sampled(name):
     rows = synth.sample_rows(M, 64, seed=1)
     codes, scales = oracle.int4_quantize(x[rows], 128)
     assert np.array_equal(host(q)[rows], oracle.pack_int4(codes, oracle.int4_sign_bits(x[rows])))
-    assert np.array_equal(host(s)[rows].view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(np.ascontiguousarray(host(s)[:, rows].T).view(np.uint32), scales.view(np.uint32))
 
 
 # ------------------------------------------------------------------ MXFP4

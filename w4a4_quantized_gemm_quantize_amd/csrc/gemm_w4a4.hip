@@ -69,7 +69,7 @@ struct Params {
   int sha, shw;               // scale column of 64-k half h = h >> sh (31: one column)
   int stages_per_group;       // GBIG only
   int M, N, K;
-  int ksa, ksw;               // scale columns per row (K / group)
+  int ksa, ksw;               // scale groups per row (K / group); scales are group-major [K/group][rows]
   void* y;
   int ydtype;
   int64_t ldy;
@@ -153,8 +153,9 @@ void k_w4a4_gemm(Params p) {
   // scales: threads 0..127 stage A-row scales, 128..255 W-row scales
   const bool s_is_a = tid < BM;
   const int srow = s_is_a ? tid : tid - BM;
-  const float* gS = s_is_a ? p.sa + (int64_t)min(tile_m + srow, p.M - 1) * p.ksa
-                           : p.sw + (int64_t)min(tile_n + srow, p.N - 1) * p.ksw;
+  // group-major scales: consecutive threads read consecutive rows of one group
+  const float* gS = s_is_a ? p.sa + min(tile_m + srow, p.M - 1) : p.sw + min(tile_n + srow, p.N - 1);
+  const int64_t sgs = s_is_a ? p.M : p.N;   // floats between groups
   const int ssh = s_is_a ? p.sha : p.shw;
   float* sS = s_is_a ? &sSA[0][0][srow] : &sSW[0][0][srow];
 
@@ -174,8 +175,9 @@ void k_w4a4_gemm(Params p) {
     R.a1 = *reinterpret_cast<const uint4*>(gA1 + off_);               \
     R.w0 = *reinterpret_cast<const uint4*>(gW0 + off_);               \
     R.w1 = *reinterpret_cast<const uint4*>(gW1 + off_);               \
-    R.s0 = gS[(2 * (KT)) >> ssh];                                     \
-    R.s1 = gS[(2 * (KT) + 1) >> ssh];                                 \
+    R.s0 = gS[(int64_t)((2 * (KT)) >> ssh) * sgs];                    \
+    /* groups >= 128: both 64-k halves share a group */               \
+    R.s1 = (MODE == G64) ? gS[(int64_t)((2 * (KT) + 1) >> ssh) * sgs] : R.s0; \
   }
 #define LSTORE(BUF, R)                                                \
   {                                                                   \
@@ -345,7 +347,7 @@ void k_w4a4_gemm(Params p) {
           const int m = tile_m + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
           const int n = tile_n + wn * 64 + j * 32 + l32;
           if (m < p.M && n < p.N) {
-            const float v = ROWA ? acc[i][j][r] * p.sa[(int64_t)m * p.ksa] : acc[i][j][r];
+            const float v = ROWA ? acc[i][j][r] * p.sa[m] : acc[i][j][r];   // one group: xs[m]
             if (p.ydtype == 0)
               static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = v;
             else

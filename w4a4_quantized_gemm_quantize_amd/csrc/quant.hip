@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
       float sc, rc;
       group_scale(a, sc, rc);
       q[(int64_t)row * cpr + mp.col] = int4_codes8(f, raw[u], sc, rc);
-      if ((threadIdx.x & (LPG - 1)) == 0) s[(int64_t)row * (cpr / LPG) + mp.col / LPG] = sc;
+      if ((threadIdx.x & (LPG - 1)) == 0) s[(int64_t)(mp.col / LPG) * M + row] = sc;   // group-major
     }
   }
 }

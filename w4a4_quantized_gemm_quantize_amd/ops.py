@@ -30,10 +30,17 @@ def _ydtype(dtype) -> int:
     raise TypeError("output dtype must be torch.float32 or torch.float16")
 
 
+def _need_scales(s: torch.Tensor, K: int, group: int, rows: int, name: str) -> None:
+    """Group-major INT4 scales: contiguous, K/group x rows floats."""
+    if group > 0 and K % group == 0 and (not s.is_contiguous() or s.numel() != (K // group) * rows):
+        raise ValueError(f"{name} must be contiguous group-major scales [K/group, rows]")
+
+
 def w4a4_quantize_act(x: torch.Tensor, group: int = 128, out=None):
     """INT4 group quantization of fp16 X[M, K] (row stride may exceed K).
 
-    Returns ``(xq uint8 [M, K/2], xs float32 [M, K/group])``.
+    Returns ``(xq uint8 [M, K/2], xs float32 [K/group, M])``: the scales are
+    group-major (``xs[c, m]`` is the scale of row m, group c).
     """
     _need(x, torch.float16, "x")
     if x.dim() != 2 or x.stride(1) != 1:
@@ -41,7 +48,7 @@ def w4a4_quantize_act(x: torch.Tensor, group: int = 128, out=None):
     M, K = x.shape
     if out is None:
         xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-        xs = torch.empty((M, max(K // max(group, 1), 0)), dtype=torch.float32, device=x.device)
+        xs = torch.empty((max(K // max(group, 1), 0), M), dtype=torch.float32, device=x.device)
     else:
         xq, xs = out
     call("w4a4_quantize_act", x.data_ptr(), M, K, x.stride(0), group,
@@ -50,14 +57,15 @@ def w4a4_quantize_act(x: torch.Tensor, group: int = 128, out=None):
 
 
 def w4a4_pack_weight(w: torch.Tensor, group: int = 128, out=None):
-    """Offline INT4 group quantization of fp16 W[N, K] (contiguous)."""
+    """Offline INT4 group quantization of fp16 W[N, K] (contiguous):
+    ``(wq uint8 [N, K/2], ws float32 [K/group, N])``, scales group-major."""
     _need(w, torch.float16, "w")
     if w.dim() != 2 or not w.is_contiguous():
         raise ValueError("w must be a contiguous 2-D tensor")
     N, K = w.shape
     if out is None:
         wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-        ws = torch.empty((N, max(K // max(group, 1), 0)), dtype=torch.float32, device=w.device)
+        ws = torch.empty((max(K // max(group, 1), 0), N), dtype=torch.float32, device=w.device)
     else:
         wq, ws = out
     call("w4a4_pack_weight", w.data_ptr(), N, K, group, wq.data_ptr(), ws.data_ptr(), _stream(w))
@@ -73,6 +81,8 @@ def w4a4_gemm(xq, xs, group_a: int, wq, ws, group_w: int, out_dtype=torch.float3
     N = wq.shape[0]
     if wq.shape[1] * 2 != K:
         raise ValueError("K of xq and wq differ")
+    _need_scales(xs, K, group_a, M, "xs")
+    _need_scales(ws, K, group_w, N, "ws")
     y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
     call("w4a4_gemm", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(), group_w,
          M, N, K, y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))

@@ -8,16 +8,20 @@
 // of exactly that block, so the block scales are applied inside the
 // instruction and accumulation is fp32 with no vector-unit epilogue. The kernel
 // is tiled for the matrix cores: each wave owns a (BM/WM) x (BN/WN) output
-// tile. The launch uses 256 x 128 workgroup tiles of 4 x 2 waves with 256-deep
-// K stages (one workgroup per CU, 2 waves per SIMD) when K % 256 == 0, else
-// 128 x 128 tiles of 2 x 2 waves with 128-deep stages. Measured on gfx950 the
-// kernel is bound by L2 request traffic (L2 busy ~96 %); the larger tile and
-// the line-sized row pieces of the deeper stage cut requests per flop.
+// tile. When K % 256 == 0 the launch uses 256 x 256 workgroup tiles of 2 x 4
+// waves (128 x 64 each: 8 MFMAs per 6 operand reads per 64-k step), 256-deep K
+// stages and one workgroup per CU (2 waves per SIMD); otherwise 128 x 128
+// tiles of 2 x 2 waves with 128-deep stages. On gfx950 the cost per flop that
+// mattered most, in the order found: accumulator copies at stage boundaries
+// (gone with the loop unrolled by the ring depth), L2 requests for row-major
+// scales (gone with the panel layout), L2 and LDS bytes per flop (cut by the
+// larger tile) and LDS bank conflicts (gone with the 64-bank swizzle below).
 //
-// Stages are fed through a 3-stage LDS ring by direct global->LDS loads (no
-// staging registers), so two stages of loads are in flight behind the matrix
-// work. The debug-partials variant runs
-// the same instruction one 32-block at a time with unit scales.
+// Stages are fed through an LDS ring by direct global->LDS loads (no staging
+// registers): 2 x 68 KB stages for the 256 x 256 tile (one stage in flight
+// behind the matrix work), 3 x 34 KB for the 128 x 128 tile (two in flight).
+// The debug-partials variant runs the same instruction one 32-block at a time
+// with unit scales.
 //
 // 32x32 MFMA output layout: D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
 // col l%32.
@@ -78,19 +82,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 // computed. A stage holds BM + BN rows of RB = KB/2 packed bytes (row-major, no
 // pad: each wave-wide 1 KB load covers 1024/RB rows) and KB/128 E8M0 dwords per
 // row. A 256-deep stage makes each row's piece a whole 128-byte line, so the L2
-// serves line-sized requests instead of 64-byte halves. The SL = RB/16 slots of
-// a row are XOR-swizzled with (row >> log2(32/SL)) & (SL-1) so the 32 lanes of a
-// half-wave that read one slot of 32 consecutive rows hit 32 distinct bank
+// serves line-sized requests instead of 64-byte halves. The LDS serves a
+// 16-byte read for 16 lanes per clock (64 banks of 4 bytes): the SL = RB/16
+// slots of a row are XOR-swizzled with (row >> log2(16/SL)) & (SL-1) so the 16
+// lanes that read one slot of 16 consecutive rows hit 16 distinct 16-byte bank
 // groups.
-template <int BM, int BN, int WM, int WN, int KB, bool PARTIALS>
+template <int BM, int BN, int WM, int WN, int KB, int S, bool PARTIALS>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_mxfp4_gemm(Params p) {
-  constexpr int S = 3;                              // ring depth
+  static_assert(S == 2 || S == 3, "ring depth");    // stages in LDS; S - 1 in flight
+  constexpr int D = S - 1;                          // prefetch distance in stages
   constexpr int NWAVE = WM * WN;
   constexpr int RB = KB / 2;                        // packed bytes per row per stage
   constexpr int SL = RB / 16;                       // 16-byte slots per row
   constexpr int RPK = 1024 / RB;                    // rows per 1 KB load
-  constexpr int SWS = SL == 4 ? 3 : 2;              // log2(32 / SL)
+  constexpr int SWS = SL == 4 ? 2 : 1;              // log2(16 / SL)
   constexpr int NSTEP = KB / 64;                    // MFMA k-steps per stage
   constexpr int NEW = KB / 128;                     // E8M0 dwords per row per stage
   constexpr int TI = BM / WM / 32, TJ = BN / WN / 32;   // 32x32 blocks per wave
@@ -107,7 +113,7 @@ void k_mxfp4_gemm(Params p) {
   // LDS reads of another and does not wait for it.
   __shared__ __align__(16) uint8_t sm0[STAGE];
   __shared__ __align__(16) uint8_t sm1[STAGE];
-  __shared__ __align__(16) uint8_t sm2[STAGE];
+  __shared__ __align__(16) uint8_t sm2[S == 3 ? STAGE : 16];
 
   const int nblk = p.tiles_m * p.tiles_n;
   int bid = blockIdx.x;
@@ -270,16 +276,18 @@ void k_mxfp4_gemm(Params p) {
     __builtin_amdgcn_s_barrier();                                       \
     __builtin_amdgcn_sched_barrier(0);                                  \
   }
-// Iteration for stage KT held in slot CUR; stage KT+2 is issued into slot NXT
+// Iteration for stage KT held in slot CUR; stage KT+D is issued into slot NXT
 // (the slot stage KT-1 used, free once every wave has passed the barrier) after
 // the first step's operand reads, so those reads never wait behind the new loads.
+// At the top, stages KT .. KT+D-1 are in flight; the wait leaves the later
+// D-1 of them outstanding.
 #define ITER(KT, CUR, NXT)                                              \
   {                                                                     \
-    if ((KT) + 1 < nk) wait_vmcnt<PER_STAGE>();                         \
+    if (D == 2 && (KT) + 1 < nk) wait_vmcnt<(D - 1) * PER_STAGE>();     \
     else wait_vmcnt<0>();                                               \
     STAGE_BARRIER();                                                    \
     LOAD_OPS(CUR, 0);                                                   \
-    if ((KT) + 2 < nk) ISSUE((KT) + 2, NXT);                            \
+    if ((KT) + D < nk) ISSUE((KT) + D, NXT);                            \
     MMA_STEP(KT, 0);                                                    \
     _Pragma("unroll") for (int u_ = 1; u_ < NSTEP; ++u_) {              \
       LOAD_OPS(CUR, u_);                                                \
@@ -288,18 +296,26 @@ void k_mxfp4_gemm(Params p) {
   }
 
   ISSUE(0, sm0);
-  if (nk > 1) ISSUE(1, sm1);
+  if (S == 3 && nk > 1) ISSUE(1, sm1);
   // Unrolled by the ring depth, so every stage names its slot statically and
   // the loop has one back edge: the accumulators stay in the registers the
   // matrix instructions write, with no copies between stages.
-  static_assert(S == 3, "the unrolled loop below names three slots");
-  for (int kt = 0;; kt += S) {
-    ITER(kt, sm0, sm2)
-    if (kt + 1 >= nk) break;
-    ITER(kt + 1, sm1, sm0)
-    if (kt + 2 >= nk) break;
-    ITER(kt + 2, sm2, sm1)
-    if (kt + 3 >= nk) break;
+  if constexpr (S == 3) {
+    for (int kt = 0;; kt += 3) {
+      ITER(kt, sm0, sm2)
+      if (kt + 1 >= nk) break;
+      ITER(kt + 1, sm1, sm0)
+      if (kt + 2 >= nk) break;
+      ITER(kt + 2, sm2, sm1)
+      if (kt + 3 >= nk) break;
+    }
+  } else {
+    for (int kt = 0;; kt += 2) {
+      ITER(kt, sm0, sm1)
+      if (kt + 1 >= nk) break;
+      ITER(kt + 1, sm1, sm0)
+      if (kt + 2 >= nk) break;
+    }
   }
 #undef ITER
 #undef STAGE_BARRIER
@@ -326,24 +342,25 @@ void k_mxfp4_gemm(Params p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int KB, bool PARTIALS>
+template <int BM, int BN, int WM, int WN, int KB, int S, bool PARTIALS>
 void launch_cfg(Params p, const GemmArgs& g, hipStream_t stream) {
   p.tile_m0 = (int)(g.m0 / BM);
   p.tile_n0 = (int)(g.n0 / BN);
   p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
   p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
-  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, KB, PARTIALS>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, KB, S, PARTIALS>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
                      dim3(64 * WM * WN), 0, stream, p);
 }
 
-// 256 x 128 tiles (8 waves) with 256-deep stages when K allows, else 128 x 128
-// with 128-deep stages.
+// 256 x 256 tiles (2 x 4 waves of 128 x 64) with 256-deep stages in a 2-stage
+// ring (2 x 68 KB) when K allows, else 128 x 128 tiles (2 x 2 waves) with
+// 128-deep stages in a 3-stage ring.
 template <bool PARTIALS>
 void launch_for(Params p, const GemmArgs& g, hipStream_t stream) {
   if (g.K % 256 == 0)
-    launch_cfg<256, 128, 4, 2, 256, PARTIALS>(p, g, stream);
+    launch_cfg<256, 256, 2, 4, 256, 2, PARTIALS>(p, g, stream);
   else
-    launch_cfg<128, 128, 2, 2, 128, PARTIALS>(p, g, stream);
+    launch_cfg<128, 128, 2, 2, 128, 3, PARTIALS>(p, g, stream);
 }
 
 }  // namespace

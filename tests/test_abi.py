@@ -121,6 +121,8 @@ def test_mxfp4_validation(lib):
     assert mg(P, P + 2, P, P, 4, 4, 128, P, 0, 4, None) == E_ALIGN
     assert mg(P, P, P, None, 4, 4, 128, P, 0, 4, None) == E_NULL
     assert mg(P, P, P, P, 0, 4, 128, None, 0, 4, None) == OK
+    assert mg(P, P, P, P, 4, 4, (1 << 23) + 128, P, 0, 4, None) == E_SHAPE   # 32-bit tile offsets
+    assert mg(P, P, P, P, 0, 4, 1 << 23, None, 0, 4, None) == OK
     mp = lambda *a: _lib.status_of("mxfp4_gemm_debug_partials", *a)
     assert mp(P, P, P, P, 4, 4, 128, 0, 5, 0, 4, P, None) == E_SHAPE
 

@@ -146,7 +146,9 @@ w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx
 
 static w4a4_status_t mx_common(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
                                int64_t M, int64_t N, int64_t K, GemmArgs& g) {
-  if (M < 0 || N < 0 || K <= 0 || K % 128) return W4A4_E_SHAPE;
+  // K <= 2^23: a 256-row tile then spans < 2^31 bytes, the kernel's 32-bit
+  // buffer offsets
+  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > (int64_t{1} << 23)) return W4A4_E_SHAPE;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!xq || !xe || !wq || !we) return W4A4_E_NULL;
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xe, 4) || !aligned(we, 4)) return W4A4_E_ALIGN;

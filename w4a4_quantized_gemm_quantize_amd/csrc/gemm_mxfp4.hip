@@ -59,14 +59,21 @@ __device__ __forceinline__ v8i as_operand(uint4 v) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
-typedef __attribute__((address_space(1))) void* glb_vptr;
 
-// Direct global -> LDS copies: lane l's 16 (4) bytes land at lds + 16 l (4 l).
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds((glb_vptr)(const_cast<void*>(g)), (lds_vptr)lds, 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): loads beyond the range read 0.
+// Word 3 is the CDNA raw-buffer format word (32-bit data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds((glb_vptr)(const_cast<void*>(g)), (lds_vptr)lds, 4, 0, 0);
+// Direct buffer -> LDS copies: lane l's 16 (4) bytes from base + voff + soff
+// land at lds + 16 l (4 l). The buffer (MUBUF) form, unlike the global (FLAT)
+// form, lets the compiler keep exact LDS-read wait counts while these loads
+// are in flight, so operand reads of the next k-step overlap the MFMAs.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt on vmcnt only (expcnt/lgkmcnt left at their maxima), gfx9 encoding.
@@ -133,67 +140,77 @@ void k_mxfp4_gemm(Params p) {
   const int row_bytes = p.K >> 1;
   const int nk = p.K / KB;
 
-  // ---- per-lane sources of this wave's loads (stage 0); LDS offsets are per wave
-  const uint8_t* srcA[NA];
-  const uint8_t* srcW[NW];
-  const uint8_t* baseE[NE];   // the lane's scale matrix (unused slots: p.ea, offsets 0)
-  int64_t panE[NE];           // bytes per full panel of that matrix (8 per row)
-  int rowE[NE];               // byte offset of the lane's dword in an 8-byte-pitch panel
-  int rowE4[NE];              // the same in a 4-byte-pitch (last, 4-block) panel
-  int hE[NE];                 // 4 for used slots: offset of the second 128-k half
+  // ---- buffer resources over this tile's rows (row offsets stay 32-bit; the
+  // host limits K so a tile's rows span < 2^31 bytes), per-lane row offsets
+  const int a_rows = min(BM, p.M - tile_m), w_rows = min(BN, p.N - tile_n);
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
+  int voffA[NA], voffW[NW];
   const int lrow = lane / SL, lslot = lane % SL;
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int row = RPK * (wave + NWAVE * i) + lrow;
     const int seg = lslot ^ ((row >> SWS) & (SL - 1));
-    srcA[i] = p.a + (int64_t)min(tile_m + row, p.M - 1) * row_bytes + 16 * seg;
+    voffA[i] = min(row, a_rows - 1) * row_bytes + 16 * seg;
   }
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int row = RPK * (wave + NWAVE * i) + lrow;
     const int seg = lslot ^ ((row >> SWS) & (SL - 1));
-    srcW[i] = p.w + (int64_t)min(tile_n + row, p.N - 1) * row_bytes + 16 * seg;
+    voffW[i] = min(row, w_rows - 1) * row_bytes + 16 * seg;
   }
   // Scales are stored in panels of 8 blocks (256 k): panel q holds, row after
   // row, each row's 8 scale bytes of blocks 8q..8q+7 (a last panel of 4 blocks
   // holds 4 bytes per row). Scale dword e = NEW * r + w of a stage is dword w of
-  // the stage's scales of A row r (r < BM) or W row r - BM, so consecutive lanes
-  // read consecutive dwords of one panel.
+  // the stage's scales of A row r (e < NEW * BM) or of W row r - BM; each wave
+  // load moves one 64-dword chunk of them, chunk c = NE * wave + j, so
+  // consecutive lanes read consecutive dwords of one panel. A buffer resource
+  // is uniform, so a chunk lies wholly in the A part or the W part.
+  constexpr int CA = NEW * BM / 64, CW = NEW * BN / 64;   // chunks per stage
+  static_assert(CA * 64 == NEW * BM && CW * 64 == NEW * BN, "scale chunks");
+  int voffE[NE], voffE4[NE];    // the lane's offset in an 8-byte / 4-byte pitch panel
 #pragma unroll
   for (int j = 0; j < NE; ++j) {
-    const int e = 64 * (NE * wave + j) + lane;
-    const int r = e / NEW, w = e % NEW;
-    const bool used = e < NEW * (BM + BN);
-    const bool is_a = r < BM;
-    const int64_t row = is_a ? min(tile_m + r, p.M - 1) : min(tile_n + r - BM, p.N - 1);
-    baseE[j] = (used && !is_a) ? p.ew : p.ea;
-    panE[j] = used ? 8 * (int64_t)(is_a ? p.M : p.N) : 0;
-    rowE[j] = used ? (int)(8 * row + 4 * w) : 0;
-    rowE4[j] = used ? (int)(4 * row) : 0;
-    hE[j] = used ? 4 : 0;
+    const int c = NE * wave + j;
+    const bool is_a = c < CA;
+    const int e = 64 * (is_a ? c : c - CA) + lane;
+    const int r = min(e / NEW, (is_a ? a_rows : w_rows) - 1), w = e % NEW;
+    voffE[j] = 8 * r + 4 * w;
+    voffE4[j] = 4 * r;
   }
   // a K that is 128 mod 256 ends in a 4-block panel (4 scale bytes per row)
   const bool half_tail = (p.K & 255) != 0;
-  // Address of scale dword slot j for stage kt: panel kt (KB = 256) or half
-  // kt % 2 of panel kt / 2 (KB = 128), whose row pitch is 4 in a last 4-block panel.
-  auto scale_src = [&](int j, int kt) -> const uint8_t* {
+  // Scale chunk j of stage kt: panel kt (KB = 256) or half kt % 2 of panel
+  // kt / 2 (KB = 128), whose row pitch is 4 in a last 4-block panel. Chunks
+  // beyond the stage's (none in the shipped tile shapes) re-read chunk 0's
+  // dwords into their own unused LDS words, so every wave issues the same
+  // number of loads per stage (the vmcnt waits count on it).
+  auto issue_scales = [&](int j, int kt, uint8_t* lds) {
+    const int c = NE * wave + j;
+    const bool is_a = c < CA || c >= CA + CW;
+    const uint8_t* mat = is_a ? p.ea : p.ew;
+    const int64_t rows_all = is_a ? p.M : p.N;
+    const int t0 = is_a ? tile_m : tile_n;
+    const int nrow = is_a ? a_rows : w_rows;
     if constexpr (KB == 256) {
-      return baseE[j] + kt * panE[j] + rowE[j];
+      dma4(buffer_rsrc(mat + 8 * rows_all * kt + 8 * t0, 8 * nrow), voffE[j], 0, lds);
     } else {
-      const uint8_t* panel = baseE[j] + (kt >> 1) * panE[j];
-      if (half_tail && kt == nk - 1) return panel + rowE4[j];
-      return panel + rowE[j] + (kt & 1) * hE[j];
+      const uint8_t* panel = mat + 8 * rows_all * (kt >> 1);
+      if (half_tail && kt == nk - 1)
+        dma4(buffer_rsrc(panel + 4 * t0, 4 * nrow), voffE4[j], 0, lds);
+      else
+        dma4(buffer_rsrc(panel + 8 * t0, 8 * nrow), voffE[j], 4 * (kt & 1), lds);
     }
   };
 #define ISSUE(KT, SM)                                                                \
   {                                                                                  \
     uint8_t* base_ = (SM);                                                           \
     _Pragma("unroll") for (int i = 0; i < NA; ++i)                                   \
-        dma16(srcA[i] + (KT) * RB, base_ + (wave + NWAVE * i) * 1024);             \
+        dma16(rA, voffA[i], (KT) * RB, base_ + (wave + NWAVE * i) * 1024);         \
     _Pragma("unroll") for (int i = 0; i < NW; ++i)                                   \
-        dma16(srcW[i] + (KT) * RB, base_ + W_OFF + (wave + NWAVE * i) * 1024);     \
+        dma16(rW, voffW[i], (KT) * RB, base_ + W_OFF + (wave + NWAVE * i) * 1024); \
     _Pragma("unroll") for (int j = 0; j < NE; ++j)                                   \
-        dma4(scale_src(j, (KT)), base_ + E_OFF + (NE * wave + j) * 256);           \
+        issue_scales(j, (KT), base_ + E_OFF + (NE * wave + j) * 256);              \
   }
 
   v16f acc[TI][TJ];
@@ -214,29 +231,31 @@ void k_mxfp4_gemm(Params p) {
     offA[u] = rowA * RB + 16 * ((2 * u + lhi) ^ ((rowA >> SWS) & (SL - 1)));
     offW[u] = rowW * RB + 16 * ((2 * u + lhi) ^ ((rowW >> SWS) & (SL - 1)));
   }
-  uint4 av[TI], wv[TJ];     // one 64-k step's operands (FP4: 16 bytes per lane)
-  int ea[TI], ew[TJ];
+  // Operands of two 64-k steps (FP4: 16 bytes per lane): step u + 1 is read
+  // from LDS while the MFMAs of step u run.
+  uint4 av[2][TI], wv[2][TJ];
+  int ea[2][TI], ew[2][TJ];
 
 // Operands of one 64-k MFMA step U from ring slot SM: lane l feeds 32-block
 // 2U + l/32 of the stage in its row and that block's E8M0 byte (byte
 // 2 (U % 2) + l/32 of the row's scale dword U / 2). The swizzle term of row
 // + 32 i equals that of row, so one base per step serves every row block i.
-#define LOAD_OPS(SM, U)                                                               \
+#define LOAD_OPS(SM, U, B)                                                            \
   {                                                                                  \
     const uint8_t* st_ = (SM);                                                       \
     const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF) + (U) / 2;  \
     _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                 \
-      av[i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 32 * RB * i);         \
-      ea[i] = (int)((se_[NEW * (rowA + 32 * i)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
+      av[B][i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 32 * RB * i);      \
+      ea[B][i] = (int)((se_[NEW * (rowA + 32 * i)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
     _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                 \
-      wv[j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 32 * RB * j); \
-      ew[j] = (int)((se_[NEW * (BM + rowW + 32 * j)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
+      wv[B][j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 32 * RB * j); \
+      ew[B][j] = (int)((se_[NEW * (BM + rowW + 32 * j)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
   }
 // Matrix work of step U of stage KT. The partials variant runs one 32-block at
 // a time with unit scales, so D = sum va*vw over that block exactly.
-#define MMA_STEP(KT, U)                                                              \
+#define MMA_STEP(KT, U, B)                                                           \
   {                                                                                  \
     if constexpr (PARTIALS) {                                                        \
       const v8i zero_ = v8i{0, 0, 0, 0, 0, 0, 0, 0};                                 \
@@ -247,7 +266,7 @@ void k_mxfp4_gemm(Params p) {
           v16f zacc;                                                                 \
           _Pragma("unroll") for (int r = 0; r < 16; ++r) zacc[r] = 0.0f;             \
           const v16f d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(            \
-              lhi == h ? as_operand(av[i]) : zero_, lhi == h ? as_operand(wv[j]) : zero_, zacc, \
+              lhi == h ? as_operand(av[B][i]) : zero_, lhi == h ? as_operand(wv[B][j]) : zero_, zacc, \
               kFmtFp4, kFmtFp4, 0, kUnitScale, 0, kUnitScale);                       \
           _Pragma("unroll") for (int r = 0; r < 16; ++r) {                           \
             const int m = tile_m + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3); \
@@ -261,8 +280,16 @@ void k_mxfp4_gemm(Params p) {
       _Pragma("unroll") for (int i = 0; i < TI; ++i)                                 \
       _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                 \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
-            as_operand(av[i]), as_operand(wv[j]), acc[i][j], kFmtFp4, kFmtFp4, 0, ea[i], 0, ew[j]); \
+            as_operand(av[B][i]), as_operand(wv[B][j]), acc[i][j], kFmtFp4, kFmtFp4, 0, ea[B][i], 0, ew[B][j]); \
     }                                                                                \
+  }
+// Keeps the next step's LDS reads ahead of this step's MFMAs.
+#ifndef PIPE_FENCE_ON
+#define PIPE_FENCE_ON 1
+#endif
+#define PIPE_FENCE()                                                    \
+  {                                                                     \
+    if (PIPE_FENCE_ON) __builtin_amdgcn_sched_barrier(0);               \
   }
 // Barrier between ring stages. Each wave has already waited for its own
 // direct loads of the stage (vmcnt), so after the barrier every wave's part of
@@ -286,12 +313,13 @@ void k_mxfp4_gemm(Params p) {
     if (D == 2 && (KT) + 1 < nk) wait_vmcnt<(D - 1) * PER_STAGE>();     \
     else wait_vmcnt<0>();                                               \
     STAGE_BARRIER();                                                    \
-    LOAD_OPS(CUR, 0);                                                   \
+    LOAD_OPS(CUR, 0, 0);                                                \
     if ((KT) + D < nk) ISSUE((KT) + D, NXT);                            \
-    MMA_STEP(KT, 0);                                                    \
-    _Pragma("unroll") for (int u_ = 1; u_ < NSTEP; ++u_) {              \
-      LOAD_OPS(CUR, u_);                                                \
-      MMA_STEP(KT, u_);                                                 \
+    _Pragma("unroll") for (int u_ = 0; u_ < NSTEP; ++u_) {              \
+      if (u_ + 1 < NSTEP) LOAD_OPS(CUR, u_ + 1, (u_ + 1) & 1);          \
+      PIPE_FENCE();                                                     \
+      MMA_STEP(KT, u_, u_ & 1);                                         \
+      PIPE_FENCE();                                                     \
     }                                                                   \
   }
 

@@ -85,3 +85,27 @@ def test_qwen_shapes_sampled(name):
     cw2, _ = oracle.mxfp4_quantize(synth.weights(N, K, seed=0, rows=np.arange(n0, n0 + win)))
     for b, I in oracle.mxfp4_block_partials(ca2, cw2):
         assert np.array_equal(part[b], I), f"block {b}"
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 200, 512), (256, 392, 768)])
+def test_full_row_tiles_fp16_and_strided_y(M, N, K):
+    """Row tiles that are all valid (the store path with scalar row offsets),
+    a ragged last column tile (its lanes beyond N must store nothing), fp16
+    output, and an output with ldy > N whose padding must stay untouched."""
+    import torch
+    run_case(M, N, K, seed=7, check_fp16=True)
+    o = ops()
+    x = synth.activations(M, K, seed=8)
+    w = synth.weights(N, K, seed=8)
+    xq, xe = o.mxfp4_quantize(dev(x))
+    wq, we = o.mxfp4_quantize(dev(w))
+    Y, T = oracle.mxfp4_gemm(*oracle.mxfp4_quantize(x), *oracle.mxfp4_quantize(w))
+    for dt in (torch.float32, torch.float16):
+        big = torch.full((M, N + 40), 7.0, dtype=dt, device="cuda")
+        o.mxfp4_gemm(xq, xe, wq, we, out_dtype=dt, out=big[:, :N])
+        b = host(big).astype(np.float64)
+        assert np.all(b[:, N:] == 7.0), "padding columns written"
+        if dt == torch.float32:
+            assert_y_close(b[:, :N], Y, T, "strided fp32")
+        else:
+            assert_y16_close(b[:, :N], Y, T, "strided fp16")

@@ -352,21 +352,63 @@ void k_mxfp4_gemm(Params p) {
 #undef ISSUE
 
   if constexpr (!PARTIALS) {
+    if (a_rows == BM) {
+      // Every row of the tile is valid: buffer stores with the row offset of
+      // each accumulator register in the scalar offset and no per-element
+      // address arithmetic or branches. A lane whose column is >= N gets a
+      // vector offset past the resource, so the hardware drops its stores
+      // (the range check covers the vector offset; rows need none here).
+      const int esz = p.ydtype == 0 ? 4 : 2;
+      const int ldb = (int)(p.ldy * esz);              // host: 256 * ldb < 2^31
+      const __amdgpu_buffer_rsrc_t rY =
+          buffer_rsrc(static_cast<uint8_t*>(p.y) + (int64_t)tile_m * ldb, BM * ldb);
+      const int row0 = wm * (BM / WM) + 4 * lhi;       // tile row of register 0, block 0
+      int voffY[TJ];
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int j = 0; j < TJ; ++j) {
+        const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
+        voffY[j] = n < p.N ? row0 * ldb + n * esz : (int)0x80000000;
+      }
+      if (p.ydtype == 0) {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = tile_m + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
-          if (m < p.M && n < p.N) {
-            if (p.ydtype == 0)
-              static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i][j][r];
-            else
-              static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) {
+            const int soff = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rY, voffY[j], soff, 0);
           }
-        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int soff = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+              __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(acc[i][j][r])), rY,
+                                                    voffY[j], soff, 0);
+          }
+      }
+    } else {
+      // last row tile of a ragged M: per-element checked stores
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = tile_m + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
+            const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
+            if (m < p.M && n < p.N) {
+              if (p.ydtype == 0)
+                static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i][j][r];
+              else
+                static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
+            }
+          }
+    }
   }
 }
 

@@ -159,9 +159,8 @@ w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx
  *   xq, xe   activation codes [M][K/2], M * K/32 scale bytes (panel layout
  *            of mxfp4_quantize)
  *   wq, we   weight codes [N][K/2], N * K/32 scale bytes (panel layout)
- *   K > 0, K % 128 == 0, K <= 2^23; y as for w4a4_gemm with 256 rows of y
- *   spanning < 2^31 bytes (ldy < 2^21 for fp32). The kernel addresses a
- *   256-row tile of X, W and Y with 32-bit offsets. xq, wq 16-byte aligned.
+ *   K > 0, K % 128 == 0, K <= 2^23 (the kernel addresses a 256-row tile of
+ *   X and W with 32-bit offsets); y as for w4a4_gemm. xq, wq 16-byte aligned.
  */
 w4a4_status_t mxfp4_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,
                          int64_t M, int64_t N, int64_t K,

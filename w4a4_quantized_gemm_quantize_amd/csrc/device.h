@@ -36,6 +36,17 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Raw buffer resource over [base, base + bytes): loads beyond the range read
+// 0 and stores beyond it are dropped (the range check covers the vector
+// offset). Word 3 is the CDNA raw-buffer format word (32-bit data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// A vector offset past any buffer resource of < 2^31 bytes: stores through it
+// are dropped, even with a scalar offset < 2^31 added.
+constexpr int kDroppedOffset = (int)0x80000000u;
+
 // Eight fp16 values from one 16-byte load, widened exactly to fp32.
 __device__ __forceinline__ void halves_to_float8(uint4 raw, float f[8]) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};

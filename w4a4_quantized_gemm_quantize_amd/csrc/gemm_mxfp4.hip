@@ -60,11 +60,6 @@ __device__ __forceinline__ v8i as_operand(uint4 v) {
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 
-// Raw buffer resource over [base, base + bytes): loads beyond the range read 0.
-// Word 3 is the CDNA raw-buffer format word (32-bit data, no swizzle).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 // Direct buffer -> LDS copies: lane l's 16 (4) bytes from base + voff + soff
 // land at lds + 16 l (4 l). The buffer (MUBUF) form, unlike the global (FLAT)
 // form, lets the compiler keep exact LDS-read wait counts while these loads
@@ -352,14 +347,15 @@ void k_mxfp4_gemm(Params p) {
 #undef ISSUE
 
   if constexpr (!PARTIALS) {
-    if (a_rows == BM) {
-      // Every row of the tile is valid: buffer stores with the row offset of
-      // each accumulator register in the scalar offset and no per-element
-      // address arithmetic or branches. A lane whose column is >= N gets a
-      // vector offset past the resource, so the hardware drops its stores
-      // (the range check covers the vector offset; rows need none here).
-      const int esz = p.ydtype == 0 ? 4 : 2;
-      const int ldb = (int)(p.ldy * esz);              // host: 256 * ldb < 2^31
+    const int esz = p.ydtype == 0 ? 4 : 2;
+    if (a_rows == BM && (int64_t)BM * p.ldy * esz < (int64_t{1} << 31)) {
+      // Every row of the tile is valid and the tile spans < 2^31 bytes: buffer
+      // stores with the row offset of each accumulator register in the scalar
+      // offset and no per-element address arithmetic or branches. A lane whose
+      // column is >= N gets a vector offset past the resource, so the hardware
+      // drops its stores (the range check covers the vector offset; rows need
+      // none here).
+      const int ldb = (int)(p.ldy * esz);
       const __amdgpu_buffer_rsrc_t rY =
           buffer_rsrc(static_cast<uint8_t*>(p.y) + (int64_t)tile_m * ldb, BM * ldb);
       const int row0 = wm * (BM / WM) + 4 * lhi;       // tile row of register 0, block 0
@@ -367,7 +363,7 @@ void k_mxfp4_gemm(Params p) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
-        voffY[j] = n < p.N ? row0 * ldb + n * esz : (int)0x80000000;
+        voffY[j] = n < p.N ? row0 * ldb + n * esz : kDroppedOffset;
       }
       if (p.ydtype == 0) {
 #pragma unroll
@@ -392,7 +388,7 @@ void k_mxfp4_gemm(Params p) {
           }
       }
     } else {
-      // last row tile of a ragged M: per-element checked stores
+      // last row tile of a ragged M (or a huge ldy): per-element checked stores
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll

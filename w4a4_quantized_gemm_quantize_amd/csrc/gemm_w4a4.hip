@@ -338,22 +338,58 @@ void k_w4a4_gemm(Params p) {
 #undef STAGE
 
   if constexpr (!PARTIALS) {
+    const int esz = p.ydtype == 0 ? 4 : 2;
+    if (tile_m + BM <= p.M && (int64_t)BM * p.ldy * esz < (int64_t{1} << 31)) {
+      // Every row of the tile is valid and the tile spans < 2^31 bytes: buffer
+      // stores with each register's row offset in the scalar offset, no
+      // per-element address arithmetic or branches. A lane whose column is
+      // >= N gets an offset past the resource, so its stores are dropped.
+      const int ldb = (int)(p.ldy * esz);
+      const __amdgpu_buffer_rsrc_t rY =
+          buffer_rsrc(static_cast<uint8_t*>(p.y) + (int64_t)tile_m * ldb, BM * ldb);
+      const int row0 = wm * 64 + 4 * lhi;                // tile row of register 0, block 0
+      int voffY[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int n = tile_n + wn * 64 + j * 32 + l32;
+        voffY[j] = n < p.N ? row0 * ldb + n * esz : kDroppedOffset;
+      }
+      const float* sa_rows = p.sa + tile_m + row0;       // ROWA: xs[m], one group
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = tile_m + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          const int n = tile_n + wn * 64 + j * 32 + l32;
-          if (m < p.M && n < p.N) {
-            const float v = ROWA ? acc[i][j][r] * p.sa[m] : acc[i][j][r];   // one group: xs[m]
+          const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+          const int soff = dr * ldb;
+          const float sa = ROWA ? sa_rows[dr] : 1.0f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float v = ROWA ? acc[i][j][r] * sa : acc[i][j][r];
             if (p.ydtype == 0)
-              static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = v;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rY, voffY[j], soff, 0);
             else
-              static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(v);
+              __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(v)), rY, voffY[j], soff, 0);
           }
         }
+    } else {
+      // last row tile of a ragged M (or a huge ldy): per-element checked stores
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = tile_m + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);
+            const int n = tile_n + wn * 64 + j * 32 + l32;
+            if (m < p.M && n < p.N) {
+              const float v = ROWA ? acc[i][j][r] * p.sa[m] : acc[i][j][r];   // one group: xs[m]
+              if (p.ydtype == 0)
+                static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = v;
+              else
+                static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(v);
+            }
+          }
+    }
   }
 }
 

@@ -25,18 +25,23 @@
  *   - Extents are int64_t element counts. A zero extent (M, N or rows == 0) is a
  *     valid no-op; pointers whose extent is zero may then be NULL.
  *   - Buffers must not overlap. Results are deterministic (no atomics).
- *   - Packed 4-bit codes are row-major [rows][K/2] bytes, K contiguous, two
- *     codes per byte.
+ *   - Packed 4-bit codes are row-major [rows][K/2] bytes, K contiguous, 4 bits
+ *     per code.
  *     MXFP4: E2M1 codes (sign<<3 | magnitude index into {0,0.5,1,1.5,2,3,4,6}),
- *     the even k in the LOW nibble.
+ *     two per byte, the even k in the LOW nibble.
  *     INT4: sign-magnitude (the symmetric rule below only yields codes in
  *     [-7, 7]), the sign bit being that of the input value (a negative input
- *     that rounds to 0 is stored as -0). Each little-endian 32-bit word holds
- *     the codes c0..c7 of 8 consecutive k; its byte b (0..3) holds sign(c_b) in
- *     bit 7, |c_b| in bits 2..0, |c_(4+b)| in bits 6..4 and sign(c_(4+(b+3)%4))
- *     in bit 3. The arrangement lets the GEMM form the 8 FP8 E4M3 operand bytes
- *     [sign 0000 |c|] (value +-|c| * 2^-9, exact) as word & 0x87878787 and
- *     rotr(word, 4) & 0x87878787.
+ *     that rounds to 0 is stored as -0). Each 8-byte unit holds the codes
+ *     c0..c15 of 16 consecutive k as two little-endian 32-bit words X, Y. Let
+ *     S be the 96-bit stream with the 6-bit field f_k = sign_k << 5 | |c_k| at
+ *     bits 6k..6k+5 -- the OCP FP6 E2M3 encoding of the subnormal +-|c_k|/8,
+ *     whose bits 3 and 4 are always zero -- and S0, S1, S2 its 32-bit words:
+ *       X = S0 | (S1 & 0x18618618),   Y = S2 | (S1 & 0x61861861)
+ *     (0x18618618 marks bit positions 3, 4 mod 6, where S0 is zero;
+ *     0x61861861 marks 0, 5 mod 6, where S2 is zero). The GEMM rebuilds its
+ *     FP6 operand as S0 = X & 0xE79E79E7, S1 = (X & 0x18618618) |
+ *     (Y & 0x61861861), S2 = Y & 0x9E79E79E; the matrix cores then multiply
+ *     the codes exactly (E8M0 scale 2^3 per operand).
  */
 #ifndef W4A4_H
 #define W4A4_H
@@ -75,9 +80,9 @@ const char* w4a4_status_str(int status);
  * |x| <= a makes |q| <= 7, so the codes fit the sign-magnitude layout above.
  *
  *   x     fp16 [M][ldx] row-major, 16-byte aligned, ldx >= K, ldx % 8 == 0
- *   M, K  K > 0, K % 8 == 0 (K % group == 0 required as well)
+ *   M, K  K > 0, K % 16 == 0 (K % group == 0 required as well)
  *   group 64, 128, 256, 512, or group == K ("per token")
- *   xq    out: u8 [M][K/2] packed codes (layout above), 4-byte aligned
+ *   xq    out: u8 [M][K/2] packed codes (layout above), 8-byte aligned
  *   xs    out: f32 [K/group][M] scales, group-major (the scale of row m and
  *         group c is xs[c * M + m]), 4-byte aligned. One K stage of a GEMM tile
  *         then reads its rows' scales as one contiguous run.
@@ -90,7 +95,7 @@ w4a4_status_t w4a4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx
  * rule as w4a4_quantize_act applied to the rows of W[N][K] (ldw = K).
  *
  *   w     fp16 [N][K], 16-byte aligned
- *   wq    out: u8 [N][K/2];  ws  out: f32 [K/group][N] (group-major, as xs)
+ *   wq    out: u8 [N][K/2] (8-byte aligned);  ws  out: f32 [K/group][N] (group-major, as xs)
  */
 w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t group,
                                uint8_t* wq, float* ws, void* stream);

@@ -16,16 +16,19 @@ taken here:
   -8, 7)``; an all-zero group has ``s = 0`` and codes 0;
 * scales are IEEE binary32; divisions are correctly rounded binary32 (the
   precision the kernel makes the integer decision in); ties round to even;
-* packed layout (the pages give none): row-major, K contiguous, two codes per
-  byte, sign-magnitude. The symmetric rule only yields codes in [-7, 7] (the
+* packed layout (the pages give none): row-major, K contiguous, 4 bits per
+  code, sign-magnitude. The symmetric rule only yields codes in [-7, 7] (the
   clamp at -8 never fires), so a sign bit and a 3-bit magnitude hold every code.
   A code's sign bit is the sign bit of its input value (so a negative input that
-  rounds to 0 is stored as -0). Each little-endian 32-bit word holds the 8 codes
-  c0..c7 of k = 8j .. 8j+7; its byte b (b = 0..3) holds the sign of c_b in bit 7,
-  |c_b| in bits 2..0, |c_(4+b)| in bits 6..4 and the sign of c_(4+(b+3) mod 4)
-  in bit 3. (With that arrangement ``word & 0x87878787`` and
-  ``rotr(word, 4) & 0x87878787`` are the OCP FP8 E4M3 bytes [sign 0000 mag] of
-  c0..c3 and c4..c7, whose values are exactly +-|c| * 2^-9.);
+  rounds to 0 is stored as -0). Each 8-byte unit holds the 16 codes c0..c15 of
+  k = 16j .. 16j+15 as two little-endian 32-bit words X, Y, defined through the
+  96-bit stream S of 6-bit fields ``f_k = sign_k << 5 | |c_k|`` at bits 6k..6k+5
+  (f_k is the OCP FP6 E2M3 encoding of the subnormal +-|c_k|/8, so its bits 3
+  and 4 are zero). With S0, S1, S2 the 32-bit words of S,
+  ``X = S0 | (S1 & FOLD_X)`` and ``Y = S2 | (S1 & FOLD_Y)``: FOLD_X marks the
+  bits of a word at positions 3, 4 mod 6 (where S0 is zero), FOLD_Y those at
+  0, 5 mod 6 (where S2 is zero), and together they cover every bit that S1
+  can have set. The kernel rebuilds S with two ANDs and an AND-OR.;
 * the GEMM is ``Y = X W^T`` (a linear layer), A = activations [M, K] and
   W = weights [N, K]; with ``g = min(g_a, g_w)`` (nested groups) the per-block
   integer partial is ``P_b[m, n] = sum_{k in block b} qa[m,k] qw[n,k]`` and
@@ -98,46 +101,74 @@ def unpack_nibbles_unsigned(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+FOLD_X = sum(1 << q for q in range(32) if q % 6 in (3, 4))   # 0x18618618
+FOLD_Y = sum(1 << q for q in range(32) if q % 6 in (0, 5))   # 0x61861861
+_MASK32 = 0xFFFFFFFF
+
+
+def _stream_words(fields: np.ndarray):
+    """The 96-bit stream of 16 six-bit fields [..., 16] as three uint64 arrays
+    holding its 32-bit words S0, S1, S2 (field k at stream bits 6k..6k+5)."""
+    words = []
+    for d in range(3):
+        acc = np.zeros(fields.shape[:-1], dtype=np.uint64)
+        for k in range(16):
+            sh = 6 * k - 32 * d
+            if -6 < sh < 32:
+                f = fields[..., k].astype(np.uint64)
+                acc |= (f << np.uint64(sh)) if sh >= 0 else (f >> np.uint64(-sh))
+        words.append(acc & np.uint64(_MASK32))
+    return words
+
+
 def pack_int4(codes: np.ndarray, negative: np.ndarray) -> np.ndarray:
     """Sign-magnitude INT4 packing (layout in the module docstring).
 
-    ``codes``: int [R, K] in [-7, 7], K a multiple of 8; ``negative``: bool
+    ``codes``: int [R, K] in [-7, 7], K a multiple of 16; ``negative``: bool
     [R, K], the sign bit of each code (must agree with the code where it is not
     zero). Returns uint8 [R, K/2].
     """
     c = np.asarray(codes).astype(np.int16)
     neg = np.asarray(negative, dtype=bool)
-    if c.ndim != 2 or c.shape[1] % 8 or neg.shape != c.shape:
-        raise ValueError("codes and signs must be 2-D, equal shapes, K a multiple of 8")
+    if c.ndim != 2 or c.shape[1] % 16 or neg.shape != c.shape:
+        raise ValueError("codes and signs must be 2-D, equal shapes, K a multiple of 16")
     if np.abs(c).max(initial=0) > 7:
         raise ValueError("sign-magnitude INT4 holds codes in [-7, 7]")
     if np.any((c != 0) & (neg != (c < 0))):
         raise ValueError("sign bits disagree with nonzero codes")
     R, K = c.shape
-    m = np.abs(c).astype(np.uint8).reshape(R, K // 8, 8)
-    sg = neg.astype(np.uint8).reshape(R, K // 8, 8)
-    out = np.empty((R, K // 8, 4), dtype=np.uint8)
-    for b in range(4):
-        out[..., b] = ((sg[..., b] << 7) | (m[..., 4 + b] << 4)
-                       | (sg[..., 4 + (b + 3) % 4] << 3) | m[..., b])
-    return out.reshape(R, K // 2)
+    fields = ((neg.astype(np.uint8) << 5) | np.abs(c).astype(np.uint8)).reshape(R, K // 16, 16)
+    s0, s1, s2 = _stream_words(fields)
+    x = s0 | (s1 & np.uint64(FOLD_X))
+    y = s2 | (s1 & np.uint64(FOLD_Y))
+    out = np.empty((R, K // 16, 2), dtype="<u4")
+    out[..., 0] = x.astype(np.uint32)
+    out[..., 1] = y.astype(np.uint32)
+    return out.reshape(R, K // 8).view(np.uint8).reshape(R, K // 2)
 
 
 def unpack_int4(packed: np.ndarray):
     """Inverse of :func:`pack_int4`: ``(codes int8 [R, K], negative bool [R, K])``."""
     p = np.asarray(packed, dtype=np.uint8)
-    if p.ndim != 2 or p.shape[1] % 4:
-        raise ValueError("packed rows must hold whole 32-bit words")
+    if p.ndim != 2 or p.shape[1] % 8:
+        raise ValueError("packed rows must hold whole 8-byte units")
     R, H = p.shape
-    w = p.reshape(R, H // 4, 4)
-    m = np.empty((R, H // 4, 8), dtype=np.int16)
-    sg = np.empty((R, H // 4, 8), dtype=bool)
-    for b in range(4):
-        m[..., b] = w[..., b] & 7
-        sg[..., b] = (w[..., b] >> 7) & 1
-        m[..., 4 + b] = (w[..., b] >> 4) & 7
-        sg[..., 4 + (b + 3) % 4] = (w[..., b] >> 3) & 1
-    codes = np.where(sg, -m, m).astype(np.int8)
+    w = np.ascontiguousarray(p).view("<u4").reshape(R, H // 8, 2).astype(np.uint64)
+    x, y = w[..., 0], w[..., 1]
+    s0 = x & np.uint64(_MASK32 ^ FOLD_X)
+    s1 = (x & np.uint64(FOLD_X)) | (y & np.uint64(FOLD_Y))
+    s2 = y & np.uint64(_MASK32 ^ FOLD_Y)
+    stream = [s0, s1, s2]
+    fields = np.empty((R, H // 8, 16), dtype=np.uint64)
+    for k in range(16):
+        d, o = divmod(6 * k, 32)
+        f = stream[d] >> np.uint64(o)
+        if o > 26:
+            f |= stream[d + 1] << np.uint64(32 - o)
+        fields[..., k] = f & np.uint64(63)
+    mag = (fields & np.uint64(7)).astype(np.int16)
+    sg = (fields >> np.uint64(5)).astype(bool)
+    codes = np.where(sg, -mag, mag).astype(np.int8)
     return codes.reshape(R, 2 * H), sg.reshape(R, 2 * H)
 
 

@@ -61,7 +61,8 @@ def test_quantize_act_validation(lib):
     M, K = 4, 256
     assert q(P, -1, K, K, 128, P, P, None) == E_SHAPE
     assert q(P, M, 0, K, 128, P, P, None) == E_SHAPE
-    assert q(P, M, 260, 264, 128, P, P, None) == E_SHAPE      # K % 8 != 0 ... 260 % 8 = 4
+    assert q(P, M, 260, 264, 128, P, P, None) == E_SHAPE      # K % 16 != 0 (260 % 16 = 4)
+    assert q(P, M, 264, 264, 264, P, P, None) == E_SHAPE      # per token, but 264 % 16 = 8
     assert q(P, M, K, K - 8, 128, P, P, None) == E_SHAPE     # ldx < K
     assert q(P, M, K, K, 96, P, P, None) == E_GROUP
     assert q(P, M, K, K, 512, P, P, None) == E_GROUP         # 512 does not divide 256
@@ -72,6 +73,7 @@ def test_quantize_act_validation(lib):
     assert q(P, M, K, K, 128, None, P, None) == E_NULL
     assert q(P + 8, M, K, K, 128, P, P, None) == E_ALIGN
     assert q(P, M, K, K, 128, P + 2, P, None) == E_ALIGN
+    assert q(P, M, K, K, 128, P + 4, P, None) == E_ALIGN        # 8-byte packed units
     assert _lib.status_of("w4a4_pack_weight", P, M, K, 100, P, P, None) == E_GROUP
     assert _lib.status_of("w4a4_pack_weight", None, M, K, 128, P, P, None) == E_NULL
 

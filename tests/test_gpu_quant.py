@@ -47,7 +47,7 @@ def test_int4_groups_ragged_rows(group):
 def test_int4_strided_rows_and_per_token_long_rows():
     int4_check(synth.activations(9, 1024, dist="t3", seed=2), 128, ldx_pad=64)
     int4_check(synth.activations(5, 28672, dist="t3", seed=3), 28672)
-    int4_check(synth.activations(3, 1000, dist="t3", seed=3), 1000)     # per token, K % 128 != 0
+    int4_check(synth.activations(3, 1008, dist="t3", seed=3), 1008)     # per token, K % 128 != 0
 
 
 def test_int4_zero_rows_and_groups():

@@ -164,52 +164,134 @@ def test_pack_nibbles_generic_layout():
     assert np.array_equal(oracle.unpack_nibbles_unsigned(oracle.pack_nibbles(u)), u)
 
 
+def table_pack16(c, neg):
+    """The INT4 word of 16 codes from an explicit bit-position table (a second,
+    independent statement of the layout): returns (X, Y) as Python ints.
+    X: c0..c4 magnitude at 6k..6k+2, sign at 6k+5; c5 magnitude bits 0, 1 at 30,
+       31, sign at 3; c6..c9 magnitude bit 0 at 6(k-6)+4, sign at 6(k-6)+9;
+       c10 magnitude bit 0 at 28.
+    Y: c5 magnitude bit 2 at 0; c10 sign at 1; c6..c10 magnitude bits 1, 2 at
+       6(k-6)+5, 6(k-6)+6; c11..c15 magnitude at 6(k-11)+2..+4, sign at 6(k-11)+7."""
+    m = [abs(int(v)) for v in c]
+    sg = [int(bool(v)) for v in neg]
+    bit = lambda v, i: (v >> i) & 1
+    x = y = 0
+    for k in range(5):
+        x |= m[k] << (6 * k) | sg[k] << (6 * k + 5)
+    x |= bit(m[5], 0) << 30 | bit(m[5], 1) << 31 | sg[5] << 3
+    y |= bit(m[5], 2) << 0
+    for k in range(6, 10):
+        x |= bit(m[k], 0) << (6 * (k - 6) + 4) | sg[k] << (6 * (k - 6) + 9)
+    x |= bit(m[10], 0) << 28
+    y |= sg[10] << 1
+    for k in range(6, 11):
+        y |= bit(m[k], 1) << (6 * (k - 6) + 5) | bit(m[k], 2) << (6 * (k - 6) + 6)
+    for k in range(11, 16):
+        y |= m[k] << (6 * (k - 11) + 2) | sg[k] << (6 * (k - 11) + 7)
+    return x, y
+
+
+def words(p):
+    w = np.ascontiguousarray(p).view("<u4").reshape(-1)
+    return [int(v) for v in w]
+
+
+def test_pack_int4_bit_table_covers_each_bit_once():
+    """Every one of the 64 bits belongs to exactly one (code, bit) pair."""
+    seen = {}
+    for k in range(16):
+        for b in range(4):          # magnitude bits 0..2, sign as bit 3
+            c = [0] * 16
+            neg = [False] * 16
+            if b < 3:
+                c[k] = 1 << b
+            else:
+                neg[k] = True
+            x, y = table_pack16(c, neg)
+            v = x | y << 32
+            assert v and v & (v - 1) == 0
+            assert v not in seen
+            seen[v] = (k, b)
+    assert len(seen) == 64
+
+
 def test_pack_int4_hand_computed_word():
-    """c = [1, -2, 3, -4, 5, -6, 7, -7], worked out bit by bit from the layout:
-    byte0 = s0<<7 | |c4|<<4 | s7<<3 | |c0| = 0 | 0x50 | 0x08 | 1 = 0x59,
-    byte1 = s1<<7 | |c5|<<4 | s4<<3 | |c1| = 0x80 | 0x60 | 0 | 2 = 0xE2,
-    byte2 = s2<<7 | |c6|<<4 | s5<<3 | |c2| = 0 | 0x70 | 0x08 | 3 = 0x7B,
-    byte3 = s3<<7 | |c7|<<4 | s6<<3 | |c3| = 0x80 | 0x70 | 0 | 4 = 0xF4."""
-    c = np.array([[1, -2, 3, -4, 5, -6, 7, -7]], dtype=np.int8)
+    """c = [1, -2, 3, -4, 5, -6, 7, -7, 0, 1, 2, 3, -5, 6, -1, 4], summed by hand
+    from the bit table:
+    X = c0 0x1 + c1 0x80|0x800 + c2 0x3000 + c3 0x100000|0x800000 + c4 0x5000000
+        + c5 (m1) 0x80000000 (sign) 0x8 + c6 (m0) 0x10 + c7 (m0) 0x400 (sign) 0x8000
+        + c9 (m0) 0x400000 = 0x85D0BC99;
+    Y = c5 (m2) 0x1 + c6 0x20|0x40 + c7 0x800|0x1000 + c10 (m1) 0x20000000
+        + c11 0xC + c12 0x500|0x2000 + c13 0x18000 + c14 0x100000|0x2000000
+        + c15 0x10000000 = 0x3211BD6D."""
+    c = np.array([[1, -2, 3, -4, 5, -6, 7, -7, 0, 1, 2, 3, -5, 6, -1, 4]], dtype=np.int8)
+    x, y = table_pack16(c[0], c[0] < 0)
+    assert (x, y) == (0x85D0BC99, 0x3211BD6D)
     p = oracle.pack_int4(c, c < 0)
-    assert p.tolist() == [[0x59, 0xE2, 0x7B, 0xF4]]
+    assert words(p) == [x, y]
     codes, neg = oracle.unpack_int4(p)
     assert np.array_equal(codes, c) and np.array_equal(neg, c < 0)
-    # negative zero: c5 is a high code, so its sign is bit 3 of byte (5 - 4 + 1) % 4 = 2;
-    # c2 is a low code, its sign is bit 7 of byte 2
-    z = np.zeros((1, 8), np.int8)
-    negz = np.zeros((1, 8), bool)
-    negz[0, 5] = True
-    assert oracle.pack_int4(z, negz).tolist() == [[0, 0, 0x08, 0]]
-    negz[0, 5] = False
-    negz[0, 2] = True
-    assert oracle.pack_int4(z, negz).tolist() == [[0, 0, 0x80, 0]]
 
 
-def test_pack_int4_words_decode_to_fp8_e4m3():
-    """Design property of the layout: masking a word with 0x87878787, and its
-    4-bit rotation with the same mask, gives the OCP FP8 E4M3 bytes of
-    c0..c3 and c4..c7; an E4M3 byte [s 0000 mmm] is the subnormal
-    (-1)^s * 2^(1-7) * m/8 = +-m * 2^-9 (OCP 8-bit floating point, E4M3)."""
+def test_pack_int4_every_code_at_every_position():
+    for k in range(16):
+        for v in range(-7, 8):
+            for negzero in ([False, True] if v == 0 else [v < 0]):
+                c = np.zeros((1, 16), np.int8)
+                neg = np.zeros((1, 16), bool)
+                c[0, k] = v
+                neg[0, k] = negzero
+                assert words(oracle.pack_int4(c, neg)) == list(table_pack16(c[0], neg[0])), (k, v, negzero)
+
+
+def test_pack_int4_random_words_match_bit_table():
+    rng = np.random.default_rng(3)
+    c = rng.integers(-7, 8, size=(4, 64)).astype(np.int8)
+    neg = (c < 0) | ((c == 0) & (rng.random(c.shape) < 0.5))
+    w = words(oracle.pack_int4(c, neg))
+    for r in range(4):
+        for j in range(4):
+            assert w[8 * r + 2 * j: 8 * r + 2 * j + 2] == list(table_pack16(c[r, 16 * j:16 * j + 16],
+                                                                            neg[r, 16 * j:16 * j + 16]))
+
+
+def test_pack_int4_words_widen_to_fp6_e2m3():
+    """Design property of the layout: S0 = X & ~FOLD_X, S1 = (X & FOLD_X) |
+    (Y & FOLD_Y), S2 = Y & ~FOLD_Y is the 96-bit stream of OCP FP6 E2M3 fields
+    (sign, 2 exponent bits, 3 mantissa bits, bias 1) of c0..c15, field k at bits
+    6k..6k+5, whose values are exactly c_k / 8 (subnormals m/8); with E8M0
+    scales 2^3 on both operands the matrix cores then multiply exact integers."""
     rng = np.random.default_rng(0)
     c = rng.integers(-7, 8, size=(5, 64)).astype(np.int8)
     neg = (c < 0) | ((c == 0) & (rng.random(c.shape) < 0.5))
-    p = oracle.pack_int4(c, neg)
-    words = p.view("<u4")
+    w = words(oracle.pack_int4(c, neg))
+    fx, fy = 0x18618618, 0x61861861
 
-    def e4m3(byte):
-        s, e, m = byte >> 7, (byte >> 3) & 15, byte & 7
-        v = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+    def e2m3(f):
+        s, e, m = f >> 5, (f >> 3) & 3, f & 7
+        v = (m / 8) if e == 0 else (1 + m / 8) * 2.0 ** (e - 1)
         return -v if s else v
 
-    for r in range(c.shape[0]):
-        for j in range(words.shape[1]):
-            wd = int(words[r, j])
-            lo = wd & 0x87878787
-            hi = (((wd >> 4) | (wd << 28)) & 0xFFFFFFFF) & 0x87878787
-            got = [e4m3((lo >> (8 * b)) & 0xFF) for b in range(4)] + \
-                  [e4m3((hi >> (8 * b)) & 0xFF) for b in range(4)]
-            assert got == [float(v) * 2.0 ** -9 for v in c[r, 8 * j:8 * j + 8]]
+    for u in range(len(w) // 2):
+        x, y = w[2 * u], w[2 * u + 1]
+        s0 = x & (0xFFFFFFFF ^ fx)
+        s1 = (x & fx) | (y & fy)
+        s2 = y & (0xFFFFFFFF ^ fy)
+        stream = s0 | s1 << 32 | s2 << 64
+        fields = [(stream >> (6 * k)) & 63 for k in range(16)]
+        r, j = divmod(u, 4)
+        assert [e2m3(f) for f in fields] == [float(v) / 8 for v in c[r, 16 * j:16 * j + 16]]
+        assert all((f >> 3) & 3 == 0 for f in fields)          # subnormal encodings
+        assert [f >> 5 for f in fields] == [int(b) for b in neg[r, 16 * j:16 * j + 16]]
+
+
+def test_pack_int4_negative_zero_placement():
+    """-0 keeps its sign bit: c5 (sign at X bit 3), c10 (Y bit 1), c13 (Y bit 19)."""
+    for k, (xw, yw) in {5: (1 << 3, 0), 10: (0, 1 << 1), 13: (0, 1 << 19)}.items():
+        z = np.zeros((1, 16), np.int8)
+        negz = np.zeros((1, 16), bool)
+        negz[0, k] = True
+        assert words(oracle.pack_int4(z, negz)) == [xw, yw]
 
 
 def test_pack_int4_round_trip_and_rejects():
@@ -219,11 +301,11 @@ def test_pack_int4_round_trip_and_rejects():
     codes, n2 = oracle.unpack_int4(oracle.pack_int4(c, neg))
     assert np.array_equal(codes, c) and np.array_equal(n2, neg)
     with pytest.raises(ValueError):
-        oracle.pack_int4(np.full((1, 8), -8, np.int8), np.ones((1, 8), bool))
+        oracle.pack_int4(np.full((1, 16), -8, np.int8), np.ones((1, 16), bool))
     with pytest.raises(ValueError):
-        oracle.pack_int4(np.ones((1, 8), np.int8), np.ones((1, 8), bool))
+        oracle.pack_int4(np.ones((1, 16), np.int8), np.ones((1, 16), bool))
     with pytest.raises(ValueError):
-        oracle.pack_int4(np.ones((1, 12), np.int8), np.zeros((1, 12), bool))
+        oracle.pack_int4(np.ones((1, 8), np.int8), np.zeros((1, 8), bool))
 
 
 def test_sign_bits_follow_input():

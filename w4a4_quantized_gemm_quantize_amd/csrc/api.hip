@@ -73,12 +73,12 @@ const char* w4a4_status_str(int status) {
 
 w4a4_status_t w4a4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group,
                                 uint8_t* xq, float* xs, void* stream) {
-  if (M < 0 || K <= 0 || K % 8 || ldx < K) return W4A4_E_SHAPE;
+  if (M < 0 || K <= 0 || K % 16 || ldx < K) return W4A4_E_SHAPE;
   if (!quant_group_ok(K, group)) return W4A4_E_GROUP;
   if (ldx % 8) return W4A4_E_ALIGN;
   if (M == 0) return W4A4_OK;
   if (!x || !xq || !xs) return W4A4_E_NULL;
-  if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xs, 4)) return W4A4_E_ALIGN;
+  if (!aligned(x, 16) || !aligned(xq, 8) || !aligned(xs, 4)) return W4A4_E_ALIGN;
   w4a4::launch_int4_quant(x, M, K, ldx, group, xq, xs, as_stream(stream));
   return launched();
 }

@@ -5,18 +5,19 @@
 // per-group dequantization done by the vector units -- the cost it identifies
 // as the W4A4 bottleneck (its "rho", matrix-unit : vector-unit throughput).
 // On gfx950 the vector unit does 64 fp32 lane-ops per clock per CU against
-// 4096 8-bit MACs on the matrix cores (packed fp32 math is not used), so the
+// 8192 6-bit MACs on the matrix cores (packed fp32 math is not used), so the
 // design moves every piece of the dequantization it can onto the matrix cores
 // and keeps the vector work per output per group at ONE fma:
 //
-//   * gfx950 has no INT4 matrix instruction, but FP8 E4M3 holds every INT4
-//     code exactly: the byte [sign 0000 m] is the subnormal +-m * 2^-9. The
-//     codes are stored sign-magnitude in a layout where a packed word d gives
-//     the 8 operand bytes of its 8 codes as d & 0x87878787 (codes 0..3) and
-//     rotr(d, 4) & 0x87878787 (codes 4..7), in k order. The threads that stage
-//     a tile unpack it ONCE per workgroup into LDS.
+//   * gfx950 has no INT4 matrix instruction, but FP6 E2M3 holds every INT4
+//     code exactly: the field [sign 00 m] is the subnormal +-m/8, and the FP6
+//     path of the matrix cores runs at the FP4 rate, twice the FP8/INT8 rate.
+//     The codes are stored 4 bits each in a layout folded from that 6-bit
+//     stream (see the C header), so the threads that stage a tile rebuild the
+//     operand stream with two ANDs and one AND-OR per 16 codes, ONCE per
+//     workgroup, into LDS.
 //   * v_mfma_scale_f32_32x32x64_f8f6f4 multiplies them with an E8M0 scale of
-//     2^9 per operand, so each partial P_b = sum qa*qw comes out as an exact
+//     2^3 per operand, so each partial P_b = sum qa*qw comes out as an exact
 //     integer in fp32 (|P_b| <= 49 g < 2^24) -- no int->float convert.
 //   * The scale product t[m][n] = s_a[m] * s_w[n] is a rank-1 matrix: one
 //     two-block 32x32x1 fp32 MFMA gives it for two 32x32 tiles, in the lane
@@ -24,7 +25,7 @@
 //   * Epilogue per output per group: acc = fma(P, t, acc).
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; tile 128 x 128 outputs,
-// K stage 128 (two MFMA k-steps), double-buffered LDS (76 KB), two workgroups
+// K stage 128 (two MFMA k-steps), double-buffered LDS (61 KB), two workgroups
 // per CU (two waves per SIMD). The staging threads fetch stage kt+2 while
 // stage kt is computed and stage kt+1 is unpacked (two register sets), and the
 // stage barrier orders LDS only, so no wait drains those loads. Within a stage
@@ -37,9 +38,10 @@
 // W slices in that XCD's L2.
 //
 // 32x32 MFMA lane layout: operand lane l holds row (col) l%32 and the k-chunk
-// l/32 (32 consecutive k for FP8); result register r of lane l is row
-// 8*(r/4) + 4*(l/32) + r%4, col l%32 (block b of the two-block fp32 MFMA in
-// registers 16b .. 16b+15, with operand lanes 32b .. 32b+31).
+// l/32 (32 consecutive k: 24 bytes of FP6 fields, field i at bits 6i);
+// result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, col l%32
+// (block b of the two-block fp32 MFMA in registers 16b .. 16b+15, with operand
+// lanes 32b .. 32b+31).
 #include "device.h"
 #include "launch.h"
 
@@ -52,10 +54,16 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int ROW_BYTES = BK / 2;   // packed bytes per row per stage
-constexpr int PITCH = 144;          // LDS bytes per row: 128 FP8 + 16 pad (conflict-free 16 B reads)
+// LDS row of one 128-k stage: four 32-code FP6 operand chunks of 24 bytes,
+// each split into a 16-byte main part and an 8-byte tail, kept in two arrays
+// so every read is naturally aligned. Pitches 80 and 40 bytes put the 16 rows
+// read together by 16 lanes in distinct bank groups.
+constexpr int PM = 80;              // main part: 4 x 16 B + 16 pad
+constexpr int PT = 40;              // tail part: 4 x 8 B + 8 pad
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;       // tile-rows per raster group
-constexpr int kUnitScale = 127 + 9; // E8M0 2^9: FP8 [s 0000 m] * 2^9 = +-m
+constexpr int kUnitScale = 127 + 3; // E8M0 2^3: FP6 E2M3 [s 00 m] = +-m/8, times 2^3 = +-m
+constexpr int kFmtFp6 = 2;          // cbsz / blgp operand format code for FP6 E2M3
 
 // Group modes: epilogue after every 64-k step (g = 64), after every stage
 // (g = 128), or after several stages (g > 128).
@@ -79,20 +87,26 @@ struct Params {
   int32_t* partials;
 };
 
-__device__ __forceinline__ uint32_t fp8_lo(uint32_t d) { return d & 0x87878787u; }
-__device__ __forceinline__ uint32_t fp8_hi(uint32_t d) { return __builtin_amdgcn_alignbit(d, d, 4) & 0x87878787u; }
+// Folding masks of the packed INT4 unit (see the C header): X carries the
+// stream's first word S0 and, at positions 3, 4 mod 6 (kFoldX), bits of S1; Y
+// carries S2 and, at positions 0, 5 mod 6 (kFoldY), the rest of S1.
+constexpr uint32_t kFoldX = 0x18618618u;
+constexpr uint32_t kFoldY = 0x61861861u;
 
-// 32 packed codes (16 B) -> 32 FP8 operand bytes in LDS, k order.
-__device__ __forceinline__ void unpack_store(uint8_t* dst, uint4 v) {
-  *reinterpret_cast<uint4*>(dst) = uint4{fp8_lo(v.x), fp8_hi(v.x), fp8_lo(v.y), fp8_hi(v.y)};
-  *reinterpret_cast<uint4*>(dst + 16) = uint4{fp8_lo(v.z), fp8_hi(v.z), fp8_lo(v.w), fp8_hi(v.w)};
+// 32 packed codes (16 B = two units X0 Y0 X1 Y1) -> their 192-bit FP6 E2M3
+// operand stream S0..S5 in LDS: S0..S3 to the main part, S4, S5 to the tail.
+__device__ __forceinline__ void unpack_store(uint8_t* dm, uint8_t* dt, uint4 v) {
+  const uint32_t s1 = (v.x & kFoldX) | (v.y & kFoldY);
+  const uint32_t s4 = (v.z & kFoldX) | (v.w & kFoldY);
+  *reinterpret_cast<uint4*>(dm) = uint4{v.x & ~kFoldX, s1, v.y & ~kFoldY, v.z & ~kFoldX};
+  *reinterpret_cast<uint2*>(dt) = uint2{s4, v.w & ~kFoldY};
 }
 
-// 32 FP8 bytes of one lane's operand (row l%32, k-chunk l/32) from LDS.
-__device__ __forceinline__ v8i load_op(const uint8_t* p) {
-  const uint4 x = *reinterpret_cast<const uint4*>(p);
-  const uint4 y = *reinterpret_cast<const uint4*>(p + 16);
-  return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+// The 6 FP6 words of one lane's operand (row l%32, k-chunk l/32) from LDS.
+__device__ __forceinline__ v8i load_op(const uint8_t* pm, const uint8_t* pt) {
+  const uint4 x = *reinterpret_cast<const uint4*>(pm);
+  const uint2 y = *reinterpret_cast<const uint2*>(pt);
+  return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, 0, 0};
 }
 
 // Workgroup barrier that orders LDS only: __syncthreads() would also wait for
@@ -109,7 +123,7 @@ struct GroupScales {
 };
 
 __device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmtFp6, kFmtFp6, 0, kUnitScale, 0, kUnitScale);
 }
 
 // ROWA: one activation scale per row (group_a == K, the per-token end of the
@@ -119,8 +133,10 @@ __device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c) {
 template <bool PARTIALS, int MODE, bool ROWA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_w4a4_gemm(Params p) {
-  __shared__ __align__(16) uint8_t sA[2][BM * PITCH];
-  __shared__ __align__(16) uint8_t sW[2][BN * PITCH];
+  __shared__ __align__(16) uint8_t sA[2][BM * PM];   // FP6 operand main parts
+  __shared__ __align__(16) uint8_t sW[2][BN * PM];
+  __shared__ __align__(16) uint8_t tA[2][BM * PT];   // FP6 operand tails
+  __shared__ __align__(16) uint8_t tW[2][BN * PT];
   __shared__ __align__(16) float sSA[2][2][BM];   // [stage][64-k half][row]
   __shared__ __align__(16) float sSW[2][2][BN];
 
@@ -148,8 +164,10 @@ void k_w4a4_gemm(Params p) {
   const uint8_t* gA1 = p.a + (int64_t)min(tile_m + 64 + (tid >> 2), p.M - 1) * row_bytes + (tid & 3) * 16;
   const uint8_t* gW0 = p.w + (int64_t)min(tile_n + (tid >> 2), p.N - 1) * row_bytes + (tid & 3) * 16;
   const uint8_t* gW1 = p.w + (int64_t)min(tile_n + 64 + (tid >> 2), p.N - 1) * row_bytes + (tid & 3) * 16;
-  const int st0 = (tid >> 2) * PITCH + (tid & 3) * 32;
-  const int st1 = st0 + 64 * PITCH;
+  const int st0 = (tid >> 2) * PM + (tid & 3) * 16;   // chunk tid & 3 of row tid >> 2
+  const int st1 = st0 + 64 * PM;
+  const int tt0 = (tid >> 2) * PT + (tid & 3) * 8;
+  const int tt1 = tt0 + 64 * PT;
   // scales: threads 0..127 stage A-row scales, 128..255 W-row scales
   const bool s_is_a = tid < BM;
   const int srow = s_is_a ? tid : tid - BM;
@@ -181,10 +199,10 @@ void k_w4a4_gemm(Params p) {
   }
 #define LSTORE(BUF, R)                                                \
   {                                                                   \
-    unpack_store(&sA[BUF][st0], R.a0);                                \
-    unpack_store(&sA[BUF][st1], R.a1);                                \
-    unpack_store(&sW[BUF][st0], R.w0);                                \
-    unpack_store(&sW[BUF][st1], R.w1);                                \
+    unpack_store(&sA[BUF][st0], &tA[BUF][tt0], R.a0);                 \
+    unpack_store(&sA[BUF][st1], &tA[BUF][tt1], R.a1);                 \
+    unpack_store(&sW[BUF][st0], &tW[BUF][tt0], R.w0);                 \
+    unpack_store(&sW[BUF][st1], &tW[BUF][tt1], R.w1);                 \
     sS[(BUF) * 2 * BM] = R.s0;                                        \
     sS[(BUF) * 2 * BM + BM] = R.s1;                                   \
   }
@@ -203,8 +221,10 @@ void k_w4a4_gemm(Params p) {
 
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-  const int rdA = (wm * 64 + l32) * PITCH + 32 * lhi;   // + i*32*PITCH + 64*s
-  const int rdW = (wn * 64 + l32) * PITCH + 32 * lhi;
+  const int rdA = (wm * 64 + l32) * PM + 16 * lhi;   // + i*32*PM + 32*s (chunk 2s + lhi)
+  const int rdW = (wn * 64 + l32) * PM + 16 * lhi;
+  const int rtA = (wm * 64 + l32) * PT + 8 * lhi;    // + i*32*PT + 16*s
+  const int rtW = (wn * 64 + l32) * PT + 8 * lhi;
   int gcount = 0;     // GBIG: stages accumulated into P since the last epilogue
   int gidx = 0;       // index of the next group to finish (partials export)
 
@@ -250,11 +270,13 @@ void k_w4a4_gemm(Params p) {
     GLOAD(RL, min((KT) + kAhead, nk - 1));                                               \
     const uint8_t* bA = &sA[BUF][rdA];                                                   \
     const uint8_t* bW = &sW[BUF][rdW];                                                   \
+    const uint8_t* cA = &tA[BUF][rtA];                                                   \
+    const uint8_t* cW = &tW[BUF][rtW];                                                   \
     v8i a[2][2], b[2][2];   /* [tile row i / col j][k-step s] */                         \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                        \
     _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                      \
-      a[i][s] = load_op(bA + i * 32 * PITCH + 64 * s);                                   \
-      b[i][s] = load_op(bW + i * 32 * PITCH + 64 * s);                                   \
+      a[i][s] = load_op(bA + i * 32 * PM + 32 * s, cA + i * 32 * PT + 16 * s);           \
+      b[i][s] = load_op(bW + i * 32 * PM + 32 * s, cW + i * 32 * PT + 16 * s);           \
     }                                                                                    \
     if constexpr (MODE == G64) {                                                         \
       _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \

@@ -4,11 +4,12 @@
 // K; other group sizes for its mixed-granularity mode). Per group:
 //   a = max|x|, s = fl32(a / 7), q = clamp(rne(fl32(x / s)), -8, 7), s = 0 and
 //   q = 0 for an all-zero group. The rule only yields q in [-7, 7], stored
-//   sign-magnitude: each 32-bit word holds the codes c0..c7 of 8 consecutive k;
-//   byte b holds sign(c_b) in bit 7, |c_b| in bits 2..0, |c_(4+b)| in bits 6..4
-//   and sign(c_(4+(b+3)%4)) in bit 3, the sign bit being that of the input value.
-//   The GEMM turns a word into 8 FP8 E4M3 operand bytes with two masks and one
-//   rotate.
+//   sign-magnitude in 4 bits per code, the sign bit being that of the input
+//   value: each 8-byte unit holds the codes c0..c15 of 16 consecutive k as two
+//   32-bit words X, Y folded from the 96-bit stream S of the 6-bit fields
+//   f_k = sign << 5 | |c_k| at bits 6k (the FP6 E2M3 encoding of the subnormal
+//   +-|c_k|/8): X = S0 | (S1 & kFoldX), Y = S2 | (S1 & kFoldY). The GEMM
+//   rebuilds S0, S1, S2 -- its FP6 operand -- with two ANDs and an AND-OR.
 // MXFP4 (the open-standard MXFP4 of the FP4 RL abstract; OCP MX v1.0 block
 // rule): per 32 elements E = floor(log2 a) - 2, codes = E2M1(x / 2^E) with
 // ties to even and saturation at 6, E8M0 byte E + 127. The scale bytes are
@@ -16,9 +17,10 @@
 // row, min(8, blocks left) bytes per row), so the GEMM reads one stage's scales
 // of a tile as one contiguous run.
 //
-// Both kernels stream HBM: each lane loads 8 fp16 (one 128-bit load) per row
-// it covers, a group's absmax is reduced across the lanes that hold it with DPP
-// row permutes (no LDS), and each lane writes its 8 codes as one 32-bit store.
+// Both kernels stream HBM: each lane loads 16 (INT4) or 8 (MXFP4) fp16 values
+// per row it covers with 128-bit loads, a group's absmax is reduced across the
+// lanes that hold it with DPP row permutes (no LDS), and each lane writes its
+// codes with one store (64-bit INT4 word, 32-bit E2M1 word).
 // The grid is 2-D (chunk column x row block), so no lane divides to find its row.
 //
 // Vector-ALU economy for the INT4 rule (the stream must not become ALU-bound):
@@ -54,20 +56,24 @@ __device__ __forceinline__ uint32_t mag_code(float t) {
   return __float_as_uint(__builtin_amdgcn_fmed3f(t, 0.0f, 7.0f) + kMagic);
 }
 
-// 8 magnitudes (low bits of m[]) and the 8 fp16 inputs they came from -> one
-// sign-magnitude word (layout in the file header).
-__device__ __forceinline__ uint32_t pack8(const uint32_t m[8], uint4 raw) {
-  const uint32_t p0 = (m[4] << 4) | m[0];     // byte 0 = |c0| | |c4| << 4
-  const uint32_t p1 = (m[5] << 4) | m[1];
-  const uint32_t p2 = (m[6] << 4) | m[2];
-  const uint32_t p3 = (m[7] << 4) | m[3];
-  const uint32_t lo = __builtin_amdgcn_perm(p1, p0, 0x0C0C0400u);    // [p0.b0, p1.b0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(p3, p2, 0x04000C0Cu);    // [0, 0, p2.b0, p3.b0]
-  // high byte of each fp16 input: bit 7 = its sign
-  const uint32_t s_lo = __builtin_amdgcn_perm(raw.y, raw.x, 0x07050301u);   // x0..x3
-  const uint32_t s_hi = __builtin_amdgcn_perm(raw.w, raw.z, 0x07050301u);   // x4..x7
-  const uint32_t s_hi_rot = __builtin_amdgcn_alignbit(s_hi, s_hi, 28);      // rotl 4: byte b bit 7 -> byte b+1 bit 3
-  return (lo | hi) | (s_lo & 0x80808080u) | (s_hi_rot & 0x08080808u);
+// Bits of a word at positions 3, 4 (mod 6), where the stream's first word is
+// zero, and at 0, 5 (mod 6), where its third word is zero; together they cover
+// every bit the second word can have set.
+constexpr uint32_t kFoldX = 0x18618618u;
+constexpr uint32_t kFoldY = 0x61861861u;
+
+// 16 magnitudes (low 3 bits of m[]) and the 16 fp16 inputs they came from
+// (r0: inputs 0..7, r1: 8..15) -> the 8-byte INT4 unit (layout in the header).
+__device__ __forceinline__ uint2 pack16(const uint32_t m[16], uint4 r0, uint4 r1) {
+  const uint32_t h[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  uint32_t f[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)    // FP6 field: sign of input k (fp16 bit 15) << 5 | |c_k|
+    f[k] = (m[k] & 7u) | (((h[k >> 1] >> (16 * (k & 1) + 15)) & 1u) << 5);
+  const uint32_t s0 = f[0] | f[1] << 6 | f[2] << 12 | f[3] << 18 | f[4] << 24 | f[5] << 30;
+  const uint32_t s1 = f[5] >> 2 | f[6] << 4 | f[7] << 10 | f[8] << 16 | f[9] << 22 | f[10] << 28;
+  const uint32_t s2 = f[10] >> 4 | f[11] << 2 | f[12] << 8 | f[13] << 14 | f[14] << 20 | f[15] << 26;
+  return uint2{s0 | (s1 & kFoldX), s2 | (s1 & kFoldY)};
 }
 
 // Group scale and its reciprocal (r = 0 for an all-zero group so every code is 0).
@@ -77,18 +83,18 @@ __device__ __forceinline__ void group_scale(float a, float& s, float& r) {
   r = (s == 0.0f) ? 0.0f : 1.0f / s;     // correctly rounded division
 }
 
-__device__ __forceinline__ uint32_t int4_codes8(const float f[8], uint4 raw, float s, float r) {
-  uint32_t m[8];
+__device__ __forceinline__ uint2 int4_codes16(const float f[16], uint4 r0, uint4 r1, float s, float r) {
+  uint32_t m[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m[i] = mag_code(div_rn(fabsf(f[i]), s, r));
-  return pack8(m, raw);
+  for (int i = 0; i < 16; ++i) m[i] = mag_code(div_rn(fabsf(f[i]), s, r));
+  return pack16(m, r0, r1);
 }
 
 // Lane mapping of the 2-D grid: a block is kQuantThreads lanes = (256 / W) row
 // slots x W chunk columns, W in {64, 128, 256}; each lane covers kRowsPerThread
 // rows spaced (256 / W) apart.
 struct Map {
-  int col;       // 8-element chunk index within the row
+  int col;       // chunk index within the row (16 elements INT4, 8 MXFP4)
   int row0;      // first row
   int rstep;     // row spacing between a lane's rows
 };
@@ -102,32 +108,39 @@ __device__ __forceinline__ Map lane_map(int wshift) {
   return m;
 }
 
-// One group of G elements spans G/8 consecutive lanes of one row.
+// One group of G elements spans G/16 consecutive lanes of one row; a lane
+// covers 16 elements (chunk col) of each of its rows.
 template <int G>
 __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int cpr, int wshift,
-    uint32_t* __restrict__ q, float* __restrict__ s) {
-  constexpr int LPG = G / 8;
+    uint2* __restrict__ q, float* __restrict__ s) {
+  constexpr int LPG = G / 16;
   const Map mp = lane_map(wshift);
   if (mp.col >= cpr) return;                  // whole lane groups drop out together
-  uint4 raw[kRowsPerThread];
+  uint4 raw[kRowsPerThread][2];
 #pragma unroll
   for (int u = 0; u < kRowsPerThread; ++u) {
     const int row = mp.row0 + u * mp.rstep;
-    if (row < M) raw[u] = *reinterpret_cast<const uint4*>(x + row * ldx + mp.col * 8);
+    if (row < M) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + mp.col * 16);
+      raw[u][0] = src[0];
+      raw[u][1] = src[1];
+    }
   }
 #pragma unroll
   for (int u = 0; u < kRowsPerThread; ++u) {
     const int row = mp.row0 + u * mp.rstep;
     if (row < M) {                            // uniform across each lane group
-      float f[8];
-      halves_to_float8(raw[u], f);
-      float a = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
-      a = fmaxf(a, fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));
+      float f[16];
+      halves_to_float8(raw[u][0], f);
+      halves_to_float8(raw[u][1], f + 8);
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
       a = group_max<LPG>(a);
       float sc, rc;
       group_scale(a, sc, rc);
-      q[(int64_t)row * cpr + mp.col] = int4_codes8(f, raw[u], sc, rc);
+      q[(int64_t)row * cpr + mp.col] = int4_codes16(f, raw[u][0], raw[u][1], sc, rc);
       if ((threadIdx.x & (LPG - 1)) == 0) s[(int64_t)(mp.col / LPG) * M + row] = sc;   // group-major
     }
   }
@@ -137,16 +150,18 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
 // absmax reduced across the block, then the row is read again from cache.
 __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
     const uint16_t* __restrict__ x, int64_t ldx, int cpr,
-    uint32_t* __restrict__ q, float* __restrict__ s) {
+    uint2* __restrict__ q, float* __restrict__ s) {
   __shared__ float wave_max[kQuantThreads / 64];
   const int row = blockIdx.x;
   const uint16_t* xr = x + row * ldx;
   float a = 0.0f;
   for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
-    float f[8];
-    halves_to_float8(*reinterpret_cast<const uint4*>(xr + c * 8), f);
+    const uint4* src = reinterpret_cast<const uint4*>(xr + c * 16);
+    float f[16];
+    halves_to_float8(src[0], f);
+    halves_to_float8(src[1], f + 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
   }
   a = group_max<64>(a);
   if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
@@ -156,10 +171,12 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
   float sc, rc;
   group_scale(a, sc, rc);
   for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(xr + c * 8);
-    float f[8];
-    halves_to_float8(raw, f);
-    q[(int64_t)row * cpr + c] = int4_codes8(f, raw, sc, rc);
+    const uint4* src = reinterpret_cast<const uint4*>(xr + c * 16);
+    const uint4 r0 = src[0], r1 = src[1];
+    float f[16];
+    halves_to_float8(r0, f);
+    halves_to_float8(r1, f + 8);
+    q[(int64_t)row * cpr + c] = int4_codes16(f, r0, r1, sc, rc);
   }
   if (threadIdx.x == 0) s[row] = sc;
 }
@@ -231,8 +248,8 @@ dim3 grid_for(int rows, int cpr, int wshift) {
 void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int group,
                        uint8_t* q, float* s, hipStream_t stream) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  uint32_t* qp = reinterpret_cast<uint32_t*>(q);
-  const int cpr = (int)(K / 8);
+  uint2* qp = reinterpret_cast<uint2*>(q);
+  const int cpr = (int)(K / 16);      // 16-element chunks per row
   const int ws = width_shift(cpr);
   const dim3 grid = grid_for((int)M, cpr, ws);
   const int m = (int)M;

@@ -273,28 +273,33 @@ void k_w4a4_gemm(Params p) {
     const uint8_t* cA = &tA[BUF][rtA];                                                   \
     const uint8_t* cW = &tW[BUF][rtW];                                                   \
     v8i a[2][2], b[2][2];   /* [tile row i / col j][k-step s] */                         \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                        \
-    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                      \
-      a[i][s] = load_op(bA + i * 32 * PM + 32 * s, cA + i * 32 * PT + 16 * s);           \
-      b[i][s] = load_op(bW + i * 32 * PM + 32 * s, cW + i * 32 * PT + 16 * s);           \
+    /* operands of k-step S; g = 64 reads each step's just before its MFMAs */          \
+    auto load_step = [&](int S) {                                                        \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                    \
+        a[i][S] = load_op(bA + i * 32 * PM + 32 * S, cA + i * 32 * PT + 16 * S);         \
+        b[i][S] = load_op(bW + i * 32 * PM + 32 * S, cW + i * 32 * PT + 16 * S);         \
+      }                                                                                  \
+    };                                                                                   \
+    if constexpr (MODE != G64) {                                                         \
+      load_step(0);                                                                      \
+      load_step(1);                                                                      \
     }                                                                                    \
     if constexpr (MODE == G64) {                                                         \
       _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
+        /* one tile at a time (its MFMA, then its epilogue): with a group per    */   \
+        /* k-step, keeping two tiles' partials in flight does not fit the VGPRs   */   \
+        load_step(s);                                                                    \
         const GroupScales T0 = TPROD(BUF, s, 0);                                         \
         P[0][0] = mma(a[0][s], b[0][s], zero16);                                         \
-        P[1][0] = mma(a[1][s], b[0][s], zero16);                                         \
-        __builtin_amdgcn_sched_barrier(0);                                               \
         EPI(0, 0, T0);                                                                   \
-        P[1][1] = mma(a[1][s], b[1][s], zero16);                                         \
-        __builtin_amdgcn_sched_barrier(0);                                               \
+        P[1][0] = mma(a[1][s], b[0][s], zero16);                                         \
         EPI(1, 0, T0);                                                                   \
         __builtin_amdgcn_sched_barrier(0);                                               \
         const GroupScales T1 = TPROD(BUF, s, 1);                                         \
-        P[0][1] = mma(a[0][s], b[1][s], zero16);                                         \
-        __builtin_amdgcn_sched_barrier(0);                                               \
+        P[1][1] = mma(a[1][s], b[1][s], zero16);                                         \
         EPI(1, 1, T1);                                                                   \
         if (s == 1) LSTORE((BUF) ^ 1, RS);                                               \
-        __builtin_amdgcn_sched_barrier(0);                                               \
+        P[0][1] = mma(a[0][s], b[1][s], zero16);                                         \
         EPI(0, 1, T1);                                                                   \
         __builtin_amdgcn_sched_barrier(0);                                               \
         ++gidx;                                                                          \

@@ -102,11 +102,14 @@ __device__ __forceinline__ void unpack_store(uint8_t* dm, uint8_t* dt, uint4 v) 
   *reinterpret_cast<uint2*>(dt) = uint2{s4, v.w & ~kFoldY};
 }
 
-// The 6 FP6 words of one lane's operand (row l%32, k-chunk l/32) from LDS.
+// The 6 FP6 words of one lane's operand (row l%32, k-chunk l/32) from LDS. In
+// FP6 mode the instruction reads registers 0..5 of the operand, so 6 and 7 are
+// left undefined (no register moves to clear them).
 __device__ __forceinline__ v8i load_op(const uint8_t* pm, const uint8_t* pt) {
-  const uint4 x = *reinterpret_cast<const uint4*>(pm);
-  const uint2 y = *reinterpret_cast<const uint2*>(pt);
-  return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, 0, 0};
+  const v4i x = *reinterpret_cast<const v4i*>(pm);
+  const v2i y = *reinterpret_cast<const v2i*>(pt);
+  const v4i y4 = __builtin_shufflevector(y, y, 0, 1, -1, -1);
+  return __builtin_shufflevector(x, y4, 0, 1, 2, 3, 4, 5, -1, -1);
 }
 
 // Workgroup barrier that orders LDS only: __syncthreads() would also wait for
@@ -274,10 +277,14 @@ void k_w4a4_gemm(Params p) {
     const uint8_t* cW = &tW[BUF][rtW];                                                   \
     v8i a[2][2], b[2][2];   /* [tile row i / col j][k-step s] */                         \
     /* operands of k-step S; g = 64 reads each step's just before its MFMAs */          \
+    /* (the barriers keep the compiler from merging two operands' 8-byte     */      \
+    /* tails into one read, which would need register moves to split them)  */      \
     auto load_step = [&](int S) {                                                        \
       _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                    \
         a[i][S] = load_op(bA + i * 32 * PM + 32 * S, cA + i * 32 * PT + 16 * S);         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
         b[i][S] = load_op(bW + i * 32 * PM + 32 * S, cW + i * 32 * PT + 16 * S);         \
+        __builtin_amdgcn_sched_barrier(0);                                               \
       }                                                                                  \
     };                                                                                   \
     if constexpr (MODE != G64) {                                                         \

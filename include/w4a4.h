@@ -114,7 +114,8 @@ w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t grou
  *                   or K itself (per token); the larger must be a multiple of
  *                   the smaller, and g <= 262144 (P_b stays an exact integer in
  *                   the fp32 matrix-core accumulator: 49 g < 2^24)
- *   M, N, K         M, N >= 0; K > 0 and K % 128 == 0
+ *   M, N, K         M, N >= 0; K > 0, K % 128 == 0 and K <= 2^24 (the kernel
+ *                   addresses a 128-row tile with 32-bit offsets)
  *   y               out: [M][ldy] fp32 or fp16 (y_dtype), ldy >= N,
  *                   aligned to its element size
  *   xq, wq 16-byte aligned; xs, ws 4-byte aligned.

@@ -93,6 +93,7 @@ def test_gemm_validation(lib):
     # the finer group bounds the fp32 partials: 49 g must stay below 2^24
     big = 1 << 19
     assert g(P, P, big, P, P, big, M, N, big, P, 0, N, None) == E_GROUP       # per token, g = 2^19
+    assert g(P, P, 128, P, P, 128, M, N, (1 << 24) + 128, P, 0, N, None) == E_SHAPE   # 32-bit tile offsets
     assert g(P, P, 128, P, P, 128, 0, N, K, None, 0, N, None) == OK           # empty
     assert g(P, P, 128, P, P, 128, M, 0, K, None, 0, 0, None) == OK
     assert g(None, P, 128, P, P, 128, M, N, K, P, 0, N, None) == E_NULL

@@ -91,7 +91,9 @@ w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t grou
 static w4a4_status_t gemm_common(const uint8_t* xq, const float* xs, int32_t ga,
                                  const uint8_t* wq, const float* ws, int32_t gw,
                                  int64_t M, int64_t N, int64_t K, GemmArgs& g) {
-  if (M < 0 || N < 0 || K <= 0 || K % 128) return W4A4_E_SHAPE;
+  // K <= 2^24: a 128-row tile then spans < 2^31 bytes, the kernel's 32-bit
+  // buffer offsets
+  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > (int64_t{1} << 24)) return W4A4_E_SHAPE;
   if (!gemm_groups_ok(K, ga, gw)) return W4A4_E_GROUP;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!xq || !xs || !wq || !ws) return W4A4_E_NULL;

@@ -125,6 +125,8 @@ struct GroupScales {
   float sw0, sw1;  // the lane's W scales of column blocks 0 and 1 (per-row A scales)
 };
 
+__device__ __forceinline__ uint4 as_uint4(v4u v) { return uint4{v.x, v.y, v.z, v.w}; }
+
 __device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmtFp6, kFmtFp6, 0, kUnitScale, 0, kUnitScale);
 }
@@ -162,21 +164,29 @@ void k_w4a4_gemm(Params p) {
   const int row_bytes = p.K >> 1;
   const int nk = p.K / BK;
 
-  // ---- staging: each thread fetches 2 x 16 B of A and of W per stage
-  const uint8_t* gA0 = p.a + (int64_t)min(tile_m + (tid >> 2), p.M - 1) * row_bytes + (tid & 3) * 16;
-  const uint8_t* gA1 = p.a + (int64_t)min(tile_m + 64 + (tid >> 2), p.M - 1) * row_bytes + (tid & 3) * 16;
-  const uint8_t* gW0 = p.w + (int64_t)min(tile_n + (tid >> 2), p.N - 1) * row_bytes + (tid & 3) * 16;
-  const uint8_t* gW1 = p.w + (int64_t)min(tile_n + 64 + (tid >> 2), p.N - 1) * row_bytes + (tid & 3) * 16;
+  // ---- staging: each thread fetches 2 x 16 B of A and of W per stage through
+  // buffer resources over the tile's rows (the host keeps a tile's rows
+  // < 2^31 bytes), the stage's k offset in the scalar offset
+  const int a_rows = min(BM, p.M - tile_m), w_rows = min(BN, p.N - tile_n);
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
+  const int vA0 = min(tid >> 2, a_rows - 1) * row_bytes + (tid & 3) * 16;
+  const int vA1 = min(64 + (tid >> 2), a_rows - 1) * row_bytes + (tid & 3) * 16;
+  const int vW0 = min(tid >> 2, w_rows - 1) * row_bytes + (tid & 3) * 16;
+  const int vW1 = min(64 + (tid >> 2), w_rows - 1) * row_bytes + (tid & 3) * 16;
   const int st0 = (tid >> 2) * PM + (tid & 3) * 16;   // chunk tid & 3 of row tid >> 2
   const int st1 = st0 + 64 * PM;
   const int tt0 = (tid >> 2) * PT + (tid & 3) * 8;
   const int tt1 = tt0 + 64 * PT;
-  // scales: threads 0..127 stage A-row scales, 128..255 W-row scales
-  const bool s_is_a = tid < BM;
+  // scales: waves 0, 1 (threads 0..127) stage A-row scales, waves 2, 3 W-row
+  // scales; group-major, so consecutive threads read consecutive rows of one
+  // group. The choice is uniform per wave, so each wave's resource is scalar.
+  const bool s_is_a = __builtin_amdgcn_readfirstlane(tid) < BM;
   const int srow = s_is_a ? tid : tid - BM;
-  // group-major scales: consecutive threads read consecutive rows of one group
-  const float* gS = s_is_a ? p.sa + min(tile_m + srow, p.M - 1) : p.sw + min(tile_n + srow, p.N - 1);
-  const int64_t sgs = s_is_a ? p.M : p.N;   // floats between groups
+  const float* sbase = s_is_a ? p.sa + tile_m : p.sw + tile_n;   // this tile's rows of group 0
+  const int64_t sgs = s_is_a ? p.M : p.N;                      // floats between groups
+  const int snr = s_is_a ? a_rows : w_rows;
+  const int vS = 4 * min(srow, snr - 1);
   const int ssh = s_is_a ? p.sha : p.shw;
   float* sS = s_is_a ? &sSA[0][0][srow] : &sSW[0][0][srow];
 
@@ -185,6 +195,11 @@ void k_w4a4_gemm(Params p) {
   // unpacked into LDS, so every load has two stages to land. The g = 64 mode
   // and the partials export keep one set (one stage ahead) to stay in registers.
   constexpr int kAhead = (MODE == G64 || PARTIALS) ? 1 : 2;
+  // scale of group column c for the thread's row: a per-stage scalar resource
+  auto load_scale = [&](int c) -> float {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sbase + c * sgs, 4 * snr);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, vS, 0, 0));
+  };
   struct Staged {
     uint4 a0, a1, w0, w1;
     float s0, s1;
@@ -192,13 +207,13 @@ void k_w4a4_gemm(Params p) {
 #define GLOAD(R, KT)                                                  \
   {                                                                   \
     const int off_ = (KT) * ROW_BYTES;                                \
-    R.a0 = *reinterpret_cast<const uint4*>(gA0 + off_);               \
-    R.a1 = *reinterpret_cast<const uint4*>(gA1 + off_);               \
-    R.w0 = *reinterpret_cast<const uint4*>(gW0 + off_);               \
-    R.w1 = *reinterpret_cast<const uint4*>(gW1 + off_);               \
-    R.s0 = gS[(int64_t)((2 * (KT)) >> ssh) * sgs];                    \
+    R.a0 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rA, vA0, off_, 0)); \
+    R.a1 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rA, vA1, off_, 0)); \
+    R.w0 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, vW0, off_, 0)); \
+    R.w1 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, vW1, off_, 0)); \
+    R.s0 = load_scale((2 * (KT)) >> ssh);                             \
     /* groups >= 128: both 64-k halves share a group */               \
-    R.s1 = (MODE == G64) ? gS[(int64_t)((2 * (KT) + 1) >> ssh) * sgs] : R.s0; \
+    R.s1 = (MODE == G64) ? load_scale((2 * (KT) + 1) >> ssh) : R.s0;  \
   }
 #define LSTORE(BUF, R)                                                \
   {                                                                   \

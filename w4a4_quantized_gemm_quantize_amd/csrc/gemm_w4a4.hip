@@ -25,7 +25,7 @@
 //   * Epilogue per output per group: acc = fma(P, t, acc).
 //
 // Workgroup: 256 threads = 4 waves in a 2 x 2 grid; tile 128 x 128 outputs,
-// K stage 128 (two MFMA k-steps), double-buffered LDS (61 KB), two workgroups
+// K stage 128 (two MFMA k-steps), double-buffered LDS (50 KB), two workgroups
 // per CU (two waves per SIMD). The staging threads fetch stage kt+2 while
 // stage kt is computed and stage kt+1 is unpacked (two register sets), and the
 // stage barrier orders LDS only, so no wait drains those loads. Within a stage
@@ -56,10 +56,15 @@ constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int ROW_BYTES = BK / 2;   // packed bytes per row per stage
 // LDS row of one 128-k stage: four 32-code FP6 operand chunks of 24 bytes,
 // each split into a 16-byte main part and an 8-byte tail, kept in two arrays
-// so every read is naturally aligned. Pitches 80 and 40 bytes put the 16 rows
-// read together by 16 lanes in distinct bank groups.
-constexpr int PM = 80;              // main part: 4 x 16 B + 16 pad
-constexpr int PT = 40;              // tail part: 4 x 8 B + 8 pad
+// so every read is naturally aligned. The LDS serves 16 lanes of 16-byte (32
+// lanes of 8-byte) accesses per clock over 64 banks: readers take one chunk
+// of 16 (32) consecutive rows, writers 4 chunks of 4 (8) rows. Unpadded rows
+// with the chunk index XOR-swizzled by (row >> 2) & 3 (main) and (row >> 3) & 3
+// (tail) put both patterns in distinct banks.
+constexpr int PM = 64;              // main part: 4 x 16 B
+constexpr int PT = 32;              // tail part: 4 x 8 B
+__device__ __forceinline__ int main_off(int row, int chunk) { return row * PM + 16 * (chunk ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int tail_off(int row, int chunk) { return row * PT + 8 * (chunk ^ ((row >> 3) & 3)); }
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;       // tile-rows per raster group
 constexpr int kUnitScale = 127 + 3; // E8M0 2^3: FP6 E2M3 [s 00 m] = +-m/8, times 2^3 = +-m
@@ -174,9 +179,9 @@ void k_w4a4_gemm(Params p) {
   const int vA1 = min(64 + (tid >> 2), a_rows - 1) * row_bytes + (tid & 3) * 16;
   const int vW0 = min(tid >> 2, w_rows - 1) * row_bytes + (tid & 3) * 16;
   const int vW1 = min(64 + (tid >> 2), w_rows - 1) * row_bytes + (tid & 3) * 16;
-  const int st0 = (tid >> 2) * PM + (tid & 3) * 16;   // chunk tid & 3 of row tid >> 2
-  const int st1 = st0 + 64 * PM;
-  const int tt0 = (tid >> 2) * PT + (tid & 3) * 8;
+  const int st0 = main_off(tid >> 2, tid & 3);      // chunk tid & 3 of row tid >> 2
+  const int st1 = st0 + 64 * PM;                     // row + 64: same swizzle
+  const int tt0 = tail_off(tid >> 2, tid & 3);
   const int tt1 = tt0 + 64 * PT;
   // scales: waves 0, 1 (threads 0..127) stage A-row scales, waves 2, 3 W-row
   // scales; group-major, so consecutive threads read consecutive rows of one
@@ -239,10 +244,16 @@ void k_w4a4_gemm(Params p) {
 
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-  const int rdA = (wm * 64 + l32) * PM + 16 * lhi;   // + i*32*PM + 32*s (chunk 2s + lhi)
-  const int rdW = (wn * 64 + l32) * PM + 16 * lhi;
-  const int rtA = (wm * 64 + l32) * PT + 8 * lhi;    // + i*32*PT + 16*s
-  const int rtW = (wn * 64 + l32) * PT + 8 * lhi;
+  // lane operand: row (wm|wn)*64 + 32i + l32, chunk 2s + lhi; row + 32i has the
+  // same swizzle as row, so one offset per k-step s serves both row blocks
+  int rdA[2], rdW[2], rtA[2], rtW[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    rdA[s] = main_off(wm * 64 + l32, 2 * s + lhi);
+    rdW[s] = main_off(wn * 64 + l32, 2 * s + lhi);
+    rtA[s] = tail_off(wm * 64 + l32, 2 * s + lhi);
+    rtW[s] = tail_off(wn * 64 + l32, 2 * s + lhi);
+  }
   int gcount = 0;     // GBIG: stages accumulated into P since the last epilogue
   int gidx = 0;       // index of the next group to finish (partials export)
 
@@ -286,19 +297,19 @@ void k_w4a4_gemm(Params p) {
 #define STAGE(KT, BUF, RL, RS)                                                           \
   {                                                                                      \
     GLOAD(RL, min((KT) + kAhead, nk - 1));                                               \
-    const uint8_t* bA = &sA[BUF][rdA];                                                   \
-    const uint8_t* bW = &sW[BUF][rdW];                                                   \
-    const uint8_t* cA = &tA[BUF][rtA];                                                   \
-    const uint8_t* cW = &tW[BUF][rtW];                                                   \
+    const uint8_t* bA = sA[BUF];                                                         \
+    const uint8_t* bW = sW[BUF];                                                         \
+    const uint8_t* cA = tA[BUF];                                                         \
+    const uint8_t* cW = tW[BUF];                                                         \
     v8i a[2][2], b[2][2];   /* [tile row i / col j][k-step s] */                         \
     /* operands of k-step S; g = 64 reads each step's just before its MFMAs */          \
     /* (the barriers keep the compiler from merging two operands' 8-byte     */      \
     /* tails into one read, which would need register moves to split them)  */      \
     auto load_step = [&](int S) {                                                        \
       _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                    \
-        a[i][S] = load_op(bA + i * 32 * PM + 32 * S, cA + i * 32 * PT + 16 * S);         \
+        a[i][S] = load_op(bA + rdA[S] + i * 32 * PM, cA + rtA[S] + i * 32 * PT);         \
         __builtin_amdgcn_sched_barrier(0);                                               \
-        b[i][S] = load_op(bW + i * 32 * PM + 32 * S, cW + i * 32 * PT + 16 * S);         \
+        b[i][S] = load_op(bW + rdW[S] + i * 32 * PM, cW + rtW[S] + i * 32 * PT);         \
         __builtin_amdgcn_sched_barrier(0);                                               \
       }                                                                                  \
     };                                                                                   \

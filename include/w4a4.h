@@ -146,12 +146,15 @@ w4a4_status_t w4a4_gemm_debug_partials(const uint8_t* xq, const float* xs, int32
  *
  *   x     fp16 [rows][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0; K % 32 == 0
  *   q     out: u8 [rows][K/2] packed E2M1 codes, 4-byte aligned
- *   e8m0  out: u8, rows * K/32 scale bytes in 256-k panels: with nb = K/32 and
- *         w_p = min(8, nb - 8p), the scale of row r and block b (p = b / 8) is
- *         at byte 8 * rows * p + w_p * r + b % 8. Panel p thus holds, row after
- *         row, the w_p scale bytes of blocks 8p .. 8p + w_p - 1, and a GEMM
- *         stage of 256 k reads one contiguous run per tile instead of one
- *         small piece per row. (K % 256 == 0: every panel is rows x 8 bytes.)
+ *   e8m0  out: u8, rows * K/32 scale bytes in 256-k panels: with nb = K/32,
+ *         w_p = min(8, nb - 8p) and j = b % 8, the scale of row r and block b
+ *         (p = b / 8) is at byte 8 * rows * p + w_p * r + pos, pos = j / 2 for
+ *         even j and ceil(w_p / 2) + j / 2 for odd j. Panel p thus holds, row
+ *         after row, the w_p scale bytes of blocks 8p .. 8p + w_p - 1, even
+ *         blocks first: a GEMM stage of 256 k reads one contiguous run per tile
+ *         instead of one small piece per row, and the 4 blocks one matrix-core
+ *         lane feeds sit in one dword. (K % 256 == 0: every panel is rows x 8
+ *         bytes, even blocks in bytes 0..3, odd ones in 4..7.)
  * Used for activations online and for weights offline.
  */
 w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,

@@ -1,6 +1,7 @@
 """Host-side layout helpers of the binding (CPU only): the 256-k panel layout
 of MXFP4 scale bytes, checked against a loop written from the C header's
-definition (panel p = blocks 8p.., rows of min(8, blocks left) bytes)."""
+definition (panel p = blocks 8p.., rows of min(8, blocks left) bytes, the even
+blocks' bytes before the odd ones')."""
 import numpy as np
 import pytest
 
@@ -13,8 +14,9 @@ def panels_by_definition(e_rows):
     pos = 0
     for p in range(0, nb, 8):
         w = min(8, nb - p)
+        order = list(range(0, w, 2)) + list(range(1, w, 2))    # even blocks first
         for r in range(rows):
-            for j in range(w):
+            for j in order:
                 out[pos] = e_rows[r, p + j]
                 pos += 1
     assert pos == rows * nb

@@ -100,7 +100,7 @@ void k_mxfp4_gemm(Params p) {
   constexpr int RPK = 1024 / RB;                    // rows per 1 KB load
   constexpr int SWS = SL == 4 ? 2 : 1;              // log2(16 / SL)
   constexpr int NSTEP = KB / 64;                    // MFMA k-steps per stage
-  constexpr int NEW = KB / 128;                     // E8M0 dwords per row per stage
+  constexpr int NEW = 2;                            // E8M0 dwords per row per stage (a panel row)
   constexpr int TI = BM / WM / 32, TJ = BN / WN / 32;   // 32x32 blocks per wave
   constexpr int NA = BM / RPK / NWAVE, NW = BN / RPK / NWAVE;   // 1 KB loads per wave per stage
   constexpr int NE = (NEW * (BM + BN) + 64 * NWAVE - 1) / (64 * NWAVE); // scale-dword loads per wave
@@ -175,8 +175,9 @@ void k_mxfp4_gemm(Params p) {
   }
   // a K that is 128 mod 256 ends in a 4-block panel (4 scale bytes per row)
   const bool half_tail = (p.K & 255) != 0;
-  // Scale chunk j of stage kt: panel kt (KB = 256) or half kt % 2 of panel
-  // kt / 2 (KB = 128), whose row pitch is 4 in a last 4-block panel. Chunks
+  // Scale chunk j of stage kt: the rows of panel kt (KB = 256) or of panel
+  // kt / 2 (KB = 128, both halves of a panel read its whole rows); a last
+  // 4-block panel has 4-byte rows, read into both dwords of a row slot. Chunks
   // beyond the stage's (none in the shipped tile shapes) re-read chunk 0's
   // dwords into their own unused LDS words, so every wave issues the same
   // number of loads per stage (the vmcnt waits count on it).
@@ -194,7 +195,7 @@ void k_mxfp4_gemm(Params p) {
       if (half_tail && kt == nk - 1)
         dma4(buffer_rsrc(panel + 4 * t0, 4 * nrow), voffE4[j], 0, lds);
       else
-        dma4(buffer_rsrc(panel + 8 * t0, 8 * nrow), voffE[j], 4 * (kt & 1), lds);
+        dma4(buffer_rsrc(panel + 8 * t0, 8 * nrow), voffE[j], 0, lds);
     }
   };
 #define ISSUE(KT, SM)                                                                \
@@ -229,23 +230,25 @@ void k_mxfp4_gemm(Params p) {
   // Operands of two 64-k steps (FP4: 16 bytes per lane): step u + 1 is read
   // from LDS while the MFMAs of step u run.
   uint4 av[2][TI], wv[2][TJ];
-  int ea[2][TI], ew[2][TJ];
+  // The lane's scale dword per operand row block, once per stage: within a
+  // panel row the even blocks' bytes come first, then the odd ones', so dword
+  // l/32 of the row holds the bytes of all 32-blocks this lane feeds and step
+  // U selects byte U with the instruction's byte select (shifted by 16 bits
+  // for the second half of a panel in 128-deep stages, and in a 4-byte last
+  // panel row for the odd lanes).
+  int ea[TI], ew[TJ];
 
 // Operands of one 64-k MFMA step U from ring slot SM: lane l feeds 32-block
-// 2U + l/32 of the stage in its row and that block's E8M0 byte (byte
-// 2 (U % 2) + l/32 of the row's scale dword U / 2). The swizzle term of row
-// + 32 i equals that of row, so one base per step serves every row block i.
+// 2U + l/32 of the stage in its row. The swizzle term of row + 32 i equals
+// that of row, so one base per step serves every row block i.
 #define LOAD_OPS(SM, U, B)                                                            \
   {                                                                                  \
     const uint8_t* st_ = (SM);                                                       \
-    const uint32_t* se_ = reinterpret_cast<const uint32_t*>(st_ + E_OFF) + (U) / 2;  \
     _Pragma("unroll") for (int i = 0; i < TI; ++i) {                                 \
       av[B][i] = *reinterpret_cast<const uint4*>(st_ + offA[U] + 32 * RB * i);      \
-      ea[B][i] = (int)((se_[NEW * (rowA + 32 * i)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
     _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                 \
       wv[B][j] = *reinterpret_cast<const uint4*>(st_ + W_OFF + offW[U] + 32 * RB * j); \
-      ew[B][j] = (int)((se_[NEW * (BM + rowW + 32 * j)] >> (8 * (2 * ((U) % 2) + lhi))) & 0xFFu); \
     }                                                                                \
   }
 // Matrix work of step U of stage KT. The partials variant runs one 32-block at
@@ -272,11 +275,30 @@ void k_mxfp4_gemm(Params p) {
         }                                                                            \
       }                                                                              \
     } else {                                                                         \
-      _Pragma("unroll") for (int i = 0; i < TI; ++i)                                 \
-      _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                 \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
-            as_operand(av[B][i]), as_operand(wv[B][j]), acc[i][j], kFmtFp4, kFmtFp4, 0, ea[B][i], 0, ew[B][j]); \
+      switch (U) {   /* the byte select is an immediate */                           \
+        case 0: MMA_SEL(B, 0) break;                                                 \
+        case 1: MMA_SEL(B, 1) break;                                                 \
+        case 2: MMA_SEL(B, 2) break;                                                 \
+        default: MMA_SEL(B, 3) break;                                                \
+      }                                                                              \
     }                                                                                \
+  }
+#define MMA_SEL(B, SEL)                                                              \
+  _Pragma("unroll") for (int i = 0; i < TI; ++i)                                     \
+  _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                     \
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                     \
+        as_operand(av[B][i]), as_operand(wv[B][j]), acc[i][j], kFmtFp4, kFmtFp4, SEL, ea[i], SEL, ew[j]);
+// The stage's scale dwords (see ea / ew).
+#define LOAD_SCALES(KT, SM)                                                          \
+  {                                                                                  \
+    const uint32_t* se_ = reinterpret_cast<const uint32_t*>((SM) + E_OFF);           \
+    const bool tail_ = KB == 128 && half_tail && (KT) == nk - 1;                     \
+    const int sh_ = KB == 256 ? 0 : tail_ ? 16 * lhi : 16 * ((KT) & 1);             \
+    const int w_ = tail_ ? 0 : lhi;                                                  \
+    _Pragma("unroll") for (int i = 0; i < TI; ++i)                                   \
+      ea[i] = (int)(se_[NEW * (rowA + 32 * i) + w_] >> sh_);                         \
+    _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                   \
+      ew[j] = (int)(se_[NEW * (BM + rowW + 32 * j) + w_] >> sh_);                    \
   }
 // Keeps the next step's LDS reads ahead of this step's MFMAs.
 #ifndef PIPE_FENCE_ON
@@ -308,6 +330,7 @@ void k_mxfp4_gemm(Params p) {
     if (D == 2 && (KT) + 1 < nk) wait_vmcnt<(D - 1) * PER_STAGE>();     \
     else wait_vmcnt<0>();                                               \
     STAGE_BARRIER();                                                    \
+    LOAD_SCALES(KT, CUR);                                               \
     LOAD_OPS(CUR, 0, 0);                                                \
     if ((KT) + D < nk) ISSUE((KT) + D, NXT);                            \
     _Pragma("unroll") for (int u_ = 0; u_ < NSTEP; ++u_) {              \
@@ -344,6 +367,8 @@ void k_mxfp4_gemm(Params p) {
 #undef STAGE_BARRIER
 #undef MMA_STEP
 #undef LOAD_OPS
+#undef LOAD_SCALES
+#undef MMA_SEL
 #undef ISSUE
 
   if constexpr (!PARTIALS) {

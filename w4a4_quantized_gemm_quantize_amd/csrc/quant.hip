@@ -14,8 +14,9 @@
 // rule): per 32 elements E = floor(log2 a) - 2, codes = E2M1(x / 2^E) with
 // ties to even and saturation at 6, E8M0 byte E + 127. The scale bytes are
 // written in 256-k panels (panel q = blocks 8q..8q+7 of every row, row after
-// row, min(8, blocks left) bytes per row), so the GEMM reads one stage's scales
-// of a tile as one contiguous run.
+// row, min(8, blocks left) bytes per row, the even blocks' bytes first), so the
+// GEMM reads one stage's scales of a tile as one contiguous run and a lane's
+// bytes as one dword.
 //
 // Both kernels stream HBM: each lane loads 16 (INT4) or 8 (MXFP4) fp16 values
 // per row it covers with 128-bit loads, a group's absmax is reduced across the
@@ -226,10 +227,11 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
       q[(int64_t)row * cpr + mp.col] = e2m1_codes8(v);
       if ((threadIdx.x & 3) == 0) {
         // panel layout: block b of the row goes to panel b / 8, whose rows hold
-        // min(8, blocks left) bytes each
+        // pw = min(8, blocks left) bytes each, the even blocks' bytes first
         const int b = mp.col >> 2, nb = cpr >> 2;
-        const int pq = b >> 3, pw = min(8, nb - 8 * pq);
-        e8m0[(int64_t)8 * rows * pq + (int64_t)row * pw + (b & 7)] = (uint8_t)(E + 127);
+        const int pq = b >> 3, pw = min(8, nb - 8 * pq), j = b & 7;
+        const int pos = (j & 1) ? ((pw + 1) >> 1) + (j >> 1) : (j >> 1);
+        e8m0[(int64_t)8 * rows * pq + (int64_t)row * pw + pos] = (uint8_t)(E + 127);
       }
     }
   }

@@ -102,14 +102,17 @@ def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int
 
 def mxfp4_scale_offsets(rows: int, K: int):
     """Byte offset of the scale of (row r, block b) in the 256-k panel layout
-    of the C header: ``8*rows*p + w_p*r + b%8`` with ``p = b // 8`` and
-    ``w_p = min(8, K/32 - 8p)``. Returns an int64 tensor [rows, K/32]."""
+    of the C header: ``8*rows*p + w_p*r + pos`` with ``p = b // 8``,
+    ``w_p = min(8, K/32 - 8p)``, ``j = b % 8`` and ``pos = j // 2`` for even
+    j, ``ceil(w_p / 2) + j // 2`` for odd j. Returns an int64 tensor [rows, K/32]."""
     nb = K // 32
     b = torch.arange(nb, dtype=torch.int64)
     p = b // 8
     w = torch.clamp(nb - 8 * p, max=8)
+    j = b % 8
+    pos = torch.where(j % 2 == 0, j // 2, (w + 1) // 2 + j // 2)
     r = torch.arange(rows, dtype=torch.int64)[:, None]
-    return 8 * rows * p[None, :] + w[None, :] * r + (b % 8)[None, :]
+    return 8 * rows * p[None, :] + w[None, :] * r + pos[None, :]
 
 
 def mxfp4_scales_to_rows(e, rows: int, K: int):

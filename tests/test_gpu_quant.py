@@ -55,8 +55,14 @@ def test_int4_zero_rows_and_groups():
     x[2] = 0
     x[5, 128:256] = 0
     x[6, :] = np.float16(-0.0)
-    int4_check(x, 128)
-    int4_check(x, 512)
+    x[7, 3] = np.float16(-0.0)                 # -0 inside groups whose absmax is not 0:
+    x[7, 130:140] = np.float16(-0.0)           # the code keeps the input's sign bit
+    x[1, 64:128] = np.float16(-0.0)            # a whole g = 64 group of -0 in a nonzero row
+    x[0, 5] = np.float16(-2.0 ** -24)          # tiny negatives that round to code -0
+    x[0, 6] = np.float16(2.0 ** -24)
+    for g in (64, 128, 512):
+        int4_check(x, g)
+    int4_check(x[:, :496], 496)                # per token, K % 32 == 16 (16-element tail)
 
 
 def test_int4_exhaustive_fp16():
@@ -92,6 +98,19 @@ def test_int4_workload_activations_sampled(name):
     codes, scales = oracle.int4_quantize(x[rows], 128)
     assert np.array_equal(host(q)[rows], oracle.pack_int4(codes, oracle.int4_sign_bits(x[rows])))
     assert np.array_equal(np.ascontiguousarray(host(s)[:, rows].T).view(np.uint32), scales.view(np.uint32))
+
+
+def test_int4_rows_beyond_one_grid_dimension():
+    """More row blocks than one grid dimension holds (65535): the kernel loops
+    over the rest. Bit-exact on sampled rows and the last rows."""
+    for g, K, M in ((128, 128, 65535 * 16 + 40), (512, 512, 65535 * 4 + 12)):
+        x = synth.bulk_normal(M, K, seed=8)
+        q, s = ops().w4a4_quantize_act(dev(x), g)
+        rows = np.concatenate([synth.sample_rows(M, 48, seed=2), np.arange(M - 80, M)])
+        codes, scales = oracle.int4_quantize(x[rows], g)
+        assert np.array_equal(host(q)[rows], oracle.pack_int4(codes, oracle.int4_sign_bits(x[rows]))), (g, M)
+        assert np.array_equal(np.ascontiguousarray(host(s)[:, rows].T).view(np.uint32), scales.view(np.uint32)), (g, M)
+        del x, q, s
 
 
 # ------------------------------------------------------------------ MXFP4

@@ -24,14 +24,14 @@ constexpr int DPP_QUAD_2301 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_MIRROR = 0x140;   // lane i <-> 15-i within a row of 16
 constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within each half row
 
-// Max over aligned groups of LANES consecutive lanes (LANES in {4,8,16,32,64}).
+// Max over aligned groups of LANES consecutive lanes (LANES in {2,4,8,16,32,64}).
 // Every lane of a group must be active; the result is in every lane.
 template <int LANES>
 __device__ __forceinline__ float group_max(float v) {
-  static_assert(LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64, "lanes");
+  static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64, "lanes");
   if constexpr (LANES >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
   v = fmaxf(v, dpp<DPP_QUAD_1032>(v));
-  v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
+  if constexpr (LANES >= 4) v = fmaxf(v, dpp<DPP_QUAD_2301>(v));
   if constexpr (LANES >= 16) v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
   if constexpr (LANES >= 32) v = fmaxf(v, __shfl_xor(v, 16));
   if constexpr (LANES >= 64) v = fmaxf(v, __shfl_xor(v, 32));

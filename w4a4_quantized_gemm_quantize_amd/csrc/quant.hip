@@ -18,22 +18,36 @@
 // GEMM reads one stage's scales of a tile as one contiguous run and a lane's
 // bytes as one dword.
 //
-// Both kernels stream HBM: each lane loads 16 (INT4) or 8 (MXFP4) fp16 values
-// per row it covers with 128-bit loads, a group's absmax is reduced across the
-// lanes that hold it with DPP row permutes (no LDS), and each lane writes its
-// codes with one store (64-bit INT4 word, 32-bit E2M1 word).
+// Both kernels stream HBM: each lane loads 32 (INT4) or 8 (MXFP4) consecutive
+// fp16 values per row it covers with 128-bit loads, a group's absmax is reduced
+// across the lanes that hold it with DPP row permutes (no LDS), and each lane
+// writes its codes with one store (two 8-byte INT4 units, one 32-bit E2M1 word).
 // The grid is 2-D (chunk column x row block), so no lane divides to find its row.
 //
-// Vector-ALU economy for the INT4 rule (the stream must not become ALU-bound):
+// Vector-ALU economy for the INT4 rule (the stream must not become ALU-bound;
+// about 4 vector instructions per element):
+//   * absmax: running max and min of the packed fp16 pairs with the three-input
+//     packed max / min, then max(max, -min) -- one instruction per two values.
 //   * x / s is computed as q0 = x*r, e = fma(-q0, s, x), q1 = fma(e, r, q0) with
 //     r = RN(1/s) computed once per group; with r correctly rounded and q0 within
 //     an ulp this Markstein-style correction yields RN(x/s) (P. Markstein, IBM
 //     J. Res. Dev. 34(1), 1990). The GPU parity tests check it against the
-//     oracle's IEEE divisions over every (absmax, x) pair of fp16 values.
+//     oracle's IEEE divisions over every (absmax, x) pair of fp16 values. The
+//     kernel runs it with r/8 and 8s in place of r and s (power-of-two factors,
+//     so every step is the same rounding scaled by 1/8) and reads x straight from
+//     its fp16 half (mixed-precision fma, no conversion): the result is t/8,
+//     t = RN(x/s).
 //   * s = RN(a/7) the same way with r7 = RN(1/7).
-//   * rne + clamp on the magnitude: RNE is symmetric, so |q| = rne(|x| / s);
-//     t = |x|/s is clamped to [0, 7] and 2^23 is added (binary32 spacing is 1 on
-//     [2^23, 2^24), so the add rounds half-to-even) leaving |q| in the low bits.
+//   * rounding, clamp, sign and packing in one instruction: |t| <= 7 (1 + 2^-23),
+//     so t/8 lies in the subnormal range of FP6 E2M3, spaced 1/8 apart, where
+//     round-to-nearest-even to FP6 is rne(t) / 8 -- the field sign << 5 | |q|.
+//     v_cvt_scalef32_2xpk16_fp6_f32 converts 32 such values (even k from its
+//     first operand, odd k from its second) into the 192-bit stream of two
+//     8-byte units, and an AND-OR per word folds it. The sign of t is that of x,
+//     zero included: the correction is written as en = fma(q0, 8s, -x),
+//     q1 = fma(-en, r/8, q0), whose zero results carry the sign of x.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -42,8 +56,11 @@ namespace w4a4 {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kRowsPerThread = 4;   // independent 16-byte loads in flight per lane
-constexpr float kMagic = 8388608.0f;    // 2^23
+constexpr int kRowsPerThread = 4;   // MXFP4: independent 16-byte loads in flight per lane
+constexpr int64_t kMaxGridY = 65535;
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // Correctly rounded x / d given r = RN(1/d) (d normal, no overflow/underflow).
 __device__ __forceinline__ float div_rn(float x, float d, float r) {
@@ -52,132 +69,195 @@ __device__ __forceinline__ float div_rn(float x, float d, float r) {
   return fmaf(e, r, q0);
 }
 
-// |q| = min(rne(t), 7) for t >= 0, in the low 3 bits of the returned word.
-__device__ __forceinline__ uint32_t mag_code(float t) {
-  return __float_as_uint(__builtin_amdgcn_fmed3f(t, 0.0f, 7.0f) + kMagic);
-}
-
 // Bits of a word at positions 3, 4 (mod 6), where the stream's first word is
 // zero, and at 0, 5 (mod 6), where its third word is zero; together they cover
 // every bit the second word can have set.
 constexpr uint32_t kFoldX = 0x18618618u;
 constexpr uint32_t kFoldY = 0x61861861u;
 
-// 16 magnitudes (low 3 bits of m[]) and the 16 fp16 inputs they came from
-// (r0: inputs 0..7, r1: 8..15) -> the 8-byte INT4 unit (layout in the header).
-__device__ __forceinline__ uint2 pack16(const uint32_t m[16], uint4 r0, uint4 r1) {
-  const uint32_t h[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  uint32_t f[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k)    // FP6 field: sign of input k (fp16 bit 15) << 5 | |c_k|
-    f[k] = (m[k] & 7u) | (((h[k >> 1] >> (16 * (k & 1) + 15)) & 1u) << 5);
-  const uint32_t s0 = f[0] | f[1] << 6 | f[2] << 12 | f[3] << 18 | f[4] << 24 | f[5] << 30;
-  const uint32_t s1 = f[5] >> 2 | f[6] << 4 | f[7] << 10 | f[8] << 16 | f[9] << 22 | f[10] << 28;
-  const uint32_t s2 = f[10] >> 4 | f[11] << 2 | f[12] << 8 | f[13] << 14 | f[14] << 20 | f[15] << 26;
-  return uint2{s0 | (s1 & kFoldX), s2 | (s1 & kFoldY)};
-}
-
-// Group scale and its reciprocal (r = 0 for an all-zero group so every code is 0).
-__device__ __forceinline__ void group_scale(float a, float& s, float& r) {
+// Group scale s, and r8 = RN(1/s) / 8, s8 = 8 s for the scaled division
+// (r8 = 0 for an all-zero group, so every code is a zero of the input's sign).
+__device__ __forceinline__ void group_scale(float a, float& s, float& r8, float& s8) {
   constexpr float r7 = 1.0f / 7.0f;      // RN(1/7), folded at compile time
   s = div_rn(a, 7.0f, r7);
-  r = (s == 0.0f) ? 0.0f : 1.0f / s;     // correctly rounded division
+  r8 = ((s == 0.0f) ? 0.0f : 1.0f / s) * 0.125f;   // correctly rounded division
+  s8 = s * 8.0f;
 }
 
-__device__ __forceinline__ uint2 int4_codes16(const float f[16], uint4 r0, uint4 r1, float s, float r) {
-  uint32_t m[16];
+// max |x| over the 2 NW fp16 values of w[0..NW) (NW even), as fp32.
+template <int NW>
+__device__ __forceinline__ float absmax_words(const uint32_t* w) {
+  h2 mx = {0, 0}, mn = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) m[i] = mag_code(div_rn(fabsf(f[i]), s, r));
-  return pack16(m, r0, r1);
+  for (int i = 0; i < NW; i += 2) {
+    const h2 a = __builtin_bit_cast(h2, w[i]), b = __builtin_bit_cast(h2, w[i + 1]);
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, a), b);
+    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, a), b);
+  }
+  mx = __builtin_elementwise_maximum(mx, -mn);
+  return fmaxf((float)mx.x, (float)mx.y);
+}
+
+// t / 8 with t = RN(x / s), sign of x kept on zero results. nz is -0.0 held in a
+// register (an fma with a literal -0 addend would be rewritten as a multiply,
+// which cannot read the fp16 operand directly).
+__device__ __forceinline__ float quot8(_Float16 h, float r8, float s8, float nz) {
+  const float x = (float)h;
+  const float q0 = fmaf(x, r8, nz);
+  const float en = fmaf(q0, s8, -x);
+  return fmaf(-en, r8, q0);
+}
+
+// Codes of the 2 NW fp16 values of w[0..NW) (NW = 16 or 8): the 192-bit FP6
+// stream of up to 32 codes, folded into 8-byte units (out.x/y: codes 0..15,
+// out.z/w: codes 16..31).
+template <int NW>
+__device__ __forceinline__ uint4 int4_codes(const uint32_t* w, float r8, float s8, float nz) {
+  v16f ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < NW) {
+      const h2 v = __builtin_bit_cast(h2, w[i]);
+      ev[i] = quot8(v.x, r8, s8, nz);   // k = 2i   -> field 2i
+      od[i] = quot8(v.y, r8, s8, nz);   // k = 2i+1 -> field 2i+1
+    } else {
+      ev[i] = 0.0f;
+      od[i] = 0.0f;
+    }
+  }
+  const auto f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  return uint4{f[0] | (f[1] & kFoldX), f[2] | (f[1] & kFoldY),
+               f[3] | (f[4] & kFoldX), f[5] | (f[4] & kFoldY)};
+}
+
+__device__ __forceinline__ float opaque_neg_zero() {
+  float nz = -0.0f;
+  asm volatile("" : "+v"(nz));
+  return nz;
+}
+
+__device__ __forceinline__ void words16(const uint4 r[4], uint32_t w[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[4 * j] = r[j].x; w[4 * j + 1] = r[j].y; w[4 * j + 2] = r[j].z; w[4 * j + 3] = r[j].w;
+  }
 }
 
 // Lane mapping of the 2-D grid: a block is kQuantThreads lanes = (256 / W) row
-// slots x W chunk columns, W in {64, 128, 256}; each lane covers kRowsPerThread
-// rows spaced (256 / W) apart.
+// slots x W chunk columns, W in {64, 128, 256}; each lane covers RPT rows
+// spaced (256 / W) apart.
 struct Map {
-  int col;       // chunk index within the row (16 elements INT4, 8 MXFP4)
+  int col;       // chunk index within the row (32 elements INT4, 8 MXFP4)
   int row0;      // first row
   int rstep;     // row spacing between a lane's rows
 };
 
+template <int RPT>
 __device__ __forceinline__ Map lane_map(int wshift) {
   const int W = 1 << wshift;
   Map m;
   m.col = blockIdx.x * W + (threadIdx.x & (W - 1));
   m.rstep = kQuantThreads >> wshift;
-  m.row0 = blockIdx.y * m.rstep * kRowsPerThread + (threadIdx.x >> wshift);
+  m.row0 = blockIdx.y * m.rstep * RPT + (threadIdx.x >> wshift);
   return m;
 }
 
-// One group of G elements spans G/16 consecutive lanes of one row; a lane
-// covers 16 elements (chunk col) of each of its rows.
+// Lane tile: a wave covers 64 / LPW rows x LPW consecutive 32-element chunks
+// (LPW = max(G / 32, 4) lanes per row, the G/32 lanes of a group adjacent), the
+// block's four waves consecutive chunk runs of the same rows; blockIdx.x walks
+// along the rows (HBM is swept row block by row block). The lanes that store a
+// group's scale hold consecutive rows of it, so the group-major scale array is
+// written in runs of 64 / LPW rows (64 bytes at G <= 128) instead of lone
+// 4-byte words. Row blocks beyond gridDim.y are taken in a loop.
+// q16: the code array is 16-byte aligned (one store per lane).
 template <int G>
 __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_groups(
-    const uint16_t* __restrict__ x, int64_t ldx, int M, int cpr, int wshift,
+    const uint16_t* __restrict__ x, int64_t ldx, int M, int cpr, int q16,
     uint2* __restrict__ q, float* __restrict__ s) {
-  constexpr int LPG = G / 16;
-  const Map mp = lane_map(wshift);
-  if (mp.col >= cpr) return;                  // whole lane groups drop out together
-  uint4 raw[kRowsPerThread][2];
+  constexpr int LPG = G / 32;
+  constexpr int LPW = LPG > 4 ? LPG : 4;
+  constexpr int RW = 64 / LPW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * (4 * LPW) + wave * LPW + (lane % LPW);
+  if (col >= cpr) return;                      // whole groups drop out together
+  const float nz = opaque_neg_zero();
+  for (int rb = blockIdx.y; rb * RW < M; rb += gridDim.y) {
+    const int row = rb * RW + lane / LPW;
+    if (row >= M) break;                       // the last row block only
+    uint4 raw[4];
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + col * 32);
 #pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    const int row = mp.row0 + u * mp.rstep;
-    if (row < M) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + mp.col * 16);
-      raw[u][0] = src[0];
-      raw[u][1] = src[1];
+    for (int j = 0; j < 4; ++j) raw[j] = src[j];
+    uint32_t w[16];
+    words16(raw, w);
+    const float a = group_max<LPG>(absmax_words<16>(w));
+    float sc, r8, s8;
+    group_scale(a, sc, r8, s8);
+    const uint4 c = int4_codes<16>(w, r8, s8, nz);
+    const int64_t pair = (int64_t)row * cpr + col;     // 16-byte unit pair index
+    if (q16) {
+      reinterpret_cast<uint4*>(q)[pair] = c;
+    } else {
+      q[2 * pair] = uint2{c.x, c.y};
+      q[2 * pair + 1] = uint2{c.z, c.w};
     }
-  }
-#pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    const int row = mp.row0 + u * mp.rstep;
-    if (row < M) {                            // uniform across each lane group
-      float f[16];
-      halves_to_float8(raw[u][0], f);
-      halves_to_float8(raw[u][1], f + 8);
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
-      a = group_max<LPG>(a);
-      float sc, rc;
-      group_scale(a, sc, rc);
-      q[(int64_t)row * cpr + mp.col] = int4_codes16(f, raw[u][0], raw[u][1], sc, rc);
-      if ((threadIdx.x & (LPG - 1)) == 0) s[(int64_t)(mp.col / LPG) * M + row] = sc;   // group-major
-    }
+    if (lane % LPG == 0) s[(int64_t)(col / LPG) * M + row] = sc;   // group-major
   }
 }
 
-// Per-token quantization (one group spans the whole row): one block per row,
-// absmax reduced across the block, then the row is read again from cache.
+// Per-token quantization (one group spans the whole row, K % 16 == 0): one
+// block per row, absmax reduced across the block, then the row is read again
+// from cache. Lanes take 32-element chunks; a 16-element tail goes to lane 0.
 __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
-    const uint16_t* __restrict__ x, int64_t ldx, int cpr,
+    const uint16_t* __restrict__ x, int64_t ldx, int K,
     uint2* __restrict__ q, float* __restrict__ s) {
   __shared__ float wave_max[kQuantThreads / 64];
   const int row = blockIdx.x;
   const uint16_t* xr = x + row * ldx;
+  const int n32 = K >> 5;
+  const bool tail = (K & 16) != 0;
   float a = 0.0f;
-  for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
-    const uint4* src = reinterpret_cast<const uint4*>(xr + c * 16);
-    float f[16];
-    halves_to_float8(src[0], f);
-    halves_to_float8(src[1], f + 8);
+  for (int c = threadIdx.x; c < n32; c += kQuantThreads) {
+    const uint4* src = reinterpret_cast<const uint4*>(xr + c * 32);
+    uint4 r[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[i]));
+    for (int j = 0; j < 4; ++j) r[j] = src[j];
+    uint32_t w[16];
+    words16(r, w);
+    a = fmaxf(a, absmax_words<16>(w));
+  }
+  if (tail && threadIdx.x == 0) {
+    const uint4* src = reinterpret_cast<const uint4*>(xr + n32 * 32);
+    const uint4 r0 = src[0], r1 = src[1];
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    a = fmaxf(a, absmax_words<8>(w));
   }
   a = group_max<64>(a);
   if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kQuantThreads / 64; ++w) a = fmaxf(a, wave_max[w]);
-  float sc, rc;
-  group_scale(a, sc, rc);
-  for (int c = threadIdx.x; c < cpr; c += kQuantThreads) {
-    const uint4* src = reinterpret_cast<const uint4*>(xr + c * 16);
+  float sc, r8, s8;
+  group_scale(a, sc, r8, s8);
+  const float nz = opaque_neg_zero();
+  uint2* qr = q + (int64_t)row * (K >> 4);
+  for (int c = threadIdx.x; c < n32; c += kQuantThreads) {
+    const uint4* src = reinterpret_cast<const uint4*>(xr + c * 32);
+    uint4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = src[j];
+    uint32_t w[16];
+    words16(r, w);
+    const uint4 v = int4_codes<16>(w, r8, s8, nz);
+    qr[2 * c] = uint2{v.x, v.y};
+    qr[2 * c + 1] = uint2{v.z, v.w};
+  }
+  if (tail && threadIdx.x == 0) {
+    const uint4* src = reinterpret_cast<const uint4*>(xr + n32 * 32);
     const uint4 r0 = src[0], r1 = src[1];
-    float f[16];
-    halves_to_float8(r0, f);
-    halves_to_float8(r1, f + 8);
-    q[(int64_t)row * cpr + c] = int4_codes16(f, r0, r1, sc, rc);
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    const uint4 v = int4_codes<8>(w, r8, s8, nz);
+    qr[2 * n32] = uint2{v.x, v.y};
   }
   if (threadIdx.x == 0) s[row] = sc;
 }
@@ -199,7 +279,7 @@ __device__ __forceinline__ uint32_t e2m1_codes8(const float v[8]) {
 __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
     const uint16_t* __restrict__ x, int64_t ldx, int rows, int cpr, int wshift,
     uint32_t* __restrict__ q, uint8_t* __restrict__ e8m0) {
-  const Map mp = lane_map(wshift);
+  const Map mp = lane_map<kRowsPerThread>(wshift);
   if (mp.col >= cpr) return;
   uint4 raw[kRowsPerThread];
 #pragma unroll
@@ -239,9 +319,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
 
 int width_shift(int cpr) { return cpr <= 64 ? 6 : cpr <= 128 ? 7 : 8; }
 
-dim3 grid_for(int rows, int cpr, int wshift) {
+dim3 grid_for(int rows, int cpr, int wshift, int rpt) {
   const int W = 1 << wshift;
-  const int rows_per_block = (kQuantThreads >> wshift) * kRowsPerThread;
+  const int rows_per_block = (kQuantThreads >> wshift) * rpt;
   return dim3((unsigned)((cpr + W - 1) / W), (unsigned)((rows + rows_per_block - 1) / rows_per_block));
 }
 
@@ -251,18 +331,22 @@ void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int gro
                        uint8_t* q, float* s, hipStream_t stream) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint2* qp = reinterpret_cast<uint2*>(q);
-  const int cpr = (int)(K / 16);      // 16-element chunks per row
-  const int ws = width_shift(cpr);
-  const dim3 grid = grid_for((int)M, cpr, ws);
+  if (group != 64 && group != 128 && group != 256 && group != 512) {   // group == K (per token)
+    hipLaunchKernelGGL(k_int4_quant_rows, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, xp, ldx, (int)K, qp, s);
+    return;
+  }
+  const int cpr = (int)(K / 32);      // 32-element chunks per row (K % group == 0)
   const int m = (int)M;
-  switch (group == K && group > 512 ? 0 : group) {
-    case 64: hipLaunchKernelGGL(k_int4_quant_groups<64>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
-    case 128: hipLaunchKernelGGL(k_int4_quant_groups<128>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
-    case 256: hipLaunchKernelGGL(k_int4_quant_groups<256>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
-    case 512: hipLaunchKernelGGL(k_int4_quant_groups<512>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, ws, qp, s); return;
-    default:  // group == K (per token), validated by the caller
-      hipLaunchKernelGGL(k_int4_quant_rows, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, xp, ldx, cpr, qp, s);
-      return;
+  const int q16 = (reinterpret_cast<uintptr_t>(q) & 15) == 0;
+  const int64_t rw = group >= 128 ? 2048 / group : 16;          // rows per wave, 64 / LPW
+  const int64_t lpw = 64 / rw;
+  const dim3 grid((unsigned)((cpr + 4 * lpw - 1) / (4 * lpw)),
+                  (unsigned)std::min<int64_t>((M + rw - 1) / rw, kMaxGridY));
+  switch (group) {
+    case 64: hipLaunchKernelGGL(k_int4_quant_groups<64>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, q16, qp, s); return;
+    case 128: hipLaunchKernelGGL(k_int4_quant_groups<128>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, q16, qp, s); return;
+    case 256: hipLaunchKernelGGL(k_int4_quant_groups<256>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, q16, qp, s); return;
+    default: hipLaunchKernelGGL(k_int4_quant_groups<512>, grid, dim3(kQuantThreads), 0, stream, xp, ldx, m, cpr, q16, qp, s); return;
   }
 }
 
@@ -270,7 +354,7 @@ void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
                         uint8_t* q, uint8_t* e8m0, hipStream_t stream) {
   const int cpr = (int)(K / 8);
   const int ws = width_shift(cpr);
-  hipLaunchKernelGGL(k_mxfp4_quant, grid_for((int)rows, cpr, ws), dim3(kQuantThreads), 0, stream,
+  hipLaunchKernelGGL(k_mxfp4_quant, grid_for((int)rows, cpr, ws, kRowsPerThread), dim3(kQuantThreads), 0, stream,
                      static_cast<const uint16_t*>(x), ldx, (int)rows, cpr, ws,
                      reinterpret_cast<uint32_t*>(q), e8m0);
 }

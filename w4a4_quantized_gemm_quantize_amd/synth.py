@@ -107,6 +107,19 @@ def activations(M: int, K: int, *, dist: str = "t3", seed: int = 0,
     return out
 
 
+def bulk_normal(M: int, K: int, *, seed: int = 0) -> np.ndarray:
+    """fp16 N(0,1) matrix [M, K] from one generator, drawn in row chunks: for
+    tests whose point is the row count (grid limits), where building one
+    generator per row would dominate."""
+    g = _rng(seed, STREAM_X, 1 << 40)
+    out = np.empty((M, K), dtype=np.float16)
+    step = max(1, (1 << 22) // max(K, 1))
+    for r in range(0, M, step):
+        n = min(step, M - r)
+        out[r:r + n] = g.standard_normal((n, K), dtype=np.float32).astype(np.float16)
+    return out
+
+
 def weights(N: int, K: int, *, std: float = 0.02, seed: int = 0, rows=None) -> np.ndarray:
     """fp16 weight matrix W[N, K] ~ N(0, std) (or the listed ``rows`` of it)."""
     row_ids = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)

@@ -152,6 +152,18 @@ def test_mxfp4_shapes():
     x[3, :64] = 0
     mx_check(x)
     mx_check(synth.weights(40, 3584, seed=7))
+    mx_check(synth.activations(19, 1120, dist="t3", seed=9))    # last panel 3 blocks wide
+    mx_check(synth.activations(5, 96, dist="t3", seed=10))      # one panel, 3 blocks
+
+
+def test_mxfp4_rows_beyond_one_grid_dimension():
+    R, K = 65535 * 8 + 24, 64
+    x = synth.bulk_normal(R, K, seed=11)
+    q, e = ops().mxfp4_quantize(dev(x))
+    rows = np.concatenate([synth.sample_rows(R, 48, seed=3), np.arange(R - 40, R)])
+    codes, e8 = oracle.mxfp4_quantize(x[rows])
+    assert np.array_equal(ops().mxfp4_scales_to_rows(host(e), R, K)[rows], e8)
+    assert np.array_equal(host(q)[rows], oracle.pack_nibbles(codes))
 
 
 def _anchor_groups(lo, hi):

@@ -49,14 +49,4 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // are dropped, even with a scalar offset < 2^31 added.
 constexpr int kDroppedOffset = (int)0x80000000u;
 
-// Eight fp16 values from one 16-byte load, widened exactly to fp32.
-__device__ __forceinline__ void halves_to_float8(uint4 raw, float f[8]) {
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xFFFFu)));
-    f[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
-  }
-}
-
 }  // namespace w4a4

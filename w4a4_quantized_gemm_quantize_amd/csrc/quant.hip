@@ -18,11 +18,11 @@
 // GEMM reads one stage's scales of a tile as one contiguous run and a lane's
 // bytes as one dword.
 //
-// Both kernels stream HBM: each lane loads 32 (INT4) or 8 (MXFP4) consecutive
-// fp16 values per row it covers with 128-bit loads, a group's absmax is reduced
-// across the lanes that hold it with DPP row permutes (no LDS), and each lane
-// writes its codes with one store (two 8-byte INT4 units, one 32-bit E2M1 word).
-// The grid is 2-D (chunk column x row block), so no lane divides to find its row.
+// Both kernels stream HBM: each lane loads 32 consecutive fp16 values of a row
+// with 128-bit loads, an INT4 group's absmax is reduced across the lanes that
+// hold it with DPP row permutes (no LDS; an MXFP4 block is one lane), and each
+// lane writes its codes with one 16-byte store. The grid is 2-D (chunk run x
+// row block), so no lane divides to find its row.
 //
 // Vector-ALU economy for the INT4 rule (the stream must not become ALU-bound;
 // about 4 vector instructions per element):
@@ -56,7 +56,6 @@ namespace w4a4 {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kRowsPerThread = 4;   // MXFP4: independent 16-byte loads in flight per lane
 constexpr int64_t kMaxGridY = 65535;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -141,25 +140,6 @@ __device__ __forceinline__ void words16(const uint4 r[4], uint32_t w[16]) {
   for (int j = 0; j < 4; ++j) {
     w[4 * j] = r[j].x; w[4 * j + 1] = r[j].y; w[4 * j + 2] = r[j].z; w[4 * j + 3] = r[j].w;
   }
-}
-
-// Lane mapping of the 2-D grid: a block is kQuantThreads lanes = (256 / W) row
-// slots x W chunk columns, W in {64, 128, 256}; each lane covers RPT rows
-// spaced (256 / W) apart.
-struct Map {
-  int col;       // chunk index within the row (32 elements INT4, 8 MXFP4)
-  int row0;      // first row
-  int rstep;     // row spacing between a lane's rows
-};
-
-template <int RPT>
-__device__ __forceinline__ Map lane_map(int wshift) {
-  const int W = 1 << wshift;
-  Map m;
-  m.col = blockIdx.x * W + (threadIdx.x & (W - 1));
-  m.rstep = kQuantThreads >> wshift;
-  m.row0 = blockIdx.y * m.rstep * RPT + (threadIdx.x >> wshift);
-  return m;
 }
 
 // Lane tile: a wave covers 64 / LPW rows x LPW consecutive 32-element chunks
@@ -262,67 +242,66 @@ __global__ __launch_bounds__(kQuantThreads) void k_int4_quant_rows(
   if (threadIdx.x == 0) s[row] = sc;
 }
 
-// E2M1 conversion of 8 values already divided by 2^E, two per instruction:
-// v_cvt_scalef32_pk_fp4_f32 (unit scale) rounds to nearest of
-// {0,0.5,1,1.5,2,3,4,6}, ties to even, saturates at 6 and keeps the sign of
-// zero -- the OCP MX rule; the parity tests check it over every fp16 input.
-__device__ __forceinline__ uint32_t e2m1_codes8(const float v[8]) {
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
-  return w;
+// E2M1 codes of 32 fp16 values (16 words, even k in the low halves) divided by
+// d = 2^E: v_cvt_scalef32_pk_fp4_f16 converts two fp16 values to the E2M1 codes
+// of x / d, rounding to nearest of {0,0.5,1,1.5,2,3,4,6} with ties to even,
+// saturating at 6 and keeping the sign of zero -- the OCP MX rule; the parity
+// tests check it over every fp16 input. Byte i of output word j holds elements
+// 8j + 2i (low nibble) and 8j + 2i + 1.
+__device__ __forceinline__ uint4 e2m1_codes32(const uint32_t w[16], float d) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t v = 0;
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(v, __builtin_bit_cast(h2, w[4 * j]), d, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(v, __builtin_bit_cast(h2, w[4 * j + 1]), d, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(v, __builtin_bit_cast(h2, w[4 * j + 2]), d, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(v, __builtin_bit_cast(h2, w[4 * j + 3]), d, 3);
+    o[j] = v;
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
 }
 
-// 32-element block = 4 lanes x 8 values.
+// Lane tile: a lane takes one 32-element block of a row (absmax within the
+// lane); a wave covers 8 rows x the 8 blocks of one 256-k panel, the block's
+// four waves the next panels of the same rows, blockIdx.x walking along the
+// rows. A wave's 64 scale bytes are then one contiguous run of the panel
+// layout (8 rows x w_p bytes). Row blocks beyond gridDim.y are looped.
+// q16: the code array is 16-byte aligned (one store per lane).
 __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
-    const uint16_t* __restrict__ x, int64_t ldx, int rows, int cpr, int wshift,
+    const uint16_t* __restrict__ x, int64_t ldx, int rows, int nb, int q16,
     uint32_t* __restrict__ q, uint8_t* __restrict__ e8m0) {
-  const Map mp = lane_map<kRowsPerThread>(wshift);
-  if (mp.col >= cpr) return;
-  uint4 raw[kRowsPerThread];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = (blockIdx.x * 4 + wave) * 8 + (lane & 7);     // block of the row
+  if (b >= nb) return;
+  // panel layout: block b goes to panel b / 8, whose rows hold pw = min(8,
+  // blocks left) bytes each, the even blocks' bytes first
+  const int pq = b >> 3, pw = min(8, nb - 8 * pq), j = b & 7;
+  const int pos = (j & 1) ? ((pw + 1) >> 1) + (j >> 1) : (j >> 1);
+  for (int rb = blockIdx.y; rb * 8 < rows; rb += gridDim.y) {
+    const int row = rb * 8 + (lane >> 3);
+    if (row >= rows) break;                  // the last row block only
+    uint4 raw[4];
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx + b * 32);
 #pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    const int row = mp.row0 + u * mp.rstep;
-    if (row < rows) raw[u] = *reinterpret_cast<const uint4*>(x + row * ldx + mp.col * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < kRowsPerThread; ++u) {
-    const int row = mp.row0 + u * mp.rstep;
-    if (row < rows) {
-      float f[8];
-      halves_to_float8(raw[u], f);
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-      a = group_max<4>(a);
-      // a is 0 or a normal fp32 (fp16 values widen to normal fp32), so its
-      // biased exponent field is floor(log2 a) + 127.
-      const int biased = (int)((__float_as_uint(a) >> 23) & 0xFF);
-      const int E = (a == 0.0f) ? -127 : biased - 127 - 2;
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = ldexpf(f[i], -E);   // exact power-of-two scaling
-      q[(int64_t)row * cpr + mp.col] = e2m1_codes8(v);
-      if ((threadIdx.x & 3) == 0) {
-        // panel layout: block b of the row goes to panel b / 8, whose rows hold
-        // pw = min(8, blocks left) bytes each, the even blocks' bytes first
-        const int b = mp.col >> 2, nb = cpr >> 2;
-        const int pq = b >> 3, pw = min(8, nb - 8 * pq), j = b & 7;
-        const int pos = (j & 1) ? ((pw + 1) >> 1) + (j >> 1) : (j >> 1);
-        e8m0[(int64_t)8 * rows * pq + (int64_t)row * pw + pos] = (uint8_t)(E + 127);
-      }
+    for (int i = 0; i < 4; ++i) raw[i] = src[i];
+    uint32_t w[16];
+    words16(raw, w);
+    const float a = absmax_words<16>(w);
+    // a is 0 or a normal fp32 (fp16 values widen to normal fp32), so its
+    // biased exponent field is floor(log2 a) + 127; E = floor(log2 a) - 2.
+    const int biased = (int)((__float_as_uint(a) >> 23) & 0xFF);
+    const int E = (a == 0.0f) ? -127 : biased - 127 - 2;
+    const float d = (a == 0.0f) ? 1.0f : __uint_as_float((uint32_t)(biased - 2) << 23);   // 2^E, normal
+    const uint4 c = e2m1_codes32(w, d);
+    const int64_t unit = (int64_t)row * nb + b;          // 16-byte code unit
+    if (q16) {
+      reinterpret_cast<uint4*>(q)[unit] = c;
+    } else {
+      q[4 * unit] = c.x; q[4 * unit + 1] = c.y; q[4 * unit + 2] = c.z; q[4 * unit + 3] = c.w;
     }
+    e8m0[(int64_t)8 * rows * pq + (int64_t)row * pw + pos] = (uint8_t)(E + 127);
   }
-}
-
-int width_shift(int cpr) { return cpr <= 64 ? 6 : cpr <= 128 ? 7 : 8; }
-
-dim3 grid_for(int rows, int cpr, int wshift, int rpt) {
-  const int W = 1 << wshift;
-  const int rows_per_block = (kQuantThreads >> wshift) * rpt;
-  return dim3((unsigned)((cpr + W - 1) / W), (unsigned)((rows + rows_per_block - 1) / rows_per_block));
 }
 
 }  // namespace
@@ -352,10 +331,11 @@ void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int gro
 
 void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
                         uint8_t* q, uint8_t* e8m0, hipStream_t stream) {
-  const int cpr = (int)(K / 8);
-  const int ws = width_shift(cpr);
-  hipLaunchKernelGGL(k_mxfp4_quant, grid_for((int)rows, cpr, ws, kRowsPerThread), dim3(kQuantThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), ldx, (int)rows, cpr, ws,
+  const int nb = (int)(K / 32);
+  const dim3 grid((unsigned)((nb + 31) / 32), (unsigned)std::min<int64_t>((rows + 7) / 8, kMaxGridY));
+  const int q16 = (reinterpret_cast<uintptr_t>(q) & 15) == 0;
+  hipLaunchKernelGGL(k_mxfp4_quant, grid, dim3(kQuantThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), ldx, (int)rows, nb, q16,
                      reinterpret_cast<uint32_t*>(q), e8m0);
 }
 

@@ -28,12 +28,17 @@
 // K stage 128 (two MFMA k-steps), double-buffered LDS (50 KB), two workgroups
 // per CU (two waves per SIMD). The staging threads fetch stage kt+2 while
 // stage kt is computed and stage kt+1 is unpacked (two register sets), and the
-// stage barrier orders LDS only, so no wait drains those loads. Within a stage
-// each wave streams its four 32x32 tiles in the order (0,0) (1,0) (1,1) (0,1),
-// issuing a tile's epilogue next to the following tile's MFMAs; with groups of
-// <= 128 only two tiles' partials are live at once. (Measured on gfx950: a wave
-// overlaps little of its own vector work with its own MFMAs; the overlap comes
-// from the other wave on the SIMD.) Tiles are ordered XCD-contiguous, then in
+// stage barrier orders LDS only, so no wait drains those loads.
+// With g = 128 a stage is one group and runs as a software pipeline of ten
+// chunks, each one MFMA issued first and then the vector work that runs under
+// it: the epilogue of a tile whose partials finished two or more MFMAs
+// earlier (so it never waits on the matrix core), one of the staging stores
+// of the next stage, or operand reads for the next chunks -- spread so that
+// the LDS queue never takes a burst. The last two tiles' epilogues run under
+// the next stage's first four MFMAs (their partials and scale product carried
+// over); empty asm statements pin each MFMA, and scheduling barriers keep
+// each chunk's work in the chunk. Other group sizes run each stage's MFMAs,
+// then its epilogues. Tiles are ordered XCD-contiguous, then in
 // groups of 8 tile-rows, so workgroups running together on one XCD share A and
 // W slices in that XCD's L2.
 //
@@ -220,14 +225,24 @@ void k_w4a4_gemm(Params p) {
     /* groups >= 128: both 64-k halves share a group */               \
     R.s1 = (MODE == G64) ? load_scale((2 * (KT) + 1) >> ssh) : R.s0;  \
   }
-#define LSTORE(BUF, R)                                                \
+// Staging stores of register set R into LDS buffer BUF, one piece at a time
+// (the pipelined g = 128 stage spreads them over its chunks), or all at once.
+#define LST_A0(BUF, R) unpack_store(&sA[BUF][st0], &tA[BUF][tt0], R.a0)
+#define LST_A1(BUF, R) unpack_store(&sA[BUF][st1], &tA[BUF][tt1], R.a1)
+#define LST_W0(BUF, R) unpack_store(&sW[BUF][st0], &tW[BUF][tt0], R.w0)
+#define LST_W1(BUF, R) unpack_store(&sW[BUF][st1], &tW[BUF][tt1], R.w1)
+#define LST_S(BUF, R)                                                 \
   {                                                                   \
-    unpack_store(&sA[BUF][st0], &tA[BUF][tt0], R.a0);                 \
-    unpack_store(&sA[BUF][st1], &tA[BUF][tt1], R.a1);                 \
-    unpack_store(&sW[BUF][st0], &tW[BUF][tt0], R.w0);                 \
-    unpack_store(&sW[BUF][st1], &tW[BUF][tt1], R.w1);                 \
     sS[(BUF) * 2 * BM] = R.s0;                                        \
     sS[(BUF) * 2 * BM + BM] = R.s1;                                   \
+  }
+#define LSTORE(BUF, R)                                                \
+  {                                                                   \
+    LST_A0(BUF, R);                                                   \
+    LST_A1(BUF, R);                                                   \
+    LST_W0(BUF, R);                                                   \
+    LST_W1(BUF, R);                                                   \
+    LST_S(BUF, R);                                                    \
   }
 
   const v16f zero16 = {};
@@ -254,6 +269,10 @@ void k_w4a4_gemm(Params p) {
     rtA[s] = tail_off(wm * 64 + l32, 2 * s + lhi);
     rtW[s] = tail_off(wn * 64 + l32, 2 * s + lhi);
   }
+  // G128 pipeline: scale product of tiles (0,1), (1,1) carried into the next
+  // stage with their partials (zero before the first stage, so its carried
+  // epilogue adds nothing)
+  GroupScales Tc{zero32, 0.0f, 0.0f};
   int gcount = 0;     // GBIG: stages accumulated into P since the last epilogue
   int gidx = 0;       // index of the next group to finish (partials export)
 
@@ -277,6 +296,33 @@ void k_w4a4_gemm(Params p) {
         acc[I][J][r] = fmaf(P[I][J][r], (T).t[16 * (I) + r], acc[I][J][r]);              \
     }                                                                                    \
   }
+  // End of a pipeline chunk: its MFMA issues first, then up to NV vector
+  // instructions, then its LDS traffic; nothing crosses into the next chunk.
+#define CHUNK_END(NV)                                                                    \
+  {                                                                                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);                                  \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                                   \
+    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+  }
+  // Half H (registers 8H .. 8H+7) of the epilogue of tile (I, J), no partials export.
+#define EPI_HALF(I, J, T, H)                                                             \
+  {                                                                                      \
+    if constexpr (ROWA) {                                                                \
+      const float swj_ = (J) == 0 ? (T).sw0 : (T).sw1;                                   \
+      _Pragma("unroll") for (int r = 8 * (H); r < 8 * (H) + 8; ++r)                      \
+        acc[I][J][r] = fmaf(P[I][J][r], swj_, acc[I][J][r]);                             \
+    } else {                                                                             \
+      _Pragma("unroll") for (int r = 8 * (H); r < 8 * (H) + 8; ++r)                      \
+        acc[I][J][r] = fmaf(P[I][J][r], (T).t[16 * (I) + r], acc[I][J][r]);              \
+    }                                                                                    \
+  }
+  // Group scales for tiles (0, J) and (1, J) from scale values already read
+  // (SA: the lane's A-row scale, SW: its W-column scale of column block J).
+#define TPRODV(SA, SW, SW1)                                                              \
+  GroupScales{ROWA ? zero32 : __builtin_amdgcn_mfma_f32_32x32x1f32(SA, SW, zero32, 0, 0, 0), \
+              ROWA ? (SW) : 0.0f, ROWA ? (SW1) : 0.0f}
   // Group scales for tiles (0, J) and (1, J) from 64-k half H of stage buffer B:
   // the two-block product s_a x s_w, or (ROWA) the lane's two W scales.
 #define TPROD(B, H, J)                                                                   \
@@ -313,7 +359,21 @@ void k_w4a4_gemm(Params p) {
         __builtin_amdgcn_sched_barrier(0);                                               \
       }                                                                                  \
     };                                                                                   \
-    if constexpr (MODE != G64) {                                                         \
+    /* W operands of column block 1 (G128 pipeline: read mid-stage) */                \
+    auto load_w1 = [&]() {                                                               \
+      _Pragma("unroll") for (int S = 0; S < 2; ++S) {                                    \
+        b[1][S] = load_op(bW + rdW[S] + 32 * PM, cW + rtW[S] + 32 * PT);                 \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+      }                                                                                  \
+    };                                                                                   \
+    if constexpr (MODE == G128 && !PARTIALS) {                                           \
+      a[0][0] = load_op(bA + rdA[0], cA + rtA[0]);                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      b[0][0] = load_op(bW + rdW[0], cW + rtW[0]);                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      a[1][0] = load_op(bA + rdA[0] + 32 * PM, cA + rtA[0] + 32 * PT);                   \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+    } else if constexpr (MODE != G64) {                                                  \
       load_step(0);                                                                      \
       load_step(1);                                                                      \
     }                                                                                    \
@@ -337,6 +397,61 @@ void k_w4a4_gemm(Params p) {
         __builtin_amdgcn_sched_barrier(0);                                               \
         ++gidx;                                                                          \
       }                                                                                  \
+    } else if constexpr (MODE == G128 && !PARTIALS) {                                    \
+      /* Software pipeline: ten chunks, each one MFMA issued first and the     */    \
+      /* vector work that runs under it. An epilogue reads partials finished  */    \
+      /* two MFMAs or more earlier (no dependency wait); tiles (1,1) and      */    \
+      /* (0,1) are finished under the next stage's first four MFMAs (their    */    \
+      /* partials and scale product Tc carried over). Tc dies before T0 is    */    \
+      /* formed and T0 before the next Tc, so one scale product is live.      */    \
+      /* the stage's scale values (tile rows / columns of this lane) */                 \
+      const float gsa_ = sSA[BUF][0][wm * 64 + lane];                                    \
+      const float gsw0_ = sSW[BUF][0][wn * 64 + l32];                                    \
+      const float gsw1_ = sSW[BUF][0][wn * 64 + 32 + l32];                               \
+      P[0][0] = mma(a[0][0], b[0][0], zero16);                                           \
+      EPI_HALF(1, 1, Tc, 0);                                                             \
+      a[0][1] = load_op(bA + rdA[1], cA + rtA[1]);                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      b[0][1] = load_op(bW + rdW[1], cW + rtW[1]);                                       \
+      CHUNK_END(8);                                                                      \
+      P[1][0] = mma(a[1][0], b[0][0], zero16);                                           \
+      EPI_HALF(1, 1, Tc, 1);                                                             \
+      LST_A0((BUF) ^ 1, RS);                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      a[1][1] = load_op(bA + rdA[1] + 32 * PM, cA + rtA[1] + 32 * PT);                   \
+      CHUNK_END(16);                                                                     \
+      P[0][0] = mma(a[0][1], b[0][1], P[0][0]);                                          \
+      EPI_HALF(0, 1, Tc, 0);                                                             \
+      CHUNK_END(8);                                                                      \
+      P[1][0] = mma(a[1][1], b[0][1], P[1][0]);                                          \
+      EPI_HALF(0, 1, Tc, 1);                                                             \
+      LST_A1((BUF) ^ 1, RS);                                                             \
+      CHUNK_END(16);                                                                     \
+      GroupScales T0 = TPRODV(gsa_, gsw0_, gsw1_);                                       \
+      asm volatile("" : "+v"(T0.t));                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      load_w1();                                                                         \
+      CHUNK_END(16);                                                                     \
+      P[1][1] = mma(a[1][0], b[1][0], zero16);                                           \
+      EPI_HALF(0, 0, T0, 0);                                                             \
+      CHUNK_END(8);                                                                      \
+      P[0][1] = mma(a[0][0], b[1][0], zero16);                                           \
+      EPI_HALF(0, 0, T0, 1);                                                             \
+      LST_W0((BUF) ^ 1, RS);                                                             \
+      CHUNK_END(16);                                                                     \
+      P[1][1] = mma(a[1][1], b[1][1], P[1][1]);                                          \
+      EPI_HALF(1, 0, T0, 0);                                                             \
+      CHUNK_END(8);                                                                      \
+      P[0][1] = mma(a[0][1], b[1][1], P[0][1]);                                          \
+      EPI_HALF(1, 0, T0, 1);                                                             \
+      LST_W1((BUF) ^ 1, RS);                                                             \
+      CHUNK_END(16);                                                                     \
+      Tc = TPRODV(gsa_, gsw1_, gsw1_);                                                   \
+      LST_S((BUF) ^ 1, RS);                                                              \
+      CHUNK_END(16);                                                                     \
+      /* keep Tc's MFMA here (it would sink into the next stage) */                     \
+      asm volatile("" : "+v"(Tc.t));                                                    \
+      ++gidx;                                                                            \
     } else if constexpr (MODE == G128) {                                                 \
       const GroupScales T0 = TPROD(BUF, 0, 0);                                           \
       P[0][0] = mma(a[0][1], b[0][1], mma(a[0][0], b[0][0], zero16));                    \
@@ -391,10 +506,24 @@ void k_w4a4_gemm(Params p) {
     STAGE(kt + 1, 1, RX, R0);
   }
   if (kt < nk) STAGE(kt, 0, R0, RX);
+  if constexpr (MODE == G128 && !PARTIALS) {   // the last stage's carried tiles
+    EPI_HALF(1, 1, Tc, 0);
+    EPI_HALF(1, 1, Tc, 1);
+    EPI_HALF(0, 1, Tc, 0);
+    EPI_HALF(0, 1, Tc, 1);
+  }
 #undef GLOAD
 #undef LSTORE
+#undef LST_A0
+#undef LST_A1
+#undef LST_W0
+#undef LST_W1
+#undef LST_S
+#undef EPI_HALF
+#undef CHUNK_END
 #undef EPI
 #undef TPROD
+#undef TPRODV
 #undef STAGE
 
   if constexpr (!PARTIALS) {

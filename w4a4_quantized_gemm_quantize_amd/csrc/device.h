@@ -38,6 +38,11 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Cache policy of the output stores: non-temporal. Y is written once and not
+// read back by the kernel; the hint keeps it from displacing the operand slabs
+// that later tiles re-read from L2 and the last-level cache.
+constexpr int kStoreNT = 2;
+
 // Raw buffer resource over [base, base + bytes): loads beyond the range read
 // 0 and stores beyond it are dropped (the range check covers the vector
 // offset). Word 3 is the CDNA raw-buffer format word (32-bit data, no swizzle).

@@ -398,7 +398,7 @@ void k_mxfp4_gemm(Params p) {
             const int soff = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rY, voffY[j], soff, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rY, voffY[j], soff, kStoreNT);
           }
       } else {
 #pragma unroll
@@ -409,7 +409,7 @@ void k_mxfp4_gemm(Params p) {
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
               __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(acc[i][j][r])), rY,
-                                                    voffY[j], soff, 0);
+                                                    voffY[j], soff, kStoreNT);
           }
       }
     } else {

@@ -555,9 +555,9 @@ void k_w4a4_gemm(Params p) {
           for (int j = 0; j < 2; ++j) {
             const float v = ROWA ? acc[i][j][r] * sa : acc[i][j][r];
             if (p.ydtype == 0)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rY, voffY[j], soff, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rY, voffY[j], soff, kStoreNT);
             else
-              __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(v)), rY, voffY[j], soff, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(v)), rY, voffY[j], soff, kStoreNT);
           }
         }
     } else {

@@ -57,6 +57,18 @@ def test_mixed_granularity(ga, gw):
     run_case(200, 160, 1024, ga, gw, seed=ga + gw, window=(60, 100, 20, 130))
 
 
+@pytest.mark.parametrize("M,N,K,ga,gw", [
+    (19, 200, 1024, 64, 128), (19, 200, 1024, 128, 64), (19, 200, 1024, 256, 128),
+    (19, 200, 1024, 128, 1024), (19, 200, 1024, 64, 64), (7, 96, 1024, 1024, 128),
+    (5, 70, 384, 128, 128),            # three groups for four waves
+    (3, 64, 384, 384, 384),            # one per-token group on each side
+    (32, 160, 512, 128, 128), (33, 160, 512, 128, 128),     # small-M path (M <= 64, few tiles)
+    (65, 160, 512, 128, 128),                                # tiled path
+    (3, 16400, 512, 64, 128)])                               # 513 workgroups: four waves each
+def test_small_m(M, N, K, ga, gw):
+    run_case(M, N, K, ga, gw, seed=M + N, check_fp16=True)
+
+
 def test_fp16_output_and_strided_y():
     import torch
     M, N, K = 64, 96, 512

@@ -582,6 +582,138 @@ void k_w4a4_gemm(Params p) {
   }
 }
 
+// ---- Small M (decode) ------------------------------------------------------
+// With few tokens the 128 x 128 tiling leaves most CUs idle (LLaMA-2-70B w2 at
+// M = 1: 64 tiles for 256 CUs, each walking all of K) and the GEMM is bound by
+// streaming W. This path gives each workgroup one 32 x 32 output tile (one
+// MFMA block) and splits K between its NW waves in whole groups: wave w
+// takes groups [G w / NW, G (w + 1) / NW). Eight waves when the launch has
+// fewer than 512 workgroups (more loads in flight per CU), else four. Operands go straight from memory into
+// registers (W is read once, A stays in L2) through an 8-step ring of loads in
+// flight, are widened there, and run through the same FP6 MFMA, partials and
+// epilogue arithmetic as the tiled kernel. The four waves' accumulators are
+// summed through LDS in a fixed order (wave 0, then 1, 2, ...): deterministic.
+constexpr int SM_TILE = 32;
+
+constexpr int SM_RING = 8;          // 64-k steps in flight per wave
+
+// 32 packed codes (16 B = two units X0 Y0 X1 Y1) -> the lane's FP6 operand in
+// registers: the words unpack_store() writes to LDS, main part then tail.
+__device__ __forceinline__ v8i widen(uint4 v) {
+  const v4i lo = v4i{(int)(v.x & ~kFoldX), (int)((v.x & kFoldX) | (v.y & kFoldY)),
+                     (int)(v.y & ~kFoldY), (int)(v.z & ~kFoldX)};
+  const v4i hi = v4i{(int)((v.z & kFoldX) | (v.w & kFoldY)), (int)(v.w & ~kFoldY), 0, 0};
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+
+template <bool PARTIALS, bool ROWA, int SM_WAVES>
+__global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_gemm_small(Params p, int steps_per_group) {
+  __shared__ float red[SM_WAVES - 1][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int tile_m = (p.tile_m0 + (int)blockIdx.x % p.tiles_m) * SM_TILE;
+  const int tile_n = (p.tile_n0 + (int)blockIdx.x / p.tiles_m) * SM_TILE;
+  const int row_bytes = p.K >> 1;
+  const int a_rows = min(SM_TILE, p.M - tile_m), w_rows = min(SM_TILE, p.N - tile_n);
+  // rows past the matrix lie past the resources and read as zero codes / scales
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
+  const int voff = l32 * row_bytes + 16 * lhi;        // row l32, 32-code chunk lhi of a 64-k step
+  const int groups = p.K / (64 * steps_per_group);
+  const int h0 = groups * wave / SM_WAVES * steps_per_group;
+  const int h1 = groups * (wave + 1) / SM_WAVES * steps_per_group;
+
+  struct Step {
+    uint4 a, w;
+    float sa, sw;
+  };
+  // operands of 64-k step h and the scales of its group's column
+  auto load = [&](Step& st, int h) {
+    st.a = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rA, voff, h * 32, 0));
+    st.w = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, voff, h * 32, 0));
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.sa + (int64_t)(h >> p.sha) * p.M + tile_m, 4 * a_rows);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.sw + (int64_t)(h >> p.shw) * p.N + tile_n, 4 * w_rows);
+    st.sa = ROWA ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, 4 * l32, 0, 0));
+    st.sw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * l32, 0, 0));
+  };
+
+  const v16f zero16 = {};
+  const v32f zero32 = {};
+  v16f acc = zero16, P = zero16;
+  int in_group = 0;
+  Step ring[SM_RING];
+#pragma unroll
+  for (int u = 0; u < SM_RING; ++u)
+    if (h0 + u < h1) load(ring[u], h0 + u);
+  for (int h = h0; h < h1; h += SM_RING) {
+#pragma unroll
+    for (int u = 0; u < SM_RING; ++u) {
+      if (h + u < h1) {
+        P = mma(widen(ring[u].a), widen(ring[u].w), P);
+        if (++in_group == steps_per_group) {
+          in_group = 0;
+          if constexpr (PARTIALS) {
+            const int gidx = (h + u) / steps_per_group;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = tile_m + 8 * (r >> 2) + 4 * lhi + (r & 3);
+              const int n = tile_n + l32;
+              if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)
+                p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = (int32_t)P[r];
+            }
+          } else if constexpr (ROWA) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf(P[r], ring[u].sw, acc[r]);
+          } else {
+            // s_a x s_w for the tile: block 0 of the two-block rank-1 product
+            const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(ring[u].sa, ring[u].sw, zero32, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = fmaf(P[r], t[r], acc[r]);
+          }
+          P = zero16;
+        }
+        if (h + SM_RING + u < h1) load(ring[u], h + SM_RING + u);
+      }
+    }
+  }
+  if constexpr (!PARTIALS) {
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave - 1][r][lane] = acc[r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < SM_WAVES - 1; ++w)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += red[w][r][lane];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tile_m + 8 * (r >> 2) + 4 * lhi + (r & 3);
+        const int n = tile_n + l32;
+        if (m < p.M && n < p.N) {
+          const float v = ROWA ? acc[r] * p.sa[m] : acc[r];   // one group: xs[m]
+          if (p.ydtype == 0)
+            static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = v;
+          else
+            static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(v);
+        }
+      }
+    }
+  }
+}
+
+template <int NW>
+void launch_small(const GemmArgs& g, const Params& p, dim3 grid, int spg, hipStream_t stream) {
+  if (g.partials)
+    hipLaunchKernelGGL((k_w4a4_gemm_small<true, false, NW>), grid, dim3(64 * NW), 0, stream, p, spg);
+  else if (g.ga == g.K)
+    hipLaunchKernelGGL((k_w4a4_gemm_small<false, true, NW>), grid, dim3(64 * NW), 0, stream, p, spg);
+  else
+    hipLaunchKernelGGL((k_w4a4_gemm_small<false, false, NW>), grid, dim3(64 * NW), 0, stream, p, spg);
+}
+
 // log2(group / 64) for a power-of-two group, 31 (a single column) for group == K.
 int scale_shift(int64_t group, int64_t K) {
   if (group == K && (group & (group - 1))) return 31;
@@ -625,6 +757,24 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.n0 = (int)g.n0;
   p.nc = (int)g.nc;
   p.partials = g.partials;
+  // Few tokens: the small-M path (32 x 32 tiles, K split between the waves of
+  // a workgroup) when M <= 32, or M <= 64 and the 128 x 128 grid would hold
+  // fewer than 128 tiles (measured crossovers on the LLaMA-2-70B FFN shapes).
+  const int64_t big_tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  if (g.M <= 32 || (g.M <= 64 && big_tiles < 128)) {
+    p.tile_m0 = (int)(g.m0 / SM_TILE);
+    p.tile_n0 = (int)(g.n0 / SM_TILE);
+    p.tiles_m = (int)((g.m0 + g.mc - 1) / SM_TILE) - p.tile_m0 + 1;
+    p.tiles_n = (int)((g.n0 + g.nc - 1) / SM_TILE) - p.tile_n0 + 1;
+    const int nwg = p.tiles_m * p.tiles_n;
+    const dim3 grid((unsigned)nwg);
+    const int spg = (int)(gmin / 64);
+    if (nwg < 512)
+      launch_small<8>(g, p, grid, spg, stream);
+    else
+      launch_small<4>(g, p, grid, spg, stream);
+    return;
+  }
   p.tile_m0 = (int)(g.m0 / BM);
   p.tile_n0 = (int)(g.n0 / BN);
   p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;

@@ -39,11 +39,14 @@ WORKLOADS = {
     "llama2_7b_ffn": (2048, [(4096, 11008), (4096, 11008), (11008, 4096)], 128, 128, "int4"),
     "granularity": (4096, [(8192, 8192)], 128, 128, "int4"),
     "qwen25_7b_mxfp4_ffn": (4096, [(3584, 18944), (3584, 18944), (18944, 3584)], 32, 32, "mxfp4"),
+    # two-pass MXFP4 with the residual appended along K (the GEMM runs K' = 2K)
+    "qwen25_7b_mxfp4_residual_ffn": (4096, [(3584, 18944), (3584, 18944), (18944, 3584)], 32, 32, "mxfp4res"),
 }
 
 
 GEMM_SOURCES = {"int4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_w4a4.hip",
-                "mxfp4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip"}
+                "mxfp4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip",
+                "mxfp4res": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip"}
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -99,10 +102,15 @@ def quant_standalone(shapes, ga, fmt, reps: int = 24, nrot: int = 6):
             sc = torch.empty((K // ga, M), dtype=torch.float32, device=dev)
             call = lambda x: ops.w4a4_quantize_act(x, ga, out=(xq, sc))
             nbytes = M * (2 * K + K // 2 + 4 * (K // ga))
-        else:
+        elif fmt == "mxfp4":
             sc = torch.empty((M * (K // 32),), dtype=torch.uint8, device=dev)
             call = lambda x: ops.mxfp4_quantize(x, out=(xq, sc))
             nbytes = M * (2 * K + K // 2 + K // 32)
+        else:
+            xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M * (2 * K // 32),), dtype=torch.uint8, device=dev)
+            call = lambda x: ops.mxfp4_quantize_residual(x, out=(xq, sc))
+            nbytes = M * (2 * K + K + 2 * K // 32)
         for i in range(nrot):
             call(xs[i])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -137,7 +145,12 @@ def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
         cols = synth.sample_rows(N, min(n_cols, N), seed=12 + li)
         x = synth.activations(M, K, dist="t3", seed=li, rows=rows)
         w = synth.weights(N, K, seed=100 + li, rows=cols)
-        wpk = oracle.int4_quantize(w, gw) if fmt == "int4" else oracle.mxfp4_quantize(w)  # offline, untimed
+        if fmt == "int4":  # weights offline, untimed
+            wpk = oracle.int4_quantize(w, gw)
+        elif fmt == "mxfp4":
+            wpk = oracle.mxfp4_quantize(w)
+        else:
+            wpk = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w))
         work.append((x, wpk, K, len(cols)))
     ops = 0
     t0 = time.perf_counter()
@@ -146,7 +159,7 @@ def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
             qa, sa = oracle.int4_quantize(x, ga)
             oracle.w4a4_gemm(qa, sa, ga, wpk[0], wpk[1], gw)
         else:
-            ca, ea = oracle.mxfp4_quantize(x)
+            ca, ea = oracle.mxfp4_quantize(x) if fmt == "mxfp4" else oracle.mxfp4_quantize_residual(x)
             oracle.mxfp4_gemm(ca, ea, wpk[0], wpk[1])
         ops += 2 * len(rows) * nc * K
     dt = time.perf_counter() - t0
@@ -213,10 +226,14 @@ def main() -> int:
             wq, ws = ops.w4a4_pack_weight(w, gw)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             xs = torch.empty((K // ga, M), dtype=torch.float32, device=dev)
-        else:
+        elif fmt == "mxfp4":
             wq, ws = ops.mxfp4_quantize(w)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             xs = torch.empty((M * (K // 32),), dtype=torch.uint8, device=dev)
+        else:
+            wq, ws = ops.mxfp4_quantize_append_copy(w)
+            xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M * (2 * K // 32),), dtype=torch.uint8, device=dev)
         del w
         y = torch.empty((M, N), dtype=ydt, device=dev)
         layers.append(dict(K=K, N=N, x=x, wq=wq, ws=ws, xq=xq, xs=xs, y=y))
@@ -229,8 +246,10 @@ def main() -> int:
                 ev[li][0].record()
             if fmt == "int4":
                 ops.w4a4_quantize_act(L["x"], ga, out=(L["xq"], L["xs"]))
-            else:
+            elif fmt == "mxfp4":
                 ops.mxfp4_quantize(L["x"], out=(L["xq"], L["xs"]))
+            else:
+                ops.mxfp4_quantize_residual(L["x"], out=(L["xq"], L["xs"]))
             if ev is not None:
                 ev[li][1].record()
             if fmt == "int4":
@@ -268,21 +287,22 @@ def main() -> int:
             e = evs[s][li]
             quant_s[li] += e[0].elapsed_time(e[1]) / 1e3
             gemm_s[li] += e[1].elapsed_time(e[2]) / 1e3
-    gemm_ops = sum(2 * M * L["N"] * L["K"] for L in layers) * args.steps
+    kmul = 2 if fmt == "mxfp4res" else 1     # the appended-residual GEMM runs K' = 2K
+    gemm_ops = sum(2 * M * L["N"] * kmul * L["K"] for L in layers) * args.steps
     achieved = gemm_ops / gemm_s.sum() / 1e12
     peak = PEAK_INT8_TOPS if fmt == "int4" else PEAK_FP4_TFLOPS
     ybytes = 4 if ydt == torch.float32 else 2
     quant_bytes = 0
     for L in layers:
-        sbytes = 4 * (L["K"] // ga) if fmt == "int4" else L["K"] // 32
-        quant_bytes += M * (2 * L["K"] + L["K"] // 2 + sbytes)
+        sbytes = 4 * (L["K"] // ga) if fmt == "int4" else kmul * L["K"] // 32
+        quant_bytes += M * (2 * L["K"] + kmul * L["K"] // 2 + sbytes)
     quant_gbs = quant_bytes * args.steps / quant_s.sum() / 1e9
     per_linear = []
     for li, L in enumerate(layers):
         per_linear.append({
             "K": L["K"], "N": L["N"],
             "gemm_us": gemm_s[li] / args.steps * 1e6,
-            "gemm_tops": 2 * M * L["N"] * L["K"] / (gemm_s[li] / args.steps) / 1e12,
+            "gemm_tops": 2 * M * L["N"] * kmul * L["K"] / (gemm_s[li] / args.steps) / 1e12,
             "quant_us": quant_s[li] / args.steps * 1e6,
         })
 
@@ -290,7 +310,10 @@ def main() -> int:
     log(f"standalone act-quant: {q_gbs:.0f} GB/s")
 
     result = {
-        "metric": METRIC if args.workload == "llama2_70b_ffn" else f"{fmt} GEMM TOPS incl. act-quant, {args.workload}",
+        "metric": (METRIC if args.workload == "llama2_70b_ffn"
+                   else f"{fmt} GEMM TOPS incl. act-quant, {args.workload}" if fmt != "mxfp4res"
+                   else f"effective TOPS (2*M*N*K of the layers) of two-pass MXFP4 with the residual appended "
+                        f"along K, incl. act-quant, {args.workload}"),
         "value": value,
         "unit": "TOPS",
         "n_gpus": 1,

@@ -161,6 +161,35 @@ w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx
                              uint8_t* q, uint8_t* e8m0, void* stream);
 
 /*
+ * Two-pass MXFP4 of the rows of X with the residual pass appended along K:
+ * the activation side of the appended-residual GEMM (Multi-Scale Dequant and
+ * ARCQuant abstracts, APEX4 page: the activation is split into low-precision
+ * components, the residual component appended as extra reduction channels so
+ * one standard block-scaled GEMM computes both terms). Output = the MXFP4
+ * quantization (rule and layouts above) of the K' = 2K wide matrix
+ * [x | r], where r = x - deq(Q(x)) is the exact residual of the first pass
+ * and each half is quantized by the rule above with its own block scales:
+ *
+ *   x, K, ldx  as for mxfp4_quantize
+ *   q     out: u8 [rows][K] (2K packed E2M1 codes: Q(x) then Q(r)), 4-byte aligned
+ *   e8m0  out: u8, rows * 2K/32 scale bytes in the panel layout of a 2K-wide
+ *         matrix (block b of Q(x) is block b, block b of Q(r) is block K/32 + b)
+ *
+ * mxfp4_gemm(q, e8m0, wq, we, M, N, 2K, ...) with W from
+ * mxfp4_quantize_append_copy then gives Q(x) Q(w)^T + Q(r) Q(w)^T.
+ */
+w4a4_status_t mxfp4_quantize_residual(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                      uint8_t* q, uint8_t* e8m0, void* stream);
+
+/*
+ * The weight side of the appended-residual GEMM: the MXFP4 quantization of
+ * the rows of W written twice along K, [Q(w) | Q(w)] (shapes and layouts as
+ * for mxfp4_quantize_residual, K' = 2K). Offline, like weight packing.
+ */
+w4a4_status_t mxfp4_quantize_append_copy(const void* w, int64_t rows, int64_t K, int64_t ldw,
+                                         uint8_t* q, uint8_t* e8m0, void* stream);
+
+/*
  * MXFP4 GEMM on the matrix cores' block-scaled FP4 path:
  *   Y[m,n] = sum_b 2^(Ea[m,b] + Ew[n,b]) * sum_{k in block b} va[m,k] * vw[n,k]
  * accumulated in fp32.

@@ -31,6 +31,8 @@ from .mxfp4 import (  # noqa: F401
     E2M1_VALUES,
     e2m1_decode,
     mxfp4_quantize,
+    mxfp4_quantize_residual,
+    mxfp4_append_copy,
     mxfp4_dequantize,
     mxfp4_block_partials,
     mxfp4_gemm,

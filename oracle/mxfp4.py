@@ -52,6 +52,25 @@ def _round_to_e2m1_index(m: np.ndarray) -> np.ndarray:
     return np.where(pick_hi, hi, lo).astype(np.int64)
 
 
+def _mx_rule(xf: np.ndarray):
+    """The OCP MX block rule above on finite float64 values [R, K] (K % 32 == 0).
+
+    Returns ``(codes, e8m0)``: codes uint8 [R, K] holding 0..15, scale bytes
+    uint8 [R, K/32].
+    """
+    R, K = xf.shape
+    xb = xf.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    a = np.abs(xb).max(axis=2)
+    _, e = np.frexp(a)                                   # a = f * 2^e, f in [0.5, 1)
+    E = np.where(a > 0, (e - 1) - E2M1_EMAX, -E8M0_BIAS)  # floor(log2 a) - 2
+    E = np.clip(E, -E8M0_BIAS, E8M0_BIAS).astype(np.int64)
+    v = np.ldexp(xb, -E[:, :, None])                     # exact scaling by 2^-E
+    idx = _round_to_e2m1_index(np.abs(v))
+    sign = np.signbit(xb).astype(np.int64)
+    codes = (sign << 3) | idx
+    return codes.reshape(R, K).astype(np.uint8), (E + E8M0_BIAS).astype(np.uint8)
+
+
 def mxfp4_quantize(x: np.ndarray):
     """MXFP4-quantize each row in blocks of 32 along K.
 
@@ -67,16 +86,36 @@ def mxfp4_quantize(x: np.ndarray):
     xf = x.astype(np.float64)                            # exact
     if not np.isfinite(xf).all():
         raise ValueError("NaN/Inf inputs are outside the quantizer's contract")
-    xb = xf.reshape(R, K // MX_BLOCK, MX_BLOCK)
-    a = np.abs(xb).max(axis=2)
-    _, e = np.frexp(a)                                   # a = f * 2^e, f in [0.5, 1)
-    E = np.where(a > 0, (e - 1) - E2M1_EMAX, -E8M0_BIAS)  # floor(log2 a) - 2
-    E = np.clip(E, -E8M0_BIAS, E8M0_BIAS).astype(np.int64)
-    v = np.ldexp(xb, -E[:, :, None])                     # exact scaling by 2^-E
-    idx = _round_to_e2m1_index(np.abs(v))
-    sign = np.signbit(xb).astype(np.int64)
-    codes = (sign << 3) | idx
-    return codes.reshape(R, K).astype(np.uint8), (E + E8M0_BIAS).astype(np.uint8)
+    return _mx_rule(xf)
+
+
+def mxfp4_quantize_residual(x: np.ndarray):
+    """Two-pass MXFP4 with the residual pass appended along K.
+
+    Multi-Scale Dequant abstract (APEX4 page): the high-precision activation is
+    decomposed into several low-precision components, each multiplied with the
+    quantized weights by the native GEMM; for MXFP4 two passes. ARCQuant
+    abstract (same page): the quantized residual is appended to the activation
+    as extra channels of the reduction dimension, so one standard GEMM computes
+    both terms. The pages give only these abstracts; reading taken here (the
+    plainest): the second pass is the same MX rule applied to the exact residual
+    ``R = x - deq(Q(x))``, with its own per-block scale. ``R`` is exact in
+    float64 (and in binary32: it needs at most 16 significant bits).
+
+    Returns ``(codes, e8m0)`` of the augmented activation: codes uint8
+    [R, 2K] = [Q(x) | Q(R)], scale bytes uint8 [R, 2K/32].
+    """
+    c1, e1 = mxfp4_quantize(x)
+    r = np.asarray(x).astype(np.float64) - mxfp4_dequantize(c1, e1)
+    c2, e2 = _mx_rule(r)
+    return np.concatenate([c1, c2], axis=1), np.concatenate([e1, e2], axis=1)
+
+
+def mxfp4_append_copy(codes: np.ndarray, e8m0: np.ndarray):
+    """The weight side of the appended-residual GEMM: each row's codes and
+    scales twice along K, so that [Q(x) | Q(R)] @ [Q(w) | Q(w)]^T =
+    Q(x) Q(w)^T + Q(R) Q(w)^T."""
+    return np.concatenate([codes, codes], axis=1), np.concatenate([e8m0, e8m0], axis=1)
 
 
 def mxfp4_dequantize(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:

@@ -118,6 +118,13 @@ def test_mxfp4_validation(lib):
     assert mq(P, 4, 64, 68, P, P, None) == E_ALIGN
     assert mq(P, 0, 64, 64, None, None, None) == OK
     assert mq(None, 4, 64, 64, P, P, None) == E_NULL
+    for fn in ("mxfp4_quantize_residual", "mxfp4_quantize_append_copy"):
+        r = lambda *a: _lib.status_of(fn, *a)
+        assert r(P, 4, 48, 48, P, P, None) == E_SHAPE
+        assert r(P, 4, 64, 68, P, P, None) == E_ALIGN
+        assert r(P, 0, 64, 64, None, None, None) == OK
+        assert r(P, 4, 64, 64, None, P, None) == E_NULL
+        assert r(P, 4, 64, 64, P + 2, P, None) == E_ALIGN
     mg = lambda *a: _lib.status_of("mxfp4_gemm", *a)
     assert mg(P, P, P, P, 4, 4, 96, P, 0, 4, None) == E_SHAPE
     assert mg(P, P, P, P, 4, 4, 128, P, 2, 4, None) == E_DTYPE

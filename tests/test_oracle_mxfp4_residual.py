@@ -1,0 +1,87 @@
+"""Pins for the two-pass MXFP4 oracle with the residual appended along K (CPU
+only): a block worked by hand from the OCP MX rule, grid-aligned inputs (zero
+residual), the per-element error bound of the second pass, "two passes never
+worse than one", and the appended GEMM against the sum of two plain GEMMs."""
+import numpy as np
+
+import oracle
+from w4a4_quantized_gemm_quantize_amd import synth
+
+
+def test_worked_block():
+    """One 32-block worked by hand. First pass: absmax 7 gives E = floor(log2 7)
+    - 2 = 0; 7 saturates to 6 (code 7), fp16(0.3) = 0.2998046875 rounds to 0.5
+    (code 1), fp16(-2.6) = -2.599609375 to -3 (code 8|5), -0 keeps its sign
+    (code 8), 5 is a tie between 4 and 6 and goes to the even code 4 (code 6).
+    Residual: 1, -0.2001953125, 0.400390625, +0 (-0 - -0), 1, zeros; absmax 1
+    gives E2 = -2, so the second pass rounds 4r: 4 (code 6), -0.80078125 to -1
+    (code 8|2), 1.6015625 to 1.5 (code 3), 0, 4 (code 6)."""
+    x = np.zeros((1, 32), np.float16)
+    x[0, :5] = [7.0, 0.3, -2.6, -0.0, 5.0]
+    codes, e8 = oracle.mxfp4_quantize_residual(x)
+    assert codes.shape == (1, 64) and e8.shape == (1, 2)
+    assert list(codes[0, :5]) == [7, 1, 13, 8, 6] and not codes[0, 5:32].any()
+    assert list(codes[0, 32:37]) == [6, 10, 3, 0, 6] and not codes[0, 37:].any()
+    assert list(e8[0]) == [127, 125]
+    deq = oracle.mxfp4_dequantize(codes, e8)
+    rec = deq[:, :32] + deq[:, 32:]
+    assert list(rec[0, :5]) == [7.0, 0.25, -2.625, 0.0, 5.0]
+
+
+def test_grid_aligned_input_has_zero_residual():
+    """x already on the MXFP4 grid of its block: the second pass sees r = 0
+    everywhere (codes 0, scale byte 0) and the first pass is x itself."""
+    rng = np.random.default_rng(0)
+    R, K = 16, 256
+    v = oracle.E2M1_VALUES[rng.integers(0, 8, (R, K))] * rng.choice([-1, 1], (R, K))
+    v[:, ::32] = 6.0                                    # absmax 6: E = 0 + e
+    E = rng.integers(-10, 5, (R, K // 32))
+    x = np.ldexp(v, np.repeat(E, 32, axis=1)).astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), np.ldexp(v, np.repeat(E, 32, axis=1)))
+    codes, e8 = oracle.mxfp4_quantize_residual(x)
+    assert not codes[:, K:].any() and not e8[:, K // 32:].any()
+    assert np.array_equal(oracle.mxfp4_dequantize(codes[:, :K], e8[:, :K // 32]), x.astype(np.float64))
+
+
+def _two_pass(x):
+    codes, e8 = oracle.mxfp4_quantize_residual(x)
+    K = x.shape[1]
+    d = oracle.mxfp4_dequantize(codes, e8)
+    return d[:, :K], d[:, K:], e8[:, K // 32:].astype(np.int64) - 127
+
+
+def test_second_pass_error_bound_and_monotone():
+    """Per element, |x - deq1 - deq2| <= 2^(E2 + 1) (the largest E2M1 rounding
+    step is 2 between 4 and 6; values in [6, 8) saturate to 6, also at most
+    2 away), and never more than the first pass alone left (0 is on the grid,
+    so the nearest point is never farther than |r|)."""
+    for seed, dist in ((0, "t3"), (1, "normal")):
+        x = synth.activations(64, 1024, dist=dist, seed=seed)
+        d1, d2, E2 = _two_pass(x)
+        xf = x.astype(np.float64)
+        err1 = np.abs(xf - d1)
+        err2 = np.abs(xf - d1 - d2)
+        bound = np.repeat(np.ldexp(1.0, E2 + 1), 32, axis=1)
+        assert np.all(err2 <= bound)
+        assert np.all(err2 <= err1)
+        assert err2.max() > 0.25 * bound.max() or err2.max() == 0  # the bound is not vacuous
+
+
+def test_appended_gemm_is_the_sum_of_two_gemms():
+    """[Q(x) | Q(r)] @ [Q(w) | Q(w)]^T = Q(x) Q(w)^T + Q(r) Q(w)^T (linearity of
+    the block sum); each side's terms are exact, so the two float64 sums agree
+    to rounding of the accumulation order."""
+    x = synth.activations(12, 512, dist="t3", seed=3)
+    w = synth.weights(20, 512, seed=4)
+    ca, ea = oracle.mxfp4_quantize_residual(x)
+    cw, ew = oracle.mxfp4_quantize(w)
+    cw2, ew2 = oracle.mxfp4_append_copy(cw, ew)
+    Y, T = oracle.mxfp4_gemm(ca, ea, cw2, ew2)
+    Y1, _ = oracle.mxfp4_gemm(ca[:, :512], ea[:, :16], cw, ew)
+    Y2, _ = oracle.mxfp4_gemm(ca[:, 512:], ea[:, 16:], cw, ew)
+    assert np.all(np.abs(Y - (Y1 + Y2)) <= 1e-12 * T + 1e-300)
+    # and it is closer to the exact product with the dequantized weights
+    xf = x.astype(np.float64)
+    wd = oracle.mxfp4_dequantize(cw, ew)
+    ref = xf @ wd.T
+    assert np.abs(Y - ref).mean() < 0.5 * np.abs(Y1 - ref).mean()

@@ -7,7 +7,8 @@ re-exported here on first use.
 """
 _OPS = (
     "w4a4_quantize_act", "w4a4_pack_weight", "w4a4_gemm", "w4a4_gemm_debug_partials",
-    "mxfp4_quantize", "mxfp4_gemm", "mxfp4_gemm_debug_partials",
+    "mxfp4_quantize", "mxfp4_quantize_residual", "mxfp4_quantize_append_copy",
+    "mxfp4_gemm", "mxfp4_gemm_debug_partials",
 )
 
 

@@ -135,15 +135,30 @@ w4a4_status_t w4a4_gemm_debug_partials(const uint8_t* xq, const float* xs, int32
   return launched();
 }
 
-w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
-                             uint8_t* q, uint8_t* e8m0, void* stream) {
+static w4a4_status_t mx_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                              uint8_t* q, uint8_t* e8m0, int mode, void* stream) {
   if (rows < 0 || K <= 0 || K % 32 || ldx < K) return W4A4_E_SHAPE;
   if (ldx % 8) return W4A4_E_ALIGN;
   if (rows == 0) return W4A4_OK;
   if (!x || !q || !e8m0) return W4A4_E_NULL;
   if (!aligned(x, 16) || !aligned(q, 4)) return W4A4_E_ALIGN;
-  w4a4::launch_mxfp4_quant(x, rows, K, ldx, q, e8m0, as_stream(stream));
+  w4a4::launch_mxfp4_quant(x, rows, K, ldx, q, e8m0, mode, as_stream(stream));
   return launched();
+}
+
+w4a4_status_t mxfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                             uint8_t* q, uint8_t* e8m0, void* stream) {
+  return mx_quant(x, rows, K, ldx, q, e8m0, 0, stream);
+}
+
+w4a4_status_t mxfp4_quantize_residual(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                      uint8_t* q, uint8_t* e8m0, void* stream) {
+  return mx_quant(x, rows, K, ldx, q, e8m0, 1, stream);
+}
+
+w4a4_status_t mxfp4_quantize_append_copy(const void* w, int64_t rows, int64_t K, int64_t ldw,
+                                         uint8_t* q, uint8_t* e8m0, void* stream) {
+  return mx_quant(w, rows, K, ldw, q, e8m0, 2, stream);
 }
 
 static w4a4_status_t mx_common(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq, const uint8_t* we,

@@ -10,8 +10,10 @@ namespace w4a4 {
 void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int group,
                        uint8_t* q, float* s, hipStream_t stream);
 
+// mode 0: MXFP4 codes of x; 1: [Q(x) | Q(x - deq Q(x))] along K (width 2K);
+// 2: [Q(x) | Q(x)] (width 2K)
 void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
-                        uint8_t* q, uint8_t* e8m0, hipStream_t stream);
+                        uint8_t* q, uint8_t* e8m0, int mode, hipStream_t stream);
 
 // Window [m0, m0+mc) x [n0, n0+nc); for the plain GEMM the window is the whole
 // output and partials == nullptr.

@@ -262,22 +262,79 @@ __device__ __forceinline__ uint4 e2m1_codes32(const uint32_t w[16], float d) {
   return uint4{o[0], o[1], o[2], o[3]};
 }
 
+// Offset of the scale byte of (row, block b) in the panel layout of a matrix
+// whose rows hold nbo blocks: panel b / 8, rows of pw = min(8, blocks left)
+// bytes, the even blocks' bytes first.
+__device__ __forceinline__ int64_t panel_offset(int rows, int nbo, int row, int b) {
+  const int pq = b >> 3, pw = min(8, nbo - 8 * pq), j = b & 7;
+  const int pos = (j & 1) ? ((pw + 1) >> 1) + (j >> 1) : (j >> 1);
+  return (int64_t)8 * rows * pq + (int64_t)row * pw + pos;
+}
+
+// Output modes of the MXFP4 quantizer. APPEND_RESIDUAL and APPEND_COPY write a
+// matrix twice as wide along K (2 nb blocks per row): block b and, at b + nb,
+// the MX quantization of the residual x - deq(Q(x)) (the activation side of
+// the appended-residual GEMM), or a copy of Q(x) (its weight side).
+enum { MX_PLAIN = 0, MX_APPEND_RESIDUAL = 1, MX_APPEND_COPY = 2 };
+
+// E2M1 codes of 32 fp32 values already divided by their block scale (exact
+// power-of-two scaling), two per instruction with unit scale: the same
+// rounding as e2m1_codes32.
+__device__ __forceinline__ uint4 e2m1_codes32_f32(const float v[32]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j], v[8 * j + 1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 2], v[8 * j + 3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 4], v[8 * j + 5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 6], v[8 * j + 7], 1.0f, 3);
+    o[j] = w;
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
+// The E2M1 values (unit scale) of the 8 codes of a word, element 2i from the
+// low nibble of byte i.
+__device__ __forceinline__ void e2m1_values8(uint32_t w, float v[8]) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+  v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+}
+
+// Block exponent E = floor(log2 a) - 2 of a block with absmax a (a is 0 or a
+// normal fp32, so its biased exponent field is floor(log2 a) + 127), -127 for
+// an all-zero block.
+__device__ __forceinline__ int block_exponent(float a) {
+  const int biased = (int)((__float_as_uint(a) >> 23) & 0xFF);
+  return (a == 0.0f) ? -127 : biased - 127 - 2;
+}
+
 // Lane tile: a lane takes one 32-element block of a row (absmax within the
 // lane); a wave covers 8 rows x the 8 blocks of one 256-k panel, the block's
 // four waves the next panels of the same rows, blockIdx.x walking along the
 // rows. A wave's 64 scale bytes are then one contiguous run of the panel
 // layout (8 rows x w_p bytes). Row blocks beyond gridDim.y are looped.
 // q16: the code array is 16-byte aligned (one store per lane).
+template <int MODE>
 __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
     const uint16_t* __restrict__ x, int64_t ldx, int rows, int nb, int q16,
     uint32_t* __restrict__ q, uint8_t* __restrict__ e8m0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = (blockIdx.x * 4 + wave) * 8 + (lane & 7);     // block of the row
   if (b >= nb) return;
-  // panel layout: block b goes to panel b / 8, whose rows hold pw = min(8,
-  // blocks left) bytes each, the even blocks' bytes first
-  const int pq = b >> 3, pw = min(8, nb - 8 * pq), j = b & 7;
-  const int pos = (j & 1) ? ((pw + 1) >> 1) + (j >> 1) : (j >> 1);
+  const int nbo = MODE == MX_PLAIN ? nb : 2 * nb;              // blocks per output row
+  auto store_codes = [&](int row, int bo, uint4 c) {
+    const int64_t unit = (int64_t)row * nbo + bo;             // 16-byte code unit
+    if (q16) {
+      reinterpret_cast<uint4*>(q)[unit] = c;
+    } else {
+      q[4 * unit] = c.x; q[4 * unit + 1] = c.y; q[4 * unit + 2] = c.z; q[4 * unit + 3] = c.w;
+    }
+  };
   for (int rb = blockIdx.y; rb * 8 < rows; rb += gridDim.y) {
     const int row = rb * 8 + (lane >> 3);
     if (row >= rows) break;                  // the last row block only
@@ -288,19 +345,39 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
     uint32_t w[16];
     words16(raw, w);
     const float a = absmax_words<16>(w);
-    // a is 0 or a normal fp32 (fp16 values widen to normal fp32), so its
-    // biased exponent field is floor(log2 a) + 127; E = floor(log2 a) - 2.
-    const int biased = (int)((__float_as_uint(a) >> 23) & 0xFF);
-    const int E = (a == 0.0f) ? -127 : biased - 127 - 2;
-    const float d = (a == 0.0f) ? 1.0f : __uint_as_float((uint32_t)(biased - 2) << 23);   // 2^E, normal
+    const int E = block_exponent(a);
+    const float d = (a == 0.0f) ? 1.0f : __uint_as_float((uint32_t)(E + 127) << 23);   // 2^E, normal
     const uint4 c = e2m1_codes32(w, d);
-    const int64_t unit = (int64_t)row * nb + b;          // 16-byte code unit
-    if (q16) {
-      reinterpret_cast<uint4*>(q)[unit] = c;
-    } else {
-      q[4 * unit] = c.x; q[4 * unit + 1] = c.y; q[4 * unit + 2] = c.z; q[4 * unit + 3] = c.w;
+    store_codes(row, b, c);
+    e8m0[panel_offset(rows, nbo, row, b)] = (uint8_t)(E + 127);
+    if constexpr (MODE == MX_APPEND_COPY) {
+      store_codes(row, nb + b, c);
+      e8m0[panel_offset(rows, nbo, row, nb + b)] = (uint8_t)(E + 127);
+    } else if constexpr (MODE == MX_APPEND_RESIDUAL) {
+      // r = x - deq(Q(x)), exact in fp32 (at most 16 significant bits); the
+      // E2M1 value of each code comes back from the reverse conversion
+      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+      float r[32];
+      float ar = 0.0f;
+#pragma unroll
+      for (int jw = 0; jw < 4; ++jw) {
+        float v[8];
+        e2m1_values8(cw[jw], v);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const int k = 8 * jw + i;
+          const h2 xx = __builtin_bit_cast(h2, w[k >> 1]);
+          r[k] = (float)xx.x - v[i] * d;
+          r[k + 1] = (float)xx.y - v[i + 1] * d;
+          ar = fmaxf(ar, fmaxf(fabsf(r[k]), fabsf(r[k + 1])));
+        }
+      }
+      const int E2 = block_exponent(ar);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) r[k] = ldexpf(r[k], -E2);   // exact
+      store_codes(row, nb + b, e2m1_codes32_f32(r));
+      e8m0[panel_offset(rows, nbo, row, nb + b)] = (uint8_t)(E2 + 127);
     }
-    e8m0[(int64_t)8 * rows * pq + (int64_t)row * pw + pos] = (uint8_t)(E + 127);
   }
 }
 
@@ -330,13 +407,26 @@ void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int gro
 }
 
 void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
-                        uint8_t* q, uint8_t* e8m0, hipStream_t stream) {
+                        uint8_t* q, uint8_t* e8m0, int mode, hipStream_t stream) {
   const int nb = (int)(K / 32);
   const dim3 grid((unsigned)((nb + 31) / 32), (unsigned)std::min<int64_t>((rows + 7) / 8, kMaxGridY));
   const int q16 = (reinterpret_cast<uintptr_t>(q) & 15) == 0;
-  hipLaunchKernelGGL(k_mxfp4_quant, grid, dim3(kQuantThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), ldx, (int)rows, nb, q16,
-                     reinterpret_cast<uint32_t*>(q), e8m0);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  uint32_t* qp = reinterpret_cast<uint32_t*>(q);
+  switch (mode) {
+    case MX_APPEND_RESIDUAL:
+      hipLaunchKernelGGL(k_mxfp4_quant<MX_APPEND_RESIDUAL>, grid, dim3(kQuantThreads), 0, stream,
+                         xp, ldx, (int)rows, nb, q16, qp, e8m0);
+      return;
+    case MX_APPEND_COPY:
+      hipLaunchKernelGGL(k_mxfp4_quant<MX_APPEND_COPY>, grid, dim3(kQuantThreads), 0, stream,
+                         xp, ldx, (int)rows, nb, q16, qp, e8m0);
+      return;
+    default:
+      hipLaunchKernelGGL(k_mxfp4_quant<MX_PLAIN>, grid, dim3(kQuantThreads), 0, stream,
+                         xp, ldx, (int)rows, nb, q16, qp, e8m0);
+      return;
+  }
 }
 
 }  // namespace w4a4

@@ -157,6 +157,35 @@ def mxfp4_quantize(x: torch.Tensor, out=None):
     return q, e
 
 
+def _mxfp4_quantize_wide(fn: str, x: torch.Tensor, out):
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    R, K = x.shape
+    if out is None:
+        q = torch.empty((R, K), dtype=torch.uint8, device=x.device)
+        e = torch.empty((R * (2 * K // 32),), dtype=torch.uint8, device=x.device)
+    else:
+        q, e = out
+    if e.numel() != R * (2 * K // 32) or not e.is_contiguous():
+        raise ValueError("e8m0 must be contiguous with rows*2K/32 bytes")
+    call(fn, x.data_ptr(), R, K, x.stride(0), q.data_ptr(), e.data_ptr(), _stream(x))
+    return q, e
+
+
+def mxfp4_quantize_residual(x: torch.Tensor, out=None):
+    """Two-pass MXFP4 with the residual appended along K: ``(codes uint8
+    [rows, K] (2K codes: Q(x) then Q(x - deq Q(x))), e8m0 uint8 [rows*2K/32]
+    in the panel layout of a 2K-wide matrix)``."""
+    return _mxfp4_quantize_wide("mxfp4_quantize_residual", x, out)
+
+
+def mxfp4_quantize_append_copy(w: torch.Tensor, out=None):
+    """``[Q(w) | Q(w)]`` along K (shapes as :func:`mxfp4_quantize_residual`):
+    the weight side of the appended-residual GEMM."""
+    return _mxfp4_quantize_wide("mxfp4_quantize_append_copy", w, out)
+
+
 def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
     """Y[M, N] = block-scaled FP4 GEMM of MXFP4 X and W."""
     for t, n in ((xq, "xq"), (xe, "xe"), (wq, "wq"), (we, "we")):

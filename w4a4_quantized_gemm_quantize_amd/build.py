@@ -27,8 +27,30 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    "-Rpass-analysis=kernel-resource-usage",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+# The debug entry points' kernels (partials export) may spill; production
+# kernels must not: a spill there costs a multiple of the kernel time (the
+# per-token GEMM variant once ran 4x slower on 87 spilled registers).
+def _is_debug_kernel(name: str) -> bool:
+    """A partials-export instantiation: PARTIALS is the first template argument
+    of the INT4 kernels and the last one of the MXFP4 kernel."""
+    return ("11k_w4a4_gemmILb1E" in name or "17k_w4a4_gemm_smallILb1E" in name
+            or ("12k_mxfp4_gemm" in name and name.endswith("Lb1EEEvNS0_6ParamsE")))
+
+
+def _scratch_report(out: str):
+    """(kernel, scratch bytes per lane) pairs from the resource-usage remarks."""
+    res, name = [], None
+    for ln in out.splitlines():
+        if "remark: Function Name:" in ln:
+            name = ln.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in ln and name:
+            res.append((name, int(ln.split("ScratchSize [bytes/lane]:")[1].split()[0])))
+            name = None
+    return res
 
 
 def _hipcc() -> str:
@@ -56,10 +78,18 @@ def build(verbose: bool = False) -> str:
         src, obj = pair
         return _run([hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj])
 
+    spills = []
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         for out in ex.map(compile_one, zip(sources, objs)):
-            if verbose and out.strip():
-                print(out)
+            for name, scratch in _scratch_report(out):
+                if scratch and not _is_debug_kernel(name):
+                    spills.append((name, scratch))
+            warn = "\n".join(ln for ln in out.splitlines() if "remark:" not in ln)
+            if verbose and warn.strip():
+                print(warn)
+    if spills:
+        raise RuntimeError("production kernels use scratch (register spills): "
+                           + ", ".join(f"{n} ({b} B/lane)" for n, b in spills))
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

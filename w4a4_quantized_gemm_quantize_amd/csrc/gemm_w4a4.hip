@@ -428,7 +428,7 @@ void k_w4a4_gemm(Params p) {
       LST_A1((BUF) ^ 1, RS);                                                             \
       CHUNK_END(16);                                                                     \
       GroupScales T0 = TPRODV(gsa_, gsw0_, gsw1_);                                       \
-      asm volatile("" : "+v"(T0.t));                                                    \
+      if constexpr (!ROWA) asm volatile("" : "+v"(T0.t));   /* no product with per-token A scales */ \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       load_w1();                                                                         \
       CHUNK_END(16);                                                                     \
@@ -450,7 +450,7 @@ void k_w4a4_gemm(Params p) {
       LST_S((BUF) ^ 1, RS);                                                              \
       CHUNK_END(16);                                                                     \
       /* keep Tc's MFMA here (it would sink into the next stage) */                     \
-      asm volatile("" : "+v"(Tc.t));                                                    \
+      if constexpr (!ROWA) asm volatile("" : "+v"(Tc.t));   /* no product with per-token A scales */ \
       ++gidx;                                                                            \
     } else if constexpr (MODE == G128) {                                                 \
       const GroupScales T0 = TPROD(BUF, 0, 0);                                           \

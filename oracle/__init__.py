@@ -1,4 +1,4 @@
-"""CPU oracle for W4A4 group-quantized GEMM and the MXFP4 variant.
+"""CPU oracle for W4A4 group-quantized GEMM and the MXFP4 and NVFP4 variants.
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import or run anything in this directory. The
@@ -6,8 +6,9 @@ HIP library never calls it, shares no code with it and must fail loudly, not
 fall back here, when its own build is missing.
 
 The oracle is plain numpy: slow, unfused, obviously correct. Floating point that
-decides an integer (the INT4 codes) is done in IEEE binary32, the precision the
-GPU kernel takes the same decision in; everything else is float64. Each function
+decides an integer (the INT4 codes, the NVFP4 scales and codes) is done in IEEE
+binary32, the precision the GPU kernel takes the same decision in; everything
+else is float64. Each function
 names the passage of the pages it follows and, where the pages are silent,
 states the reading taken.
 
@@ -36,4 +37,13 @@ from .mxfp4 import (  # noqa: F401
     mxfp4_dequantize,
     mxfp4_block_partials,
     mxfp4_gemm,
+)
+from .nvfp4 import (  # noqa: F401
+    e4m3_decode,
+    e4m3_round,
+    nvfp4_global_scale,
+    nvfp4_quantize,
+    nvfp4_dequantize,
+    nvfp4_block_partials,
+    nvfp4_gemm,
 )

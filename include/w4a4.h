@@ -1,6 +1,6 @@
 /*
- * w4a4.h -- C ABI of libw4a4.so: W4A4 group-quantized GEMM and MXFP4 GEMM on
- * AMD Instinct MI355X (gfx950).
+ * w4a4.h -- C ABI of libw4a4.so: W4A4 group-quantized GEMM, MXFP4 GEMM and
+ * NVFP4 GEMM on AMD Instinct MI355X (gfx950).
  *
  * What is computed (see the operation comments below for the passages):
  *   Y[M,N] = X[M,K] * W[N,K]^T for a linear layer whose activations X and
@@ -12,7 +12,11 @@
  *   - or MXFP4: FP4 E2M1 values with one E8M0 power-of-two scale per 32 K
  *     elements ("the open-standard MXFP4", FP4 RL post-training abstract on the
  *     "Depth Registers Unlock W4A4 on SwiGLU" page; block rule from the OCP
- *     Microscaling Formats v1.0 specification).
+ *     Microscaling Formats v1.0 specification),
+ *   - or NVFP4: FP4 E2M1 values with one FP8 E4M3 scale per 16 K elements and
+ *     one binary32 global scale per tensor (ARCQuant abstract on the APEX4
+ *     page; Minima abstract on the "Daily Papers" page: 16-element block
+ *     scaling and a calibrated per-module global scale).
  *
  * Conventions (all entry points):
  *   - Every data pointer is a DEVICE pointer, owned by the caller. The library
@@ -24,11 +28,12 @@
  *     A launch failure reported by hipGetLastError() returns W4A4_E_HIP.
  *   - Extents are int64_t element counts. A zero extent (M, N or rows == 0) is a
  *     valid no-op; pointers whose extent is zero may then be NULL.
- *   - Buffers must not overlap. Results are deterministic (no atomics).
+ *   - Buffers must not overlap. Results are deterministic (no floating-point
+ *     atomics; nvfp4_global_scale's one integer atomic max is order-free).
  *   - Packed 4-bit codes are row-major [rows][K/2] bytes, K contiguous, 4 bits
  *     per code.
- *     MXFP4: E2M1 codes (sign<<3 | magnitude index into {0,0.5,1,1.5,2,3,4,6}),
- *     two per byte, the even k in the LOW nibble.
+ *     MXFP4 and NVFP4: E2M1 codes (sign<<3 | magnitude index into
+ *     {0,0.5,1,1.5,2,3,4,6}), two per byte, the even k in the LOW nibble.
  *     INT4: sign-magnitude (the symmetric rule below only yields codes in
  *     [-7, 7]), the sign bit being that of the input value (a negative input
  *     that rounds to 0 is stored as -0). Each 8-byte unit holds the codes
@@ -212,6 +217,81 @@ w4a4_status_t mxfp4_gemm(const uint8_t* xq, const uint8_t* xe, const uint8_t* wq
  */
 w4a4_status_t mxfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xe,
                                         const uint8_t* wq, const uint8_t* we,
+                                        int64_t M, int64_t N, int64_t K,
+                                        int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                                        int32_t* partials, void* stream);
+
+/*
+ * NVFP4 global scale of a tensor: *global_scale = fl32(max|x| / 2688),
+ * 2688 = 6 * 448 (the largest E2M1 value times the largest E4M3 value), so
+ * the block holding the absmax gets the largest block scale. The pages name a
+ * calibrated global scale per module (Minima abstract); this is the plain
+ * choice for calibrating it from data, and for weights offline.
+ *
+ *   x             fp16 [rows][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0;
+ *                 K % 8 == 0; finite values
+ *   global_scale  out: ONE float in device memory (4-byte aligned); written on
+ *                 the stream by three launches (clear, integer atomic max of
+ *                 the fp16 magnitude bits, finish), so no host sync; rows == 0
+ *                 writes 0.
+ */
+w4a4_status_t nvfp4_global_scale(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                 float* global_scale, void* stream);
+
+/*
+ * NVFP4 quantization of the rows of X with a given global scale s_g (read on
+ * the device from global_scale: finite, >= 0, normal or 0). Per block of 16 K
+ * elements with absmax a, in correctly rounded binary32 (the pages give no
+ * formula; this is the plain reading of the format):
+ *   d = fl32(6 s_g); r = fl32(a / d) (a = 0: r = 0), saturated at 448;
+ *   s_b = E4M3 rounding of r to nearest, ties to even (OCP FP8 E4M3FN);
+ *   e = fl32(1 / fl32(s_b s_g)) (0 when that product is 0);
+ *   code = E2M1 rounding of fl32(x e) to nearest, ties to even, saturating at
+ *          6, the sign bit that of x (also when the magnitude rounds to 0).
+ * Then x ~ v * s_b * s_g.
+ *
+ *   x       fp16 [rows][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0;
+ *           K % 256 == 0
+ *   q       out: u8 [rows][K/2] packed E2M1 codes, 4-byte aligned
+ *   scales  out: u8, rows * K/16 E4M3 bytes in 256-k panels, 2-byte aligned:
+ *           the scale of row r and block b (p = b / 16, j = b % 16) is at byte
+ *           16 * rows * p + 16 * r + 8 * ((j >> 1) & 1) + 2 * (j >> 2) + (j & 1).
+ *           A panel row thus holds blocks 0,1,4,5,8,9,12,13 in bytes 0..7 and
+ *           2,3,6,7,10,11,14,15 in bytes 8..15: a GEMM stage of 256 k reads a
+ *           tile's scales as one contiguous run, and each matrix-core lane the
+ *           8 block scales it needs as one 8-byte word.
+ */
+w4a4_status_t nvfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, const float* global_scale,
+                             uint8_t* q, uint8_t* scales, void* stream);
+
+/*
+ * NVFP4 GEMM: Y[m,n] = g_x g_w * sum_b s_x[m,b] s_w[n,b] * sum_{k in block b}
+ * vx[m,k] vw[n,k], block b = 16 consecutive k. The matrix cores scale FP4
+ * only by E8M0 powers of two per 32 elements, so each operand fragment is
+ * converted to fp16 (v * s_b, exact) and multiplied on the fp16 matrix-core
+ * path with fp32 accumulation; Y = fl32(acc * fl32(g_x g_w)).
+ *
+ *   xq, xs    activation codes [M][K/2] (16-byte aligned) and M * K/16 scale
+ *             bytes (panel layout of nvfp4_quantize, 16-byte aligned)
+ *   x_global  ONE float in device memory: the activations' global scale
+ *   wq, ws, w_global   the same for the weights [N][K/2]
+ *   K > 0, K % 256 == 0, K <= 2^23; y as for w4a4_gemm.
+ */
+w4a4_status_t nvfp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* x_global,
+                         const uint8_t* wq, const uint8_t* ws, const float* w_global,
+                         int64_t M, int64_t N, int64_t K,
+                         void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * Debug export of the exact per-block integers I_b = sum_{k in b} (2 vx)(2 vw)
+ * of nvfp4_gemm (16-element blocks), from the same loads, conversion and
+ * fp16 matrix-core instructions run one block at a time with unit scales, for
+ * the window [m0, m0+mc) x [n0, n0+nc):
+ *   partials  out: int32 [K/16][mc][nc]
+ * The scale arrays are read (as by nvfp4_gemm) but do not enter the result.
+ */
+w4a4_status_t nvfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xs,
+                                        const uint8_t* wq, const uint8_t* ws,
                                         int64_t M, int64_t N, int64_t K,
                                         int64_t m0, int64_t mc, int64_t n0, int64_t nc,
                                         int32_t* partials, void* stream);

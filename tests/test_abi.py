@@ -137,6 +137,31 @@ def test_mxfp4_validation(lib):
     assert mp(P, P, P, P, 4, 4, 128, 0, 5, 0, 4, P, None) == E_SHAPE
 
 
+def test_nvfp4_validation(lib):
+    gs = lambda *a: _lib.status_of("nvfp4_global_scale", *a)
+    assert gs(P, 4, 60, 60, P, None) == E_SHAPE          # K % 8
+    assert gs(P, 4, 64, 68, P, None) == E_ALIGN
+    assert gs(P, 4, 64, 64, None, None) == E_NULL
+    assert gs(None, 4, 64, 64, P, None) == E_NULL
+    assert gs(P + 8, 4, 64, 64, P, None) == E_ALIGN
+    nq = lambda *a: _lib.status_of("nvfp4_quantize", *a)
+    assert nq(P, 4, 128, 128, P, P, P, None) == E_SHAPE  # K % 256
+    assert nq(P, 4, 256, 260, P, P, P, None) == E_ALIGN
+    assert nq(P, 0, 256, 256, None, None, None, None) == OK
+    assert nq(P, 4, 256, 256, None, P, P, None) == E_NULL
+    assert nq(P, 4, 256, 256, P, P, P + 1, None) == E_ALIGN
+    ng = lambda *a: _lib.status_of("nvfp4_gemm", *a)
+    assert ng(P, P, P, P, P, P, 4, 4, 128, P, 0, 4, None) == E_SHAPE
+    assert ng(P, P, P, P, P, P, 4, 4, 256, P, 2, 4, None) == E_DTYPE
+    assert ng(P, P + 4, P, P, P, P, 4, 4, 256, P, 0, 4, None) == E_ALIGN   # scales 16-byte aligned
+    assert ng(P, P, None, P, P, P, 4, 4, 256, P, 0, 4, None) == E_NULL
+    assert ng(P, P, P, P, P, P, 0, 4, 256, None, 0, 4, None) == OK
+    assert ng(P, P, P, P, P, P, 4, 4, (1 << 23) + 256, P, 0, 4, None) == E_SHAPE
+    npart = lambda *a: _lib.status_of("nvfp4_gemm_debug_partials", *a)
+    assert npart(P, P, P, P, 4, 4, 256, 0, 5, 0, 4, P, None) == E_SHAPE
+    assert npart(P, P, P, P, 4, 4, 256, 0, 4, 0, 4, None, None) == E_NULL
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libw4a4.so"))

@@ -40,3 +40,26 @@ def test_mxfp4_panel_layout_torch():
     flat = ops.mxfp4_scales_to_panels(e_rows)
     assert torch.equal(ops.mxfp4_scales_to_rows(flat, 6, 384), e_rows)
     assert np.array_equal(flat.numpy(), panels_by_definition(e_rows.numpy()))
+
+
+def nv_panels_by_definition(s_rows):
+    """The NVFP4 scale panel layout written out with loops from its definition:
+    panel p = blocks 16p..16p+15, rows of 16 bytes, the blocks in the order
+    0,1,4,5,8,9,12,13,2,3,6,7,10,11,14,15."""
+    rows, nb = s_rows.shape
+    order = [0, 1, 4, 5, 8, 9, 12, 13, 2, 3, 6, 7, 10, 11, 14, 15]
+    out = []
+    for p in range(nb // 16):
+        for r in range(rows):
+            for j in order:
+                out.append(s_rows[r, 16 * p + j])
+    return np.array(out, dtype=s_rows.dtype)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 256), (5, 512), (3, 3584)])
+def test_nvfp4_panel_layout(rows, K):
+    rng = np.random.default_rng(rows + K)
+    s_rows = rng.integers(0, 256, (rows, K // 16), dtype=np.uint8)
+    flat = ops.nvfp4_scales_to_panels(s_rows)
+    assert np.array_equal(flat, nv_panels_by_definition(s_rows))
+    assert np.array_equal(ops.nvfp4_scales_to_rows(flat, rows, K), s_rows)

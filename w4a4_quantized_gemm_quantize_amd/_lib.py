@@ -38,6 +38,11 @@ SIGNATURES = {
     "mxfp4_gemm": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p],
     "mxfp4_gemm_debug_partials": [_p, _p, _p, _p, _i64, _i64, _i64,
                                   _i64, _i64, _i64, _i64, _p, _p],
+    "nvfp4_global_scale": [_p, _i64, _i64, _i64, _p, _p],
+    "nvfp4_quantize": [_p, _i64, _i64, _i64, _p, _p, _p, _p],
+    "nvfp4_gemm": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p],
+    "nvfp4_gemm_debug_partials": [_p, _p, _p, _p, _i64, _i64, _i64,
+                                  _i64, _i64, _i64, _i64, _p, _p],
 }
 
 

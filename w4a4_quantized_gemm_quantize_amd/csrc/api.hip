@@ -205,4 +205,77 @@ w4a4_status_t mxfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xe,
   return launched();
 }
 
+static w4a4_status_t nv_quant_shape(int64_t rows, int64_t K, int64_t ldx) {
+  if (rows < 0 || K <= 0 || K % 256 || ldx < K || K > (int64_t{1} << 30)) return W4A4_E_SHAPE;
+  if (ldx % 8) return W4A4_E_ALIGN;
+  return W4A4_OK;
+}
+
+w4a4_status_t nvfp4_global_scale(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                 float* global_scale, void* stream) {
+  if (rows < 0 || K <= 0 || K % 8 || ldx < K || K > (int64_t{1} << 30)) return W4A4_E_SHAPE;
+  if (ldx % 8) return W4A4_E_ALIGN;
+  if (!global_scale || (rows > 0 && !x)) return W4A4_E_NULL;
+  if (!aligned(global_scale, 4) || (rows > 0 && !aligned(x, 16))) return W4A4_E_ALIGN;
+  w4a4::launch_nvfp4_global_scale(x, rows, K, ldx, global_scale, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t nvfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, const float* global_scale,
+                             uint8_t* q, uint8_t* scales, void* stream) {
+  w4a4_status_t st = nv_quant_shape(rows, K, ldx);
+  if (st != W4A4_OK || rows == 0) return st;
+  if (!x || !global_scale || !q || !scales) return W4A4_E_NULL;
+  if (!aligned(x, 16) || !aligned(global_scale, 4) || !aligned(q, 4) || !aligned(scales, 2)) return W4A4_E_ALIGN;
+  w4a4::launch_nvfp4_quant(x, rows, K, ldx, global_scale, q, scales, as_stream(stream));
+  return launched();
+}
+
+static w4a4_status_t nv_common(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                               int64_t M, int64_t N, int64_t K, GemmArgs& g) {
+  // K <= 2^23: a 256-row tile then spans < 2^31 bytes, the kernel's 32-bit
+  // buffer offsets
+  if (M < 0 || N < 0 || K <= 0 || K % 256 || K > (int64_t{1} << 23)) return W4A4_E_SHAPE;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !xs || !wq || !ws) return W4A4_E_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xs, 16) || !aligned(ws, 16)) return W4A4_E_ALIGN;
+  g.a = xq; g.sa = xs; g.w = wq; g.sw = ws;
+  g.ga = 16; g.gw = 16;
+  g.M = M; g.N = N; g.K = K;
+  return W4A4_OK;
+}
+
+w4a4_status_t nvfp4_gemm(const uint8_t* xq, const uint8_t* xs, const float* x_global,
+                         const uint8_t* wq, const uint8_t* ws, const float* w_global,
+                         int64_t M, int64_t N, int64_t K,
+                         void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = nv_common(xq, xs, wq, ws, M, N, K, g);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (!x_global || !w_global) return W4A4_E_NULL;
+  if (!aligned(x_global, 4) || !aligned(w_global, 4)) return W4A4_E_ALIGN;
+  if ((st = check_y(y, y_dtype, N, ldy)) != W4A4_OK) return st;
+  g.y = y; g.ydtype = y_dtype; g.ldy = ldy;
+  g.m0 = 0; g.mc = M; g.n0 = 0; g.nc = N; g.partials = nullptr;
+  w4a4::launch_nvfp4_gemm(g, x_global, w_global, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t nvfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xs,
+                                        const uint8_t* wq, const uint8_t* ws,
+                                        int64_t M, int64_t N, int64_t K,
+                                        int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                                        int32_t* partials, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = nv_common(xq, xs, wq, ws, M, N, K, g);
+  if (st != W4A4_OK) return st;
+  if ((st = check_window(M, N, m0, mc, n0, nc)) != W4A4_OK) return st;
+  if (!partials) return W4A4_E_NULL;
+  if (!aligned(partials, 4)) return W4A4_E_ALIGN;
+  g.y = nullptr; g.ydtype = 0; g.ldy = 0;
+  g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc; g.partials = partials;
+  w4a4::launch_nvfp4_gemm(g, nullptr, nullptr, as_stream(stream));
+  return launched();
+}
+
 }  // extern "C"

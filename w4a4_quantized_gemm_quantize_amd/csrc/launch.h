@@ -19,7 +19,7 @@ void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
 // output and partials == nullptr.
 struct GemmArgs {
   const uint8_t* a;
-  const void* sa;      // float* (INT4) or uint8_t* (MXFP4)
+  const void* sa;      // float* (INT4) or uint8_t* (MXFP4, NVFP4)
   const uint8_t* w;
   const void* sw;
   int ga, gw;          // INT4 group sizes (unused for MXFP4)
@@ -33,5 +33,14 @@ struct GemmArgs {
 
 void launch_w4a4_gemm(const GemmArgs& a, hipStream_t stream);
 void launch_mxfp4_gemm(const GemmArgs& a, hipStream_t stream);
+
+// NVFP4: *gscale = fl32(max|x| / 2688) (0 for rows == 0)
+void launch_nvfp4_global_scale(const void* x, int64_t rows, int64_t K, int64_t ldx, float* gscale,
+                               hipStream_t stream);
+void launch_nvfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx, const float* gscale,
+                        uint8_t* q, uint8_t* scales, hipStream_t stream);
+// a.sa / a.sw: E4M3 panel scales; ga, gw: device pointers to the global scales
+// (unused by the partials export)
+void launch_nvfp4_gemm(const GemmArgs& a, const float* ga, const float* gw, hipStream_t stream);
 
 }  // namespace w4a4

@@ -50,6 +50,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace w4a4 {
 
@@ -59,7 +60,6 @@ constexpr int kQuantThreads = 256;
 constexpr int64_t kMaxGridY = 65535;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // Correctly rounded x / d given r = RN(1/d) (d normal, no overflow/underflow).
 __device__ __forceinline__ float div_rn(float x, float d, float r) {
@@ -81,20 +81,6 @@ __device__ __forceinline__ void group_scale(float a, float& s, float& r8, float&
   s = div_rn(a, 7.0f, r7);
   r8 = ((s == 0.0f) ? 0.0f : 1.0f / s) * 0.125f;   // correctly rounded division
   s8 = s * 8.0f;
-}
-
-// max |x| over the 2 NW fp16 values of w[0..NW) (NW even), as fp32.
-template <int NW>
-__device__ __forceinline__ float absmax_words(const uint32_t* w) {
-  h2 mx = {0, 0}, mn = {0, 0};
-#pragma unroll
-  for (int i = 0; i < NW; i += 2) {
-    const h2 a = __builtin_bit_cast(h2, w[i]), b = __builtin_bit_cast(h2, w[i + 1]);
-    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, a), b);
-    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, a), b);
-  }
-  mx = __builtin_elementwise_maximum(mx, -mn);
-  return fmaxf((float)mx.x, (float)mx.y);
 }
 
 // t / 8 with t = RN(x / s), sign of x kept on zero results. nz is -0.0 held in a
@@ -127,19 +113,6 @@ __device__ __forceinline__ uint4 int4_codes(const uint32_t* w, float r8, float s
   const auto f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
   return uint4{f[0] | (f[1] & kFoldX), f[2] | (f[1] & kFoldY),
                f[3] | (f[4] & kFoldX), f[5] | (f[4] & kFoldY)};
-}
-
-__device__ __forceinline__ float opaque_neg_zero() {
-  float nz = -0.0f;
-  asm volatile("" : "+v"(nz));
-  return nz;
-}
-
-__device__ __forceinline__ void words16(const uint4 r[4], uint32_t w[16]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[4 * j] = r[j].x; w[4 * j + 1] = r[j].y; w[4 * j + 2] = r[j].z; w[4 * j + 3] = r[j].w;
-  }
 }
 
 // Lane tile: a wave covers 64 / LPW rows x LPW consecutive 32-element chunks
@@ -276,23 +249,6 @@ __device__ __forceinline__ int64_t panel_offset(int rows, int nbo, int row, int 
 // the MX quantization of the residual x - deq(Q(x)) (the activation side of
 // the appended-residual GEMM), or a copy of Q(x) (its weight side).
 enum { MX_PLAIN = 0, MX_APPEND_RESIDUAL = 1, MX_APPEND_COPY = 2 };
-
-// E2M1 codes of 32 fp32 values already divided by their block scale (exact
-// power-of-two scaling), two per instruction with unit scale: the same
-// rounding as e2m1_codes32.
-__device__ __forceinline__ uint4 e2m1_codes32_f32(const float v[32]) {
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j], v[8 * j + 1], 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 2], v[8 * j + 3], 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 4], v[8 * j + 5], 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * j + 6], v[8 * j + 7], 1.0f, 3);
-    o[j] = w;
-  }
-  return uint4{o[0], o[1], o[2], o[3]};
-}
 
 // The E2M1 values (unit scale) of the 8 codes of a word, element 2i from the
 // low nibble of byte i.

@@ -210,3 +210,111 @@ def mxfp4_gemm_debug_partials(xq, xe, wq, we, m0: int, mc: int, n0: int, nc: int
     call("mxfp4_gemm_debug_partials", xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(),
          M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
     return part
+
+
+# ------------------------------------------------------------------- NVFP4
+
+def nvfp4_scale_offsets(rows: int, K: int):
+    """Byte offset of the E4M3 scale of (row r, block b) in the 256-k panel
+    layout of the C header: ``16*rows*p + 16*r + 8*((j>>1)&1) + 2*(j>>2) +
+    (j&1)`` with ``p = b // 16``, ``j = b % 16``. Returns int64 [rows, K/16]."""
+    b = torch.arange(K // 16, dtype=torch.int64)
+    p, j = b // 16, b % 16
+    pos = 8 * ((j >> 1) & 1) + 2 * (j >> 2) + (j & 1)
+    r = torch.arange(rows, dtype=torch.int64)[:, None]
+    return 16 * rows * p[None, :] + 16 * r + pos[None, :]
+
+
+def nvfp4_scales_to_rows(s, rows: int, K: int):
+    """Panel-layout scale bytes (flat, ``rows*K/16``) -> row-major [rows, K/16]
+    (torch tensor on its device, or numpy array)."""
+    idx = nvfp4_scale_offsets(rows, K)
+    if isinstance(s, torch.Tensor):
+        return s.reshape(-1)[idx.to(s.device)]
+    return s.reshape(-1)[idx.numpy()]
+
+
+def nvfp4_scales_to_panels(s_rows):
+    """Row-major [rows, K/16] scale bytes -> the flat panel layout."""
+    rows, nb = s_rows.shape
+    idx = nvfp4_scale_offsets(rows, 16 * nb).reshape(-1)
+    if isinstance(s_rows, torch.Tensor):
+        out = torch.empty(rows * nb, dtype=s_rows.dtype, device=s_rows.device)
+        out[idx.to(s_rows.device)] = s_rows.reshape(-1)
+        return out
+    import numpy as np
+    out = np.empty(rows * nb, dtype=s_rows.dtype)
+    out[idx.numpy()] = s_rows.reshape(-1)
+    return out
+
+
+def _need_scalar(t, name: str) -> None:
+    _need(t, torch.float32, name)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold one float")
+
+
+def nvfp4_global_scale(x: torch.Tensor, out=None):
+    """``fl32(max|x| / 2688)`` of fp16 X[rows, K] as a one-element float32
+    tensor on the device (computed there, no host sync)."""
+    _need(x, torch.float16, "x")
+    if x.dim() != 2 or (x.shape[0] > 0 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit column stride")
+    g = torch.empty((1,), dtype=torch.float32, device=x.device) if out is None else out
+    _need_scalar(g, "out")
+    ldx = x.stride(0) if x.shape[0] > 0 else x.shape[1]
+    call("nvfp4_global_scale", x.data_ptr(), x.shape[0], x.shape[1], ldx, g.data_ptr(), _stream(x))
+    return g
+
+
+def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor, out=None):
+    """NVFP4 quantization of fp16 X[rows, K] with a device global scale:
+    ``(codes uint8 [rows, K/2], E4M3 scales uint8 [rows*K/16] in the 256-k
+    panel layout)``; see :func:`nvfp4_scales_to_rows`."""
+    _need(x, torch.float16, "x")
+    _need_scalar(global_scale, "global_scale")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    R, K = x.shape
+    if out is None:
+        q = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((R * (K // 16),), dtype=torch.uint8, device=x.device)
+    else:
+        q, s = out
+    if s.numel() != R * (K // 16) or not s.is_contiguous():
+        raise ValueError("scales must be contiguous with rows*K/16 bytes")
+    call("nvfp4_quantize", x.data_ptr(), R, K, x.stride(0), global_scale.data_ptr(),
+         q.data_ptr(), s.data_ptr(), _stream(x))
+    return q, s
+
+
+def _nv_shapes(xq, xs, wq, ws):
+    for t, n in ((xq, "xq"), (xs, "xs"), (wq, "wq"), (ws, "ws")):
+        _need(t, torch.uint8, n)
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("K of xq and wq differ")
+    if xs.numel() != M * (K // 16) or ws.numel() != N * (K // 16):
+        raise ValueError("scale tensors must hold rows*K/16 bytes (panel layout)")
+    return M, N, K
+
+
+def nvfp4_gemm(xq, xs, x_global, wq, ws, w_global, out_dtype=torch.float32, out=None):
+    """Y[M, N] = NVFP4 GEMM of X and W (fp16 matrix cores, fp32 accumulation)."""
+    M, N, K = _nv_shapes(xq, xs, wq, ws)
+    _need_scalar(x_global, "x_global")
+    _need_scalar(w_global, "w_global")
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    call("nvfp4_gemm", xq.data_ptr(), xs.data_ptr(), x_global.data_ptr(), wq.data_ptr(), ws.data_ptr(),
+         w_global.data_ptr(), M, N, K, y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
+    return y
+
+
+def nvfp4_gemm_debug_partials(xq, xs, wq, ws, m0: int, mc: int, n0: int, nc: int):
+    """Exact int32 block integers I_b = sum (2vx)(2vw) over 16-blocks; [K/16, mc, nc]."""
+    M, N, K = _nv_shapes(xq, xs, wq, ws)
+    part = torch.empty((K // 16, mc, nc), dtype=torch.int32, device=xq.device)
+    call("nvfp4_gemm_debug_partials", xq.data_ptr(), xs.data_ptr(), wq.data_ptr(), ws.data_ptr(),
+         M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
+    return part

@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4-g128 GEMM TOPS incl. act-quant, LLaMA-70B FFN shapes; % of MFMA peak"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix-core peak (5.0 POP/s)
 PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4/fp6 matrix-core peak
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 matrix-core peak (the NVFP4 GEMM's instructions)
 PEAK_HBM_GBS = 8000.0
 
 # name -> (tokens M, [(K, N), ...], act group, weight group, format)
@@ -41,12 +42,15 @@ WORKLOADS = {
     "qwen25_7b_mxfp4_ffn": (4096, [(3584, 18944), (3584, 18944), (18944, 3584)], 32, 32, "mxfp4"),
     # two-pass MXFP4 with the residual appended along K (the GEMM runs K' = 2K)
     "qwen25_7b_mxfp4_residual_ffn": (4096, [(3584, 18944), (3584, 18944), (18944, 3584)], 32, 32, "mxfp4res"),
+    # NVFP4 (E4M3 scale per 16, global scale per tensor) on the same shapes
+    "qwen25_7b_nvfp4_ffn": (4096, [(3584, 18944), (3584, 18944), (18944, 3584)], 16, 16, "nvfp4"),
 }
 
 
 GEMM_SOURCES = {"int4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_w4a4.hip",
                 "mxfp4": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip",
-                "mxfp4res": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip"}
+                "mxfp4res": "w4a4_quantized_gemm_quantize_amd/csrc/gemm_mxfp4.hip",
+                "nvfp4": "w4a4_quantized_gemm_quantize_amd/csrc/nvfp4.hip"}
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_traffic.json")
 
 
@@ -106,6 +110,11 @@ def quant_standalone(shapes, ga, fmt, reps: int = 24, nrot: int = 6):
             sc = torch.empty((M * (K // 32),), dtype=torch.uint8, device=dev)
             call = lambda x: ops.mxfp4_quantize(x, out=(xq, sc))
             nbytes = M * (2 * K + K // 2 + K // 32)
+        elif fmt == "nvfp4":
+            sc = torch.empty((M * (K // 16),), dtype=torch.uint8, device=dev)
+            g = ops.nvfp4_global_scale(xs[0])      # a calibrated (static) global scale
+            call = lambda x: ops.nvfp4_quantize(x, g, out=(xq, sc))
+            nbytes = M * (2 * K + K // 2 + K // 16)
         else:
             xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
             sc = torch.empty((M * (2 * K // 32),), dtype=torch.uint8, device=dev)
@@ -149,6 +158,9 @@ def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
             wpk = oracle.int4_quantize(w, gw)
         elif fmt == "mxfp4":
             wpk = oracle.mxfp4_quantize(w)
+        elif fmt == "nvfp4":  # weights and both global scales offline (calibration), untimed
+            sgw = oracle.nvfp4_global_scale(w)
+            wpk = (*oracle.nvfp4_quantize(w, sgw), sgw, oracle.nvfp4_global_scale(x))
         else:
             wpk = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w))
         work.append((x, wpk, K, len(cols)))
@@ -158,6 +170,9 @@ def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
         if fmt == "int4":
             qa, sa = oracle.int4_quantize(x, ga)
             oracle.w4a4_gemm(qa, sa, ga, wpk[0], wpk[1], gw)
+        elif fmt == "nvfp4":
+            ca, sa = oracle.nvfp4_quantize(x, wpk[3])
+            oracle.nvfp4_gemm(ca, sa, wpk[3], wpk[0], wpk[1], wpk[2])
         else:
             ca, ea = oracle.mxfp4_quantize(x) if fmt == "mxfp4" else oracle.mxfp4_quantize_residual(x)
             oracle.mxfp4_gemm(ca, ea, wpk[0], wpk[1])
@@ -230,6 +245,14 @@ def main() -> int:
             wq, ws = ops.mxfp4_quantize(w)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             xs = torch.empty((M * (K // 32),), dtype=torch.uint8, device=dev)
+        elif fmt == "nvfp4":
+            # weight global scale and packing offline; the activation global
+            # scale calibrated once on this input, untimed (a static scale)
+            gwt = ops.nvfp4_global_scale(w)
+            wq, ws = ops.nvfp4_quantize(w, gwt)
+            gxt = ops.nvfp4_global_scale(x)
+            xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M * (K // 16),), dtype=torch.uint8, device=dev)
         else:
             wq, ws = ops.mxfp4_quantize_append_copy(w)
             xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
@@ -237,6 +260,8 @@ def main() -> int:
         del w
         y = torch.empty((M, N), dtype=ydt, device=dev)
         layers.append(dict(K=K, N=N, x=x, wq=wq, ws=ws, xq=xq, xs=xs, y=y))
+        if fmt == "nvfp4":
+            layers[-1].update(gx=gxt, gw=gwt)
         log(f"linear {li}: K={K} N={N} ready")
     torch.cuda.synchronize()
 
@@ -248,12 +273,16 @@ def main() -> int:
                 ops.w4a4_quantize_act(L["x"], ga, out=(L["xq"], L["xs"]))
             elif fmt == "mxfp4":
                 ops.mxfp4_quantize(L["x"], out=(L["xq"], L["xs"]))
+            elif fmt == "nvfp4":
+                ops.nvfp4_quantize(L["x"], L["gx"], out=(L["xq"], L["xs"]))
             else:
                 ops.mxfp4_quantize_residual(L["x"], out=(L["xq"], L["xs"]))
             if ev is not None:
                 ev[li][1].record()
             if fmt == "int4":
                 ops.w4a4_gemm(L["xq"], L["xs"], ga, L["wq"], L["ws"], gw, out=L["y"])
+            elif fmt == "nvfp4":
+                ops.nvfp4_gemm(L["xq"], L["xs"], L["gx"], L["wq"], L["ws"], L["gw"], out=L["y"])
             else:
                 ops.mxfp4_gemm(L["xq"], L["xs"], L["wq"], L["ws"], out=L["y"])
             if ev is not None:
@@ -290,11 +319,11 @@ def main() -> int:
     kmul = 2 if fmt == "mxfp4res" else 1     # the appended-residual GEMM runs K' = 2K
     gemm_ops = sum(2 * M * L["N"] * kmul * L["K"] for L in layers) * args.steps
     achieved = gemm_ops / gemm_s.sum() / 1e12
-    peak = PEAK_INT8_TOPS if fmt == "int4" else PEAK_FP4_TFLOPS
+    peak = {"int4": PEAK_INT8_TOPS, "nvfp4": PEAK_FP16_TFLOPS}.get(fmt, PEAK_FP4_TFLOPS)
     ybytes = 4 if ydt == torch.float32 else 2
     quant_bytes = 0
     for L in layers:
-        sbytes = 4 * (L["K"] // ga) if fmt == "int4" else kmul * L["K"] // 32
+        sbytes = 4 * (L["K"] // ga) if fmt == "int4" else L["K"] // 16 if fmt == "nvfp4" else kmul * L["K"] // 32
         quant_bytes += M * (2 * L["K"] + kmul * L["K"] // 2 + sbytes)
     quant_gbs = quant_bytes * args.steps / quant_s.sum() / 1e9
     per_linear = []
@@ -328,7 +357,7 @@ def main() -> int:
         "config": {
             "workload": args.workload, "tokens": M,
             "linears_KxN": [f"{K}x{N}" for K, N in wl],
-            "group_a": ga if fmt == "int4" else 32, "group_w": gw if fmt == "int4" else 32,
+            "group_a": ga if fmt in ("int4", "nvfp4") else 32, "group_w": gw if fmt in ("int4", "nvfp4") else 32,
             "y_dtype": args.ydtype, "parallelism": "single GPU",
         },
         "roofline": {

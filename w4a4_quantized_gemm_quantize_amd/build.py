@@ -36,8 +36,9 @@ HIPCC_FLAGS = [
 # per-token GEMM variant once ran 4x slower on 87 spilled registers).
 def _is_debug_kernel(name: str) -> bool:
     """A partials-export instantiation: PARTIALS is the first template argument
-    of the INT4 kernels and the last one of the MXFP4 kernel."""
+    of the INT4 and NVFP4 kernels and the last one of the MXFP4 kernel."""
     return ("11k_w4a4_gemmILb1E" in name or "17k_w4a4_gemm_smallILb1E" in name
+            or "12k_nvfp4_gemmILb1E" in name
             or ("12k_mxfp4_gemm" in name and name.endswith("Lb1EEEvNS0_6ParamsE")))
 
 

@@ -200,9 +200,9 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 // 16 consecutive rows hit 16 distinct 16-byte bank groups) and the 512 rows'
 // 16 panel scale bytes.
 template <bool PARTIALS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_nvfp4_gemm(Params p) {
-  constexpr int BM = 256, BN = 256, WM = 2, WN = 2, KB = 256;
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, KB = 256;
   constexpr int NWAVE = WM * WN;
   constexpr int RB = KB / 2;                        // packed bytes per row per stage
   constexpr int SL = RB / 16;                       // 16-byte slots per row
@@ -213,6 +213,7 @@ void k_nvfp4_gemm(Params p) {
   constexpr int S_OFF = (BM + BN) * RB;
   constexpr int STAGE = S_OFF + (BM + BN) * 16;
   constexpr int NS = (BM + BN) / 64 / NWAVE;       // 1 KB scale loads per wave per stage
+  constexpr int VPM = (TI + TJ) * 8 / (TI * TJ);    // conversion instructions per MFMA
   static_assert(NS * NWAVE * 64 == BM + BN, "scale loads cover the stage's rows");
   __shared__ __align__(16) uint8_t sm0[STAGE];
   __shared__ __align__(16) uint8_t sm1[STAGE];
@@ -355,20 +356,40 @@ void k_nvfp4_gemm(Params p) {
         fa_[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((U) < 2 ? scA[i].x : scA[i].y, 1.0f, ((U) & 1) != 0); \
       _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                 \
         fw_[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((U) < 2 ? scW[j].x : scW[j].y, 1.0f, ((U) & 1) != 0); \
+      /* two sets of converted fragments: words q + 1 are converted while the */    \
+      /* MFMAs of words q run, one MFMA between every four conversions */           \
+      h8 a16_[2][TI], w16_[2][TJ];                                                   \
+      DEQ(0, 0);                                                                     \
+      __builtin_amdgcn_sched_barrier(0);                                             \
       _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
-        h8 a16_[TI], w16_[TJ];                                                       \
-        _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
-          a16_[i] = dequant8(word_of(av[B][i], q), q < 2 ? fa_[i].x : fa_[i].y);     \
-        _Pragma("unroll") for (int j = 0; j < TJ; ++j)                               \
-          w16_[j] = dequant8(word_of(wv[B][j], q), q < 2 ? fw_[j].x : fw_[j].y);     \
+        if (q < 3) DEQ((q + 1) & 1, q + 1);                                          \
         if (q == 3 && (NEXTU) < 4) LOAD_OPS(SM, (NEXTU) & 3, 0);                     \
         _Pragma("unroll") for (int i = 0; i < TI; ++i)                               \
         _Pragma("unroll") for (int j = 0; j < TJ; ++j)                               \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a16_[i], w16_[j], acc[i][j], 0, 0, 0); \
-        __builtin_amdgcn_sched_barrier(0);  /* one k16 step's fragments live at a time */ \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a16_[q & 1][i], w16_[q & 1][j], acc[i][j], 0, 0, 0); \
+        if (q < 3) {                                                                 \
+          _Pragma("unroll") for (int g = 0; g < TI * TJ; ++g) {                      \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   /* one MFMA */     \
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0); /* conversions */  \
+          }                                                                          \
+        } else if ((NEXTU) < 4) {                                                    \
+          _Pragma("unroll") for (int g = 0; g < TI + TJ; ++g) {                      \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   /* one MFMA */     \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   /* one LDS read */ \
+          }                                                                          \
+        }                                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                           \
       }                                                                              \
     }                                                                                \
   }                                                                                  \
+  }
+// Convert words Q of the step's operands into fragment set SET.
+#define DEQ(SET, Q)                                                                  \
+  {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < TI; ++i)                                   \
+      a16_[SET][i] = dequant8(word_of(av[0][i], (Q)), (Q) < 2 ? fa_[i].x : fa_[i].y); \
+    _Pragma("unroll") for (int j = 0; j < TJ; ++j)                                   \
+      w16_[SET][j] = dequant8(word_of(wv[0][j], (Q)), (Q) < 2 ? fw_[j].x : fw_[j].y); \
   }
 #define PIPE_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define STAGE_BARRIER()                                                 \
@@ -407,6 +428,7 @@ void k_nvfp4_gemm(Params p) {
 #undef STAGE_BARRIER
 #undef PIPE_FENCE
 #undef MMA_STEP
+#undef DEQ
 #undef LOAD_SCALES
 #undef LOAD_OPS
 #undef ISSUE
@@ -528,9 +550,9 @@ void launch_nvfp4_gemm(const GemmArgs& g, const float* ga, const float* gw, hipS
   p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   if (g.partials)
-    hipLaunchKernelGGL(k_nvfp4_gemm<true>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_nvfp4_gemm<true>, grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL(k_nvfp4_gemm<false>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_nvfp4_gemm<false>, grid, dim3(512), 0, stream, p);
 }
 
 }  // namespace w4a4

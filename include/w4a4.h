@@ -131,6 +131,38 @@ w4a4_status_t w4a4_gemm(const uint8_t* xq, const float* xs, int32_t group_a,
                         void* y, int32_t y_dtype, int64_t ldy, void* stream);
 
 /*
+ * w4a4_gemm with K split across workgroups, for shapes whose output tiles
+ * alone leave the chip's workgroup slots idle (load balancing; LLaMA-2-70B w2
+ * at M = 256 has 128 tiles of 128 x 128 for 512 slots). Split s computes the
+ * group partials of its K range [s S, (s+1) S) (S whole groups' worth of
+ * 128-k stages) exactly as w4a4_gemm does and writes its fp32 sum to
+ * workspace[s][M][N]; a second kernel adds the splits in split order
+ * (deterministic) and stores Y as y_dtype. Y differs from w4a4_gemm's only by
+ * the fp32 summation order (within the same tolerance).
+ *
+ *   splits     0: the library picks (1 when the tiles fill the chip or the
+ *              few-token path applies); > 0: at most that many (clamped to
+ *              the number of groups). One split runs w4a4_gemm itself and
+ *              needs no workspace.
+ *   workspace  device memory of at least w4a4_gemm_splitk_workspace(...)
+ *              bytes, 16-byte aligned, owned by the caller, overwritten;
+ *              may be NULL when that size is 0
+ *   other arguments as for w4a4_gemm.
+ */
+w4a4_status_t w4a4_gemm_splitk(const uint8_t* xq, const float* xs, int32_t group_a,
+                               const uint8_t* wq, const float* ws, int32_t group_w,
+                               int64_t M, int64_t N, int64_t K, int32_t splits,
+                               void* workspace, int64_t workspace_bytes,
+                               void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * Workspace bytes w4a4_gemm_splitk needs for these arguments (0 when it runs
+ * unsplit), or -1 when they are invalid. Host-only; launches nothing.
+ */
+int64_t w4a4_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w,
+                                   int32_t splits);
+
+/*
  * Debug export of the integer group partials P_b of w4a4_gemm, computed by the
  * same load / unpack / matrix-core code, for the output window
  * [m0, m0+mc) x [n0, n0+nc):

@@ -137,6 +137,33 @@ def test_mxfp4_validation(lib):
     assert mp(P, P, P, P, 4, 4, 128, 0, 5, 0, 4, P, None) == E_SHAPE
 
 
+def test_splitk_plan_and_validation(lib):
+    wsb = _lib.splitk_workspace_bytes
+    # LLaMA-2-70B w2 at M = 256: 2 x 64 tiles of 128 x 128 for 512 slots -> 4 splits of 56 stages
+    assert wsb(256, 8192, 28672, 128, 128, 0) == 4 * 256 * 8192 * 4
+    assert wsb(256, 8192, 28672, 128, 128, 3) == 3 * 256 * 8192 * 4
+    assert wsb(256, 8192, 28672, 512, 128, 0) == 4 * 256 * 8192 * 4     # splits on 512-groups
+    assert wsb(256, 8192, 28672, 128, 128, 1) == 0
+    assert wsb(4096, 8192, 28672, 128, 128, 0) == 0                      # tiles fill the chip
+    assert wsb(16, 8192, 28672, 128, 128, 0) == 0                        # few-token path
+    assert wsb(300, 392, 1024, 128, 128, 100) == 8 * 300 * 392 * 4       # clamped to the 8 groups
+    assert wsb(300, 392, 1024, 1024, 128, 100) == 8 * 300 * 392 * 4      # per-token A: W groups bound it
+    assert wsb(300, 392, 1024, 256, 128, 100) == 8 * 300 * 392 * 4       # finer group 128
+    assert wsb(300, 392, 1024, 256, 256, 100) == 4 * 300 * 392 * 4      # 2-stage groups
+    assert lib.w4a4_gemm_splitk_workspace(4, 4, 96, 128, 128, 0) == -1
+    assert lib.w4a4_gemm_splitk_workspace(4, 4, 256, 128, 128, -1) == -1
+    assert lib.w4a4_gemm_splitk_workspace(4, 4, 256, 96, 128, 0) == -1
+    sk = lambda *a: _lib.status_of("w4a4_gemm_splitk", *a)
+    need = 4 * 256 * 8192 * 4
+    assert sk(P, P, 128, P, P, 128, 256, 8192, 28672, 0, P, need - 4, P, 0, 8192, None) == E_SHAPE
+    assert sk(P, P, 128, P, P, 128, 256, 8192, 28672, 0, None, need, P, 0, 8192, None) == E_NULL
+    assert sk(P, P, 128, P, P, 128, 256, 8192, 28672, 0, P + 4, need, P, 0, 8192, None) == E_ALIGN
+    assert sk(P, P, 128, P, P, 128, 256, 8192, 28672, -1, P, need, P, 0, 8192, None) == E_SHAPE
+    assert sk(P, P, 128, P, P, 128, 256, 8192, 28672, 0, P, need, P, 3, 8192, None) == E_DTYPE
+    assert sk(P, P, 96, P, P, 128, 256, 8192, 28672, 0, P, need, P, 0, 8192, None) == E_GROUP
+    assert sk(P, P, 128, P, P, 128, 0, 8192, 28672, 0, None, 0, None, 0, 8192, None) == OK
+
+
 def test_nvfp4_validation(lib):
     gs = lambda *a: _lib.status_of("nvfp4_global_scale", *a)
     assert gs(P, 4, 60, 60, P, None) == E_SHAPE          # K % 8

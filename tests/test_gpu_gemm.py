@@ -170,3 +170,49 @@ def test_llama70b_w2(M):
 @pytest.mark.parametrize("ga", [64, 128, 256, 512, 8192])
 def test_granularity_sweep(ga):
     sampled_case(4096, 8192, 8192, ga, 128)
+
+
+# ----------------------------------------------------------------- K split
+@pytest.mark.parametrize("ga,gw,splits", [(128, 128, 2), (128, 128, 3), (128, 128, 8), (64, 128, 4),
+                                          (256, 128, 5), (256, 256, 3), (1024, 128, 4), (512, 1024, 2)])
+def test_splitk_small(ga, gw, splits):
+    """Each split's partial sums are the plain kernel's over its K range; the
+    reduced Y meets the oracle bound (ragged M and N, uneven last split)."""
+    import torch
+    M, N, K = 300, 392, 1024
+    x = synth.activations(M, K, seed=ga + splits)
+    w = synth.weights(N, K, seed=gw)
+    o = ops()
+    xq, xs = o.w4a4_quantize_act(dev(x), ga)
+    wq, ws = o.w4a4_pack_weight(dev(w), gw)
+    Y, T = oracle.w4a4_gemm(*oracle.int4_quantize(x, ga), ga, *oracle.int4_quantize(w, gw), gw)
+    y = host(o.w4a4_gemm_splitk(xq, xs, ga, wq, ws, gw, splits=splits))
+    assert_y_close(y, Y, T, f"splitk ga={ga} gw={gw} splits={splits}")
+    if splits == 3:
+        y16 = o.w4a4_gemm_splitk(xq, xs, ga, wq, ws, gw, splits=splits, out_dtype=torch.float16)
+        assert_y16_close(host(y16).astype(np.float64), Y, T, "splitk fp16")
+        big = torch.full((M, N + 24), 7.0, dtype=torch.float32, device="cuda")
+        o.w4a4_gemm_splitk(xq, xs, ga, wq, ws, gw, splits=splits, out=big[:, :N])
+        b = host(big)
+        assert np.all(b[:, N:] == 7.0), "padding columns written"
+        assert_y_close(b[:, :N], Y, T, "splitk strided")
+
+
+@pytest.mark.parametrize("N,K", [(8192, 28672), (28672, 8192)])
+def test_splitk_llama70b_m256(N, K):
+    """The automatic split at M = 256 (w2: 128 tiles -> 4 splits), sampled
+    against the oracle and against the unsplit kernel's output."""
+    M, ga, gw = 256, 128, 128
+    o = ops()
+    wq, ws = _weights_dev(N, K, gw)
+    x = synth.activations(M, K, dist="t3", seed=0)
+    xq, xs = o.w4a4_quantize_act(dev(x), ga)
+    y = host(o.w4a4_gemm_splitk(xq, xs, ga, wq, ws, gw))
+    y1 = host(o.w4a4_gemm(xq, xs, ga, wq, ws, gw))
+    rows = synth.sample_rows(M, 8, seed=2)
+    cols = synth.sample_rows(N, 384, seed=3)
+    qa, sa = oracle.int4_quantize(x[rows], ga)
+    qw, sw = oracle.int4_quantize(synth.weights(N, K, seed=0, rows=cols), gw)
+    Y, T = oracle.w4a4_gemm(qa, sa, ga, qw, sw, gw)
+    assert_y_close(y[np.ix_(rows, cols)], Y, T, f"splitk M=256 N={N} K={K}")
+    assert_y_close(y1[np.ix_(rows, cols)], Y, T, f"plain M=256 N={N} K={K}")

@@ -6,7 +6,7 @@ tensor-level entry points (same names as the C ABI) are in :mod:`.ops` and are
 re-exported here on first use.
 """
 _OPS = (
-    "w4a4_quantize_act", "w4a4_pack_weight", "w4a4_gemm", "w4a4_gemm_debug_partials",
+    "w4a4_quantize_act", "w4a4_pack_weight", "w4a4_gemm", "w4a4_gemm_splitk", "w4a4_gemm_debug_partials",
     "mxfp4_quantize", "mxfp4_quantize_residual", "mxfp4_quantize_append_copy",
     "mxfp4_gemm", "mxfp4_gemm_debug_partials",
     "nvfp4_global_scale", "nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_debug_partials",

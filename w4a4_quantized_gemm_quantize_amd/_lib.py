@@ -32,6 +32,8 @@ SIGNATURES = {
     "w4a4_gemm": [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _p, _i32, _i64, _p],
     "w4a4_gemm_debug_partials": [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64,
                                  _i64, _i64, _i64, _i64, _p, _p],
+    "w4a4_gemm_splitk": [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _i32, _p, _i64,
+                         _p, _i32, _i64, _p],
     "mxfp4_quantize": [_p, _i64, _i64, _i64, _p, _p, _p],
     "mxfp4_quantize_residual": [_p, _i64, _i64, _i64, _p, _p, _p],
     "mxfp4_quantize_append_copy": [_p, _i64, _i64, _i64, _p, _p, _p],
@@ -74,8 +76,18 @@ def load_library() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.w4a4_status_str.argtypes = [ctypes.c_int]
         lib.w4a4_status_str.restype = ctypes.c_char_p
+        lib.w4a4_gemm_splitk_workspace.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
+        lib.w4a4_gemm_splitk_workspace.restype = ctypes.c_int64
         _lib = lib
         return lib
+
+
+def splitk_workspace_bytes(M: int, N: int, K: int, group_a: int, group_w: int, splits: int) -> int:
+    """Bytes of workspace w4a4_gemm_splitk needs (0: it runs unsplit); raises on invalid arguments."""
+    n = load_library().w4a4_gemm_splitk_workspace(M, N, K, group_a, group_w, splits)
+    if n < 0:
+        raise W4A4Error("w4a4_gemm_splitk_workspace", 2, "invalid arguments")
+    return n
 
 
 def call(name: str, *args) -> None:

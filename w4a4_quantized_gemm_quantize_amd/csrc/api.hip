@@ -118,6 +118,39 @@ w4a4_status_t w4a4_gemm(const uint8_t* xq, const float* xs, int32_t group_a,
   return launched();
 }
 
+int64_t w4a4_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w,
+                                   int32_t splits) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > (int64_t{1} << 24) || splits < 0) return -1;
+  if (!gemm_groups_ok(K, group_a, group_w)) return -1;
+  if (M == 0 || N == 0) return 0;
+  const w4a4::SplitPlan pl = w4a4::plan_w4a4_splitk(M, N, K, group_a, group_w, splits);
+  return pl.splits > 1 ? (int64_t)pl.splits * M * N * 4 : 0;
+}
+
+w4a4_status_t w4a4_gemm_splitk(const uint8_t* xq, const float* xs, int32_t group_a,
+                               const uint8_t* wq, const float* ws, int32_t group_w,
+                               int64_t M, int64_t N, int64_t K, int32_t splits,
+                               void* workspace, int64_t workspace_bytes,
+                               void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = gemm_common(xq, xs, group_a, wq, ws, group_w, M, N, K, g);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (splits < 0) return W4A4_E_SHAPE;
+  if ((st = check_y(y, y_dtype, N, ldy)) != W4A4_OK) return st;
+  g.y = y; g.ydtype = y_dtype; g.ldy = ldy;
+  g.m0 = 0; g.mc = M; g.n0 = 0; g.nc = N; g.partials = nullptr;
+  const w4a4::SplitPlan pl = w4a4::plan_w4a4_splitk(M, N, K, group_a, group_w, splits);
+  if (pl.splits == 1) {
+    w4a4::launch_w4a4_gemm(g, as_stream(stream));
+    return launched();
+  }
+  if (workspace_bytes < (int64_t)pl.splits * M * N * 4) return W4A4_E_SHAPE;
+  if (!workspace) return W4A4_E_NULL;
+  if (!aligned(workspace, 16)) return W4A4_E_ALIGN;
+  w4a4::launch_w4a4_gemm_splitk(g, pl, static_cast<float*>(workspace), as_stream(stream));
+  return launched();
+}
+
 w4a4_status_t w4a4_gemm_debug_partials(const uint8_t* xq, const float* xs, int32_t group_a,
                                        const uint8_t* wq, const float* ws, int32_t group_w,
                                        int64_t M, int64_t N, int64_t K,

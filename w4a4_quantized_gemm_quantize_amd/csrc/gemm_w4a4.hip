@@ -47,6 +47,8 @@
 // result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, col l%32
 // (block b of the two-block fp32 MFMA in registers 16b .. 16b+15, with operand
 // lanes 32b .. 32b+31).
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -95,6 +97,8 @@ struct Params {
   int tile_m0, tile_n0;       // first tile of the launch
   int m0, mc, n0, nc;         // partials window
   int32_t* partials;
+  int stages_per_split;       // K split: workgroup b takes stages [s S, (s+1) S), s = b / tiles
+  int64_t split_stride;       // elements between the splits' outputs (0: no split)
 };
 
 // Folding masks of the packed INT4 unit (see the C header): X carries the
@@ -155,9 +159,11 @@ void k_w4a4_gemm(Params p) {
   __shared__ __align__(16) float sSA[2][2][BM];   // [stage][64-k half][row]
   __shared__ __align__(16) float sSW[2][2][BN];
 
-  // ---- tile raster: XCD-contiguous ranges, then groups of kGroupRows tile-rows
+  // ---- tile raster: XCD-contiguous ranges, then groups of kGroupRows tile-rows;
+  // with a K split, workgroup b takes K range b / tiles of tile b % tiles
   const int nblk = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x;
+  const int split = blockIdx.x / nblk;
+  int bid = blockIdx.x - split * nblk;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   const int per_group = kGroupRows * p.tiles_n;
   const int grp = bid / per_group;
@@ -172,7 +178,10 @@ void k_w4a4_gemm(Params p) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int row_bytes = p.K >> 1;
-  const int nk = p.K / BK;
+  // this workgroup's K stages [kb, ke) (whole groups: the host splits on group
+  // boundaries)
+  const int kb = split * p.stages_per_split;
+  const int ke = min(p.K / BK, kb + p.stages_per_split);
 
   // ---- staging: each thread fetches 2 x 16 B of A and of W per stage through
   // buffer resources over the tile's rows (the host keeps a tile's rows
@@ -331,7 +340,7 @@ void k_w4a4_gemm(Params p) {
                ROWA ? sSW[B][H][wn * 64 + l32] : 0.0f,                                   \
                ROWA ? sSW[B][H][wn * 64 + 32 + l32] : 0.0f}
 
-  // One K stage from LDS buffer BUF: fetch stage min(KT+kAhead, nk-1) into
+  // One K stage from LDS buffer BUF: fetch stage min(KT+kAhead, ke-1) into
   // register set RL, compute, unpack register set RS (stage KT+1) into buffer
   // BUF^1. The
   // fetch and the store are unconditional (at the end they repeat the final
@@ -342,7 +351,7 @@ void k_w4a4_gemm(Params p) {
   // together.
 #define STAGE(KT, BUF, RL, RS)                                                           \
   {                                                                                      \
-    GLOAD(RL, min((KT) + kAhead, nk - 1));                                               \
+    GLOAD(RL, min((KT) + kAhead, ke - 1));                                               \
     const uint8_t* bA = sA[BUF];                                                         \
     const uint8_t* bW = sW[BUF];                                                         \
     const uint8_t* cA = tA[BUF];                                                         \
@@ -496,16 +505,16 @@ void k_w4a4_gemm(Params p) {
 
   Staged R0, R1;
   Staged& RX = (kAhead == 2) ? R1 : R0;
-  GLOAD(R0, 0);
+  GLOAD(R0, kb);
   LSTORE(0, R0);
-  if constexpr (kAhead == 2) GLOAD(R1, min(1, nk - 1));
+  if constexpr (kAhead == 2) GLOAD(R1, min(kb + 1, ke - 1));
   lds_barrier();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
+  int kt = kb;
+  for (; kt + 1 < ke; kt += 2) {
     STAGE(kt, 0, R0, RX);
     STAGE(kt + 1, 1, RX, R0);
   }
-  if (kt < nk) STAGE(kt, 0, R0, RX);
+  if (kt < ke) STAGE(kt, 0, R0, RX);
   if constexpr (MODE == G128 && !PARTIALS) {   // the last stage's carried tiles
     EPI_HALF(1, 1, Tc, 0);
     EPI_HALF(1, 1, Tc, 1);
@@ -528,6 +537,7 @@ void k_w4a4_gemm(Params p) {
 
   if constexpr (!PARTIALS) {
     const int esz = p.ydtype == 0 ? 4 : 2;
+    void* const yb = static_cast<uint8_t*>(p.y) + split * p.split_stride * esz;   // this split's output
     if (tile_m + BM <= p.M && (int64_t)BM * p.ldy * esz < (int64_t{1} << 31)) {
       // Every row of the tile is valid and the tile spans < 2^31 bytes: buffer
       // stores with each register's row offset in the scalar offset, no
@@ -535,7 +545,7 @@ void k_w4a4_gemm(Params p) {
       // >= N gets an offset past the resource, so its stores are dropped.
       const int ldb = (int)(p.ldy * esz);
       const __amdgpu_buffer_rsrc_t rY =
-          buffer_rsrc(static_cast<uint8_t*>(p.y) + (int64_t)tile_m * ldb, BM * ldb);
+          buffer_rsrc(static_cast<uint8_t*>(yb) + (int64_t)tile_m * ldb, BM * ldb);
       const int row0 = wm * 64 + 4 * lhi;                // tile row of register 0, block 0
       int voffY[2];
 #pragma unroll
@@ -573,11 +583,48 @@ void k_w4a4_gemm(Params p) {
             if (m < p.M && n < p.N) {
               const float v = ROWA ? acc[i][j][r] * p.sa[m] : acc[i][j][r];   // one group: xs[m]
               if (p.ydtype == 0)
-                static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = v;
+                static_cast<float*>(yb)[(int64_t)m * p.ldy + n] = v;
               else
-                static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(v);
+                static_cast<__half*>(yb)[(int64_t)m * p.ldy + n] = __float2half_rn(v);
             }
           }
+    }
+  }
+}
+
+// Sum of the K splits' fp32 outputs ws[s][M][N] in split order (deterministic),
+// stored as fp32 or fp16 into y[M][ldy]. Each thread takes four consecutive
+// columns of a row (N % 4 == 0) or one element.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int splits, int M, int N,
+                                                      int64_t split_stride, void* __restrict__ y, int ydtype,
+                                                      int64_t ldy) {
+  const int vec = (N & 3) == 0 ? 4 : 1;
+  const int64_t per_row = N / vec, total = (int64_t)M * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / per_row;
+    const int n = (int)(i - m * per_row) * vec;
+    const float* src = ws + m * N + n;
+    if (vec == 4) {
+      float4 a = *reinterpret_cast<const float4*>(src);
+      for (int s = 1; s < splits; ++s) {
+        const float4 b = *reinterpret_cast<const float4*>(src + s * split_stride);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      if (ydtype == 0) {
+        float* d = static_cast<float*>(y) + m * ldy + n;
+        d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+      } else {
+        __half* d = static_cast<__half*>(y) + m * ldy + n;
+        d[0] = __float2half_rn(a.x); d[1] = __float2half_rn(a.y);
+        d[2] = __float2half_rn(a.z); d[3] = __float2half_rn(a.w);
+      }
+    } else {
+      float a = src[0];
+      for (int s = 1; s < splits; ++s) a += src[s * split_stride];
+      if (ydtype == 0)
+        static_cast<float*>(y)[m * ldy + n] = a;
+      else
+        static_cast<__half*>(y)[m * ldy + n] = __float2half_rn(a);
     }
   }
 }
@@ -757,6 +804,8 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.n0 = (int)g.n0;
   p.nc = (int)g.nc;
   p.partials = g.partials;
+  p.stages_per_split = (int)(g.K / BK);
+  p.split_stride = 0;
   // Few tokens: the small-M path (32 x 32 tiles, K split between the waves of
   // a workgroup) when M <= 32, or M <= 64 and the 128 x 128 grid would hold
   // fewer than 128 tiles (measured crossovers on the LLaMA-2-70B FFN shapes).
@@ -786,6 +835,68 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     launch_mode<false, true>(mode, p, grid, stream);
   else
     launch_mode<false, false>(mode, p, grid, stream);
+}
+
+SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int requested) {
+  const int64_t nk = K / BK;
+  const int64_t gmin = ga < gw ? ga : gw;
+  const int64_t unit = gmin > BK ? gmin / BK : 1;        // stages per group: splits fall on group edges
+  const int64_t units = nk / unit;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  int64_t want = requested;
+  if (want <= 0) {
+    // enough workgroups for every slot of the chip (two per CU) when the
+    // tile grid alone leaves them idle; the few-token path needs no split
+    const int64_t slots = 2 * 256;
+    const bool small_path = M <= 32 || (M <= 64 && tiles < 128);
+    want = (small_path || tiles * 2 > slots) ? 1 : slots / tiles;
+  }
+  want = want < 1 ? 1 : want > units ? units : want;
+  SplitPlan pl;
+  pl.stages_per_split = (int)(((units + want - 1) / want) * unit);
+  pl.splits = (int)((nk + pl.stages_per_split - 1) / pl.stages_per_split);
+  return pl;
+}
+
+void launch_w4a4_gemm_splitk(const GemmArgs& g, const SplitPlan& pl, float* ws, hipStream_t stream) {
+  Params p;
+  p.a = g.a;
+  p.sa = static_cast<const float*>(g.sa);
+  p.w = g.w;
+  p.sw = static_cast<const float*>(g.sw);
+  p.sha = scale_shift(g.ga, g.K);
+  p.shw = scale_shift(g.gw, g.K);
+  const int64_t gmin = g.ga < g.gw ? g.ga : g.gw;
+  const int mode = gmin == 64 ? G64 : gmin == 128 ? G128 : GBIG;
+  p.stages_per_group = (int)(gmin / BK);
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  p.ksa = (int)(g.K / g.ga);
+  p.ksw = (int)(g.K / g.gw);
+  p.y = ws;                      // split s writes fp32 ws[s][M][N]
+  p.ydtype = 0;
+  p.ldy = g.N;
+  p.m0 = 0;
+  p.mc = (int)g.M;
+  p.n0 = 0;
+  p.nc = (int)g.N;
+  p.partials = nullptr;
+  p.stages_per_split = pl.stages_per_split;
+  p.split_stride = g.M * g.N;
+  p.tile_m0 = 0;
+  p.tile_n0 = 0;
+  p.tiles_m = (int)((g.M + BM - 1) / BM);
+  p.tiles_n = (int)((g.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * pl.splits));
+  if (g.ga == g.K)
+    launch_mode<false, true>(mode, p, grid, stream);
+  else
+    launch_mode<false, false>(mode, p, grid, stream);
+  const int64_t work = g.M * ((g.N & 3) == 0 ? g.N / 4 : g.N);
+  const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, stream, ws, pl.splits, (int)g.M, (int)g.N,
+                     p.split_stride, g.y, g.ydtype, g.ldy);
 }
 
 }  // namespace w4a4

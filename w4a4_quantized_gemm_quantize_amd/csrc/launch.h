@@ -32,6 +32,17 @@ struct GemmArgs {
 };
 
 void launch_w4a4_gemm(const GemmArgs& a, hipStream_t stream);
+
+// K split of the tiled W4A4 GEMM: `splits` workgroups per output tile, each
+// over `stages_per_split` 128-k stages (whole groups), fp32 partial outputs in
+// a workspace [splits][M][N], summed in split order into y.
+struct SplitPlan {
+  int splits;
+  int stages_per_split;
+};
+// requested <= 0: enough splits to fill the chip when the tile grid does not
+SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int requested);
+void launch_w4a4_gemm_splitk(const GemmArgs& a, const SplitPlan& plan, float* workspace, hipStream_t stream);
 void launch_mxfp4_gemm(const GemmArgs& a, hipStream_t stream);
 
 // NVFP4: *gscale = fl32(max|x| / 2688) (0 for rows == 0)

@@ -89,6 +89,33 @@ def w4a4_gemm(xq, xs, group_a: int, wq, ws, group_w: int, out_dtype=torch.float3
     return y
 
 
+def w4a4_gemm_splitk(xq, xs, group_a: int, wq, ws, group_w: int, splits: int = 0,
+                     out_dtype=torch.float32, out=None, workspace=None):
+    """w4a4_gemm with K split across workgroups (``splits=0``: the library
+    picks). The fp32 workspace is allocated here with torch unless given."""
+    from ._lib import splitk_workspace_bytes
+    for t, n in ((xq, "xq"), (wq, "wq")):
+        _need(t, torch.uint8, n)
+    _need(xs, torch.float32, "xs")
+    _need(ws, torch.float32, "ws")
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("K of xq and wq differ")
+    _need_scales(xs, K, group_a, M, "xs")
+    _need_scales(ws, K, group_w, N, "ws")
+    nbytes = splitk_workspace_bytes(M, N, K, group_a, group_w, splits)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 16) // 4,), dtype=torch.float32, device=xq.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must hold {nbytes} bytes")
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    call("w4a4_gemm_splitk", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(), group_w,
+         M, N, K, splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+         y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
+    return y
+
+
 def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int, mc: int, n0: int, nc: int):
     """Exact int32 group partials P_b for the window; shape [K/g, mc, nc]."""
     M, K = xq.shape[0], xq.shape[1] * 2

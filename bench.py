@@ -241,6 +241,9 @@ def main() -> int:
             wq, ws = ops.w4a4_pack_weight(w, gw)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             xs = torch.empty((K // ga, M), dtype=torch.float32, device=dev)
+            # K-split workspace when the tiles alone would leave CUs idle (small M); none at M = 4096
+            nws = _lib.splitk_workspace_bytes(M, N, K, ga, gw, 0)
+            wsp = torch.empty((max(nws, 16) // 4,), dtype=torch.float32, device=dev)
         elif fmt == "mxfp4":
             wq, ws = ops.mxfp4_quantize(w)
             xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
@@ -260,6 +263,8 @@ def main() -> int:
         del w
         y = torch.empty((M, N), dtype=ydt, device=dev)
         layers.append(dict(K=K, N=N, x=x, wq=wq, ws=ws, xq=xq, xs=xs, y=y))
+        if fmt == "int4":
+            layers[-1].update(wsp=wsp)
         if fmt == "nvfp4":
             layers[-1].update(gx=gxt, gw=gwt)
         log(f"linear {li}: K={K} N={N} ready")
@@ -280,7 +285,7 @@ def main() -> int:
             if ev is not None:
                 ev[li][1].record()
             if fmt == "int4":
-                ops.w4a4_gemm(L["xq"], L["xs"], ga, L["wq"], L["ws"], gw, out=L["y"])
+                ops.w4a4_gemm_splitk(L["xq"], L["xs"], ga, L["wq"], L["ws"], gw, out=L["y"], workspace=L["wsp"])
             elif fmt == "nvfp4":
                 ops.nvfp4_gemm(L["xq"], L["xs"], L["gx"], L["wq"], L["ws"], L["gw"], out=L["y"])
             else:

@@ -135,6 +135,42 @@ def test_quantize_exhaustive_fp16():
         nv_check(x, what="exhaustive band")
 
 
+def _every_scale_blocks(sg):
+    """Blocks [a_b, x_1..x_15] where a_b = fp16(fl32(6 s_g) * E4M3 value b) for
+    every E4M3 byte b = 1..126 (so the block gets scale byte b: the fp16
+    rounding of a_b is far finer than E4M3 spacing) and the x run over every
+    fp16 value with |x| <= a_b, both signs; zero-padded to rows of 256."""
+    d = np.float32(np.float32(6) * np.float32(sg))
+    vals = oracle.e4m3_decode(np.arange(1, 0x7F))
+    pos = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    blocks = []
+    for v in vals:
+        a = np.float16(d * np.float32(v))
+        if not np.isfinite(a) or a == 0:
+            continue
+        xs = pos[pos <= np.float32(a)]
+        xs = np.concatenate([xs, -xs[1:]]).astype(np.float16)
+        n = -(-xs.size // 15)
+        pad = np.zeros(n * 15, np.float16)
+        pad[:xs.size] = xs
+        blk = np.empty((n, 16), np.float16)
+        blk[:, 0] = a
+        blk[:, 1:] = pad.reshape(n, 15)
+        blocks.append(blk)
+    flat = np.concatenate(blocks).reshape(-1)
+    flat = np.concatenate([flat, np.zeros((-flat.size) % 256, np.float16)])
+    return flat.reshape(-1, 256)
+
+
+@pytest.mark.parametrize("sg", [2.0 ** -4, 0.37])
+def test_quantize_every_scale_every_x(sg):
+    """Every reachable block scale (126 E4M3 bytes for this global scale) with
+    every fp16 input at or below its block's absmax: every code decision the
+    quantizer can take under that global scale, bit-exact."""
+    x = _every_scale_blocks(sg)
+    nv_check(x, sg=np.float32(sg), what=f"every scale x every x, sg={sg}")
+
+
 # ------------------------------------------------------------------ GEMM
 def run_case(M, N, K, seed=0, window=None, dist="t3", check_fp16=False):
     import torch

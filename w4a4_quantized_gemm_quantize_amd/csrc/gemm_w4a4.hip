@@ -642,7 +642,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // summed through LDS in a fixed order (wave 0, then 1, 2, ...): deterministic.
 constexpr int SM_TILE = 32;
 
-constexpr int SM_RING = 8;          // 64-k steps in flight per wave
+constexpr int SM_RING = 8;          // 64-k steps in flight per wave (a multiple of 4)
+static_assert(SM_RING % 4 == 0, "the ring is refilled four steps at a time");
 
 // 32 packed codes (16 B = two units X0 Y0 X1 Y1) -> the lane's FP6 operand in
 // registers: the words unpack_store() writes to LDS, main part then tail.
@@ -720,7 +721,14 @@ __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_gemm_small(Params p, int
           }
           P = zero16;
         }
-        if (h + SM_RING + u < h1) load(ring[u], h + SM_RING + u);
+      }
+      // refill four steps at once: a row's four 32-byte pieces of one 128-byte
+      // W line go out back to back (one per step refilled one at a time
+      // streamed W 7-19 % slower at M = 1)
+      if ((u & 3) == 3) {
+#pragma unroll
+        for (int v = u - 3; v <= u; ++v)
+          if (h + SM_RING + v < h1) load(ring[v], h + SM_RING + v);
       }
     }
   }

@@ -133,7 +133,7 @@ w4a4_status_t w4a4_gemm(const uint8_t* xq, const float* xs, int32_t group_a,
 /*
  * w4a4_gemm with K split across workgroups, for shapes whose output tiles
  * alone leave the chip's workgroup slots idle (load balancing; LLaMA-2-70B w2
- * at M = 256 has 128 tiles of 128 x 128 for 512 slots). Split s computes the
+ * at M = 256 has 64 tiles of 256 x 128 for 256 CUs). Split s computes the
  * group partials of its K range [s S, (s+1) S) (S whole groups' worth of
  * 128-k stages) exactly as w4a4_gemm does and writes its fp32 sum to
  * workspace[s][M][N]; a second kernel adds the splits in split order

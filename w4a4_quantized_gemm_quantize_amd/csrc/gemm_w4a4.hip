@@ -24,9 +24,12 @@
 //     layout of the partials.
 //   * Epilogue per output per group: acc = fma(P, t, acc).
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; tile 128 x 128 outputs,
-// K stage 128 (two MFMA k-steps), double-buffered LDS (50 KB), two workgroups
-// per CU (two waves per SIMD). The staging threads fetch stage kt+2 while
+// Workgroup: TM x 128 output tile, 2 TM threads = TM / 32 waves in a
+// (TM / 64) x 2 grid of 64 x 64, K stage 128 (two MFMA k-steps),
+// double-buffered LDS. TM = 256 (82 KB, one workgroup per CU) stages a
+// quarter fewer rows per MAC than TM = 128 (50 KB, two per CU), which serves
+// M <= 128, where a 256-row tile would be half empty. Either way two waves per
+// SIMD. The staging threads fetch stage kt+2 while
 // stage kt is computed and stage kt+1 is unpacked (two register sets), and the
 // stage barrier orders LDS only, so no wait drains those loads.
 // With g = 128 a stage is one group and runs as a software pipeline of ten
@@ -59,7 +62,7 @@ namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int BN = 128, BK = 128;
 constexpr int ROW_BYTES = BK / 2;   // packed bytes per row per stage
 // LDS row of one 128-k stage: four 32-code FP6 operand chunks of 24 bytes,
 // each split into a 16-byte main part and an 8-byte tail, kept in two arrays
@@ -72,7 +75,6 @@ constexpr int PM = 64;              // main part: 4 x 16 B
 constexpr int PT = 32;              // tail part: 4 x 8 B
 __device__ __forceinline__ int main_off(int row, int chunk) { return row * PM + 16 * (chunk ^ ((row >> 2) & 3)); }
 __device__ __forceinline__ int tail_off(int row, int chunk) { return row * PT + 8 * (chunk ^ ((row >> 3) & 3)); }
-constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;       // tile-rows per raster group
 constexpr int kUnitScale = 127 + 3; // E8M0 2^3: FP6 E2M3 [s 00 m] = +-m/8, times 2^3 = +-m
 constexpr int kFmtFp6 = 2;          // cbsz / blgp operand format code for FP6 E2M3
@@ -149,15 +151,25 @@ __device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c) {
 // mixed-granularity mode). Then s_a[m] is common to every group and factors
 // out of the sum: the epilogue is acc = fma(P, s_w[n], acc) with s_w[n] a
 // per-lane constant (no scale-product MFMA) and the store multiplies by s_a[m].
-template <bool PARTIALS, int MODE, bool ROWA>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool PARTIALS, int MODE, bool ROWA, int TM>
+__global__ __launch_bounds__(2 * TM) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_w4a4_gemm(Params p) {
+  static_assert(TM == 128 || TM == 256, "tile heights");
+  constexpr int BM = TM, kThreads = 2 * TM;
+  constexpr int HALF = TM / 2;          // A rows staged per thread: r, r + HALF
+  constexpr bool W2 = TM == 128;        // W rows staged per thread: r (and r + 64)
   __shared__ __align__(16) uint8_t sA[2][BM * PM];   // FP6 operand main parts
   __shared__ __align__(16) uint8_t sW[2][BN * PM];
   __shared__ __align__(16) uint8_t tA[2][BM * PT];   // FP6 operand tails
   __shared__ __align__(16) uint8_t tW[2][BN * PT];
   __shared__ __align__(16) float sSA[2][2][BM];   // [stage][64-k half][row]
   __shared__ __align__(16) float sSW[2][2][BN];
+  // scale stores of the threads past the tile's BM + BN scale rows (TM = 256:
+  // waves 6, 7), never read: a destination for them keeps the staging store
+  // branch-free (a branch in the pipelined stage made the compiler spill
+  // ~1 KB per lane)
+  constexpr int kSpare = kThreads - BM - BN;
+  __shared__ __align__(16) float sSX[2][2][kSpare > 0 ? kSpare : 1];
 
   // ---- tile raster: XCD-contiguous ranges, then groups of kGroupRows tile-rows;
   // with a K split, workgroup b takes K range b / tiles of tile b % tiles
@@ -183,23 +195,26 @@ void k_w4a4_gemm(Params p) {
   const int kb = split * p.stages_per_split;
   const int ke = min(p.K / BK, kb + p.stages_per_split);
 
-  // ---- staging: each thread fetches 2 x 16 B of A and of W per stage through
+  // ---- staging: each thread fetches 2 x 16 B of A (rows r, r + HALF) and
+  // 16 B of W (row r; TM = 128: also r + 64) per stage through
   // buffer resources over the tile's rows (the host keeps a tile's rows
   // < 2^31 bytes), the stage's k offset in the scalar offset
   const int a_rows = min(BM, p.M - tile_m), w_rows = min(BN, p.N - tile_n);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
   const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
   const int vA0 = min(tid >> 2, a_rows - 1) * row_bytes + (tid & 3) * 16;
-  const int vA1 = min(64 + (tid >> 2), a_rows - 1) * row_bytes + (tid & 3) * 16;
+  const int vA1 = min(HALF + (tid >> 2), a_rows - 1) * row_bytes + (tid & 3) * 16;
   const int vW0 = min(tid >> 2, w_rows - 1) * row_bytes + (tid & 3) * 16;
   const int vW1 = min(64 + (tid >> 2), w_rows - 1) * row_bytes + (tid & 3) * 16;
   const int st0 = main_off(tid >> 2, tid & 3);      // chunk tid & 3 of row tid >> 2
-  const int st1 = st0 + 64 * PM;                     // row + 64: same swizzle
+  const int st1 = st0 + HALF * PM;                   // row + HALF: same swizzle
   const int tt0 = tail_off(tid >> 2, tid & 3);
-  const int tt1 = tt0 + 64 * PT;
-  // scales: waves 0, 1 (threads 0..127) stage A-row scales, waves 2, 3 W-row
-  // scales; group-major, so consecutive threads read consecutive rows of one
-  // group. The choice is uniform per wave, so each wave's resource is scalar.
+  const int tt1 = tt0 + HALF * PT;
+  // scales: threads [0, BM) stage A-row scales, [BM, BM + 128) W-row scales
+  // and any rest (TM = 256: waves 6, 7) a repeat of the last W row into a
+  // dummy array;
+  // group-major, so consecutive threads read consecutive rows of one group.
+  // The choice is uniform per wave, so each wave's resource is scalar.
   const bool s_is_a = __builtin_amdgcn_readfirstlane(tid) < BM;
   const int srow = s_is_a ? tid : tid - BM;
   const float* sbase = s_is_a ? p.sa + tile_m : p.sw + tile_n;   // this tile's rows of group 0
@@ -207,7 +222,8 @@ void k_w4a4_gemm(Params p) {
   const int snr = s_is_a ? a_rows : w_rows;
   const int vS = 4 * min(srow, snr - 1);
   const int ssh = s_is_a ? p.sha : p.shw;
-  float* sS = s_is_a ? &sSA[0][0][srow] : &sSW[0][0][srow];
+  float* sS = s_is_a ? &sSA[0][0][srow] : (kSpare <= 0 || srow < BN) ? &sSW[0][0][srow] : &sSX[0][0][srow - BN];
+  const int sstr = s_is_a ? BM : BN;          // floats between the [half] rows of this thread's array
 
   // Two register sets of staged global data: stage kt+2 is fetched while
   // stage kt is computed and stage kt+1 (fetched one stage earlier) is
@@ -229,7 +245,7 @@ void k_w4a4_gemm(Params p) {
     R.a0 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rA, vA0, off_, 0)); \
     R.a1 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rA, vA1, off_, 0)); \
     R.w0 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, vW0, off_, 0)); \
-    R.w1 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, vW1, off_, 0)); \
+    if constexpr (W2) R.w1 = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, vW1, off_, 0)); \
     R.s0 = load_scale((2 * (KT)) >> ssh);                             \
     /* groups >= 128: both 64-k halves share a group */               \
     R.s1 = (MODE == G64) ? load_scale((2 * (KT) + 1) >> ssh) : R.s0;  \
@@ -239,11 +255,12 @@ void k_w4a4_gemm(Params p) {
 #define LST_A0(BUF, R) unpack_store(&sA[BUF][st0], &tA[BUF][tt0], R.a0)
 #define LST_A1(BUF, R) unpack_store(&sA[BUF][st1], &tA[BUF][tt1], R.a1)
 #define LST_W0(BUF, R) unpack_store(&sW[BUF][st0], &tW[BUF][tt0], R.w0)
-#define LST_W1(BUF, R) unpack_store(&sW[BUF][st1], &tW[BUF][tt1], R.w1)
+#define LST_W1(BUF, R) \
+  if constexpr (W2) unpack_store(&sW[BUF][st1], &tW[BUF][tt1], R.w1)
 #define LST_S(BUF, R)                                                 \
   {                                                                   \
-    sS[(BUF) * 2 * BM] = R.s0;                                        \
-    sS[(BUF) * 2 * BM + BM] = R.s1;                                   \
+    sS[(BUF) * 2 * sstr] = R.s0;                                      \
+    sS[(BUF) * 2 * sstr + sstr] = R.s1;                               \
   }
 #define LSTORE(BUF, R)                                                \
   {                                                                   \
@@ -630,7 +647,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 // ---- Small M (decode) ------------------------------------------------------
-// With few tokens the 128 x 128 tiling leaves most CUs idle (LLaMA-2-70B w2 at
+// With few tokens the big tiling leaves most CUs idle (LLaMA-2-70B w2 at
 // M = 1: 64 tiles for 256 CUs, each walking all of K) and the GEMM is bound by
 // streaming W. This path gives each workgroup one 32 x 32 output tile (one
 // MFMA block) and splits K between its NW waves in whole groups: wave w
@@ -777,13 +794,26 @@ int scale_shift(int64_t group, int64_t K) {
   return s;
 }
 
-template <bool PARTIALS, bool ROWA>
-void launch_mode(int mode, const Params& p, dim3 grid, hipStream_t stream) {
+template <bool PARTIALS, bool ROWA, int TM>
+void launch_mode_tm(int mode, const Params& p, dim3 grid, hipStream_t stream) {
+  const dim3 block(2 * TM);
   switch (mode) {
-    case G64: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G64, ROWA>), grid, dim3(kThreads), 0, stream, p); return;
-    case G128: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G128, ROWA>), grid, dim3(kThreads), 0, stream, p); return;
-    default: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, GBIG, ROWA>), grid, dim3(kThreads), 0, stream, p); return;
+    case G64: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G64, ROWA, TM>), grid, block, 0, stream, p); return;
+    case G128: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, G128, ROWA, TM>), grid, block, 0, stream, p); return;
+    default: hipLaunchKernelGGL((k_w4a4_gemm<PARTIALS, GBIG, ROWA, TM>), grid, block, 0, stream, p); return;
   }
+}
+
+// Tile height of the tiled kernel for M rows: 128 up to 128 rows (a 256-row
+// tile would be half empty), else 256.
+int tile_rows(int64_t M) { return M > 128 ? 256 : 128; }
+
+template <bool PARTIALS, bool ROWA>
+void launch_mode(int mode, int tm, const Params& p, dim3 grid, hipStream_t stream) {
+  if (tm == 256)
+    launch_mode_tm<PARTIALS, ROWA, 256>(mode, p, grid, stream);
+  else
+    launch_mode_tm<PARTIALS, ROWA, 128>(mode, p, grid, stream);
 }
 
 }  // namespace
@@ -815,9 +845,9 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   p.stages_per_split = (int)(g.K / BK);
   p.split_stride = 0;
   // Few tokens: the small-M path (32 x 32 tiles, K split between the waves of
-  // a workgroup) when M <= 32, or M <= 64 and the 128 x 128 grid would hold
-  // fewer than 128 tiles (measured crossovers on the LLaMA-2-70B FFN shapes).
-  const int64_t big_tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  // a workgroup) when M <= 32, or M <= 64 and the grid (one tile row, N / 128
+  // tiles) would hold fewer than 128 tiles (measured crossovers on the LLaMA-2-70B FFN shapes).
+  const int64_t big_tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
   if (g.M <= 32 || (g.M <= 64 && big_tiles < 128)) {
     p.tile_m0 = (int)(g.m0 / SM_TILE);
     p.tile_n0 = (int)(g.n0 / SM_TILE);
@@ -832,17 +862,18 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
       launch_small<4>(g, p, grid, spg, stream);
     return;
   }
+  const int BM = tile_rows(g.mc);
   p.tile_m0 = (int)(g.m0 / BM);
   p.tile_n0 = (int)(g.n0 / BN);
   p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
   p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   if (g.partials)
-    launch_mode<true, false>(mode, p, grid, stream);
+    launch_mode<true, false>(mode, BM, p, grid, stream);
   else if (g.ga == g.K)
-    launch_mode<false, true>(mode, p, grid, stream);
+    launch_mode<false, true>(mode, BM, p, grid, stream);
   else
-    launch_mode<false, false>(mode, p, grid, stream);
+    launch_mode<false, false>(mode, BM, p, grid, stream);
 }
 
 SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int requested) {
@@ -850,12 +881,14 @@ SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int 
   const int64_t gmin = ga < gw ? ga : gw;
   const int64_t unit = gmin > BK ? gmin / BK : 1;        // stages per group: splits fall on group edges
   const int64_t units = nk / unit;
+  const int BM = tile_rows(M);
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   int64_t want = requested;
   if (want <= 0) {
-    // enough workgroups for every slot of the chip (two per CU) when the
-    // tile grid alone leaves them idle; the few-token path needs no split
-    const int64_t slots = 2 * 256;
+    // enough workgroups for every slot of the chip (one 256-row or two
+    // 128-row tiles per CU) when the tile grid alone leaves them idle; the
+    // few-token path needs no split
+    const int64_t slots = BM == 256 ? 256 : 512;
     const bool small_path = M <= 32 || (M <= 64 && tiles < 128);
     want = (small_path || tiles * 2 > slots) ? 1 : slots / tiles;
   }
@@ -894,13 +927,14 @@ void launch_w4a4_gemm_splitk(const GemmArgs& g, const SplitPlan& pl, float* ws, 
   p.split_stride = g.M * g.N;
   p.tile_m0 = 0;
   p.tile_n0 = 0;
+  const int BM = tile_rows(g.M);
   p.tiles_m = (int)((g.M + BM - 1) / BM);
   p.tiles_n = (int)((g.N + BN - 1) / BN);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * pl.splits));
   if (g.ga == g.K)
-    launch_mode<false, true>(mode, p, grid, stream);
+    launch_mode<false, true>(mode, BM, p, grid, stream);
   else
-    launch_mode<false, false>(mode, p, grid, stream);
+    launch_mode<false, false>(mode, BM, p, grid, stream);
   const int64_t work = g.M * ((g.N & 3) == 0 ? g.N / 4 : g.N);
   const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 8192);
   hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, stream, ws, pl.splits, (int)g.M, (int)g.N,

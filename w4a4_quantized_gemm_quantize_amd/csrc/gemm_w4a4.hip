@@ -804,9 +804,11 @@ void launch_mode_tm(int mode, const Params& p, dim3 grid, hipStream_t stream) {
   }
 }
 
-// Tile height of the tiled kernel for M rows: 128 up to 128 rows (a 256-row
-// tile would be half empty), else 256.
-int tile_rows(int64_t M) { return M > 128 ? 256 : 128; }
+// Tile height of the tiled kernel for M rows and smallest group gmin: 128 up
+// to 128 rows (a 256-row tile would be half empty) and for g = 64 (its
+// one-stage-ahead loads and per-k-step epilogue measured 6-10 % slower on 256
+// rows at LLaMA-2-70B FFN shapes), else 256.
+int tile_rows(int64_t M, int64_t gmin) { return M > 128 && gmin != 64 ? 256 : 128; }
 
 template <bool PARTIALS, bool ROWA>
 void launch_mode(int mode, int tm, const Params& p, dim3 grid, hipStream_t stream) {
@@ -862,7 +864,7 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
       launch_small<4>(g, p, grid, spg, stream);
     return;
   }
-  const int BM = tile_rows(g.mc);
+  const int BM = tile_rows(g.mc, gmin);
   p.tile_m0 = (int)(g.m0 / BM);
   p.tile_n0 = (int)(g.n0 / BN);
   p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
@@ -881,7 +883,7 @@ SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int 
   const int64_t gmin = ga < gw ? ga : gw;
   const int64_t unit = gmin > BK ? gmin / BK : 1;        // stages per group: splits fall on group edges
   const int64_t units = nk / unit;
-  const int BM = tile_rows(M);
+  const int BM = tile_rows(M, gmin);
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   int64_t want = requested;
   if (want <= 0) {
@@ -927,7 +929,7 @@ void launch_w4a4_gemm_splitk(const GemmArgs& g, const SplitPlan& pl, float* ws, 
   p.split_stride = g.M * g.N;
   p.tile_m0 = 0;
   p.tile_n0 = 0;
-  const int BM = tile_rows(g.M);
+  const int BM = tile_rows(g.M, gmin);
   p.tiles_m = (int)((g.M + BM - 1) / BM);
   p.tiles_n = (int)((g.N + BN - 1) / BN);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * pl.splits));

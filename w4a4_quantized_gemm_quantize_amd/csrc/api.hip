@@ -35,6 +35,10 @@ bool gemm_group_ok(int64_t K, int32_t g) {
 // for them to be exact integers.
 constexpr int32_t kMaxPartialGroup = 1 << 18;
 
+// Longest K of the INT4 GEMM: a 256-row tile of packed codes (K / 2 bytes per
+// row) must span < 2^31 bytes for the kernel's 32-bit buffer offsets.
+constexpr int64_t kMaxGemmK = int64_t{1} << 23;
+
 bool gemm_groups_ok(int64_t K, int32_t ga, int32_t gw) {
   if (!gemm_group_ok(K, ga) || !gemm_group_ok(K, gw)) return false;
   const int32_t lo = ga < gw ? ga : gw, hi = ga < gw ? gw : ga;
@@ -91,9 +95,9 @@ w4a4_status_t w4a4_pack_weight(const void* w, int64_t N, int64_t K, int32_t grou
 static w4a4_status_t gemm_common(const uint8_t* xq, const float* xs, int32_t ga,
                                  const uint8_t* wq, const float* ws, int32_t gw,
                                  int64_t M, int64_t N, int64_t K, GemmArgs& g) {
-  // K <= 2^24: a 128-row tile then spans < 2^31 bytes, the kernel's 32-bit
-  // buffer offsets
-  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > (int64_t{1} << 24)) return W4A4_E_SHAPE;
+  // K <= 2^23: a 256-row tile then spans <= 2^30 bytes, within the kernel's
+  // signed 32-bit buffer sizes and offsets
+  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > kMaxGemmK) return W4A4_E_SHAPE;
   if (!gemm_groups_ok(K, ga, gw)) return W4A4_E_GROUP;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!xq || !xs || !wq || !ws) return W4A4_E_NULL;
@@ -120,7 +124,7 @@ w4a4_status_t w4a4_gemm(const uint8_t* xq, const float* xs, int32_t group_a,
 
 int64_t w4a4_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w,
                                    int32_t splits) {
-  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > (int64_t{1} << 24) || splits < 0) return -1;
+  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > kMaxGemmK || splits < 0) return -1;
   if (!gemm_groups_ok(K, group_a, group_w)) return -1;
   if (M == 0 || N == 0) return 0;
   const w4a4::SplitPlan pl = w4a4::plan_w4a4_splitk(M, N, K, group_a, group_w, splits);

@@ -32,9 +32,9 @@
 // power of two, so it runs with 1.0) and four packed fp16 multiplies by s_b.
 // Loads and ring follow the MXFP4 kernel: 256 x 256 workgroup tiles, 256-deep
 // K stages in a 2-stage LDS ring filled by direct global->LDS loads, 64-bank
-// row swizzle. The waves are 2 x 2 of 128 x 128 each, one per SIMD with the
-// whole register file (256 accumulators): per fp16 MFMA a wave then converts
-// half an operand fragment, against one with 128 x 64 waves. In one 64-k step lane l holds
+// row swizzle. The eight waves are 2 x 4 of 128 x 64 each (4 x 2 blocks of
+// 32 x 32), two per SIMD, so one wave's conversions run under the other's
+// MFMAs. In one 64-k step lane l holds
 // the 32 codes of k = 32 (l/32) .. +32 of its row (16 bytes); its four
 // 16-deep MFMAs take words 0..3 of them, the same words of the A and the W
 // lane, so each MFMA sums a consistent set of 16 k and the four together the
@@ -192,8 +192,8 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Workgroup tile 256 x 256, waves 2 x 2 (128 x 128 each = 4 x 4 blocks of
-// 32 x 32), 256-deep K stages in a 2-stage ring: stage kt + 1 loads while
+// Workgroup tile 256 x 256, waves 2 x 4 (128 x 64 each = 4 x 2 blocks of
+// 32 x 32, two waves per SIMD), 256-deep K stages in a 2-stage ring: stage kt + 1 loads while
 // stage kt is computed. A stage holds 512 rows of 128 packed bytes (A rows,
 // then W rows; each wave-wide 1 KB load covers 8 rows; the 8 16-byte slots of
 // a row XOR-swizzled with (row >> 1) & 7 so the 16 lanes reading one slot of

@@ -30,6 +30,36 @@ def _ydtype(dtype) -> int:
     raise TypeError("output dtype must be torch.float32 or torch.float16")
 
 
+def _check_out(t, name: str, shape, dtype, device, row_stride_ok: bool = False) -> None:
+    """A caller-supplied output buffer must have exactly the shape, dtype and
+    device the kernel writes (the C ABI cannot see buffer sizes: an undersized
+    or foreign buffer would be written past its end). ``row_stride_ok``: a 2-D
+    output may have a row stride above its width (unit column stride)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if row_stride_ok and t.dim() == 2:
+        if t.numel() and (t.stride(1) != 1 or t.stride(0) < t.shape[1]):
+            raise ValueError(f"{name} must have unit column stride and row stride >= its width")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _y_out(out, M: int, N: int, out_dtype, device) -> torch.Tensor:
+    """The GEMM output: a new [M, N] tensor, or the caller's, checked (fp32 or
+    fp16, [M, N] on the inputs' device, unit column stride, row stride >= N)."""
+    if out is None:
+        return torch.empty((M, N), dtype=out_dtype, device=device)
+    _ydtype(out.dtype)
+    _check_out(out, "out", (M, N), out.dtype, device, row_stride_ok=True)
+    return out
+
+
 def _need_scales(s: torch.Tensor, K: int, group: int, rows: int, name: str) -> None:
     """Group-major INT4 scales: contiguous, K/group x rows floats."""
     if group > 0 and K % group == 0 and (not s.is_contiguous() or s.numel() != (K // group) * rows):
@@ -51,6 +81,8 @@ def w4a4_quantize_act(x: torch.Tensor, group: int = 128, out=None):
         xs = torch.empty((max(K // max(group, 1), 0), M), dtype=torch.float32, device=x.device)
     else:
         xq, xs = out
+        _check_out(xq, "xq", (M, K // 2), torch.uint8, x.device)
+        _check_out(xs, "xs", (K // max(group, 1), M), torch.float32, x.device)
     call("w4a4_quantize_act", x.data_ptr(), M, K, x.stride(0), group,
          xq.data_ptr(), xs.data_ptr(), _stream(x))
     return xq, xs
@@ -68,6 +100,8 @@ def w4a4_pack_weight(w: torch.Tensor, group: int = 128, out=None):
         ws = torch.empty((max(K // max(group, 1), 0), N), dtype=torch.float32, device=w.device)
     else:
         wq, ws = out
+        _check_out(wq, "wq", (N, K // 2), torch.uint8, w.device)
+        _check_out(ws, "ws", (K // max(group, 1), N), torch.float32, w.device)
     call("w4a4_pack_weight", w.data_ptr(), N, K, group, wq.data_ptr(), ws.data_ptr(), _stream(w))
     return wq, ws
 
@@ -83,7 +117,7 @@ def w4a4_gemm(xq, xs, group_a: int, wq, ws, group_w: int, out_dtype=torch.float3
         raise ValueError("K of xq and wq differ")
     _need_scales(xs, K, group_a, M, "xs")
     _need_scales(ws, K, group_w, N, "ws")
-    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    y = _y_out(out, M, N, out_dtype, xq.device)
     call("w4a4_gemm", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(), group_w,
          M, N, K, y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
     return y
@@ -107,9 +141,14 @@ def w4a4_gemm_splitk(xq, xs, group_a: int, wq, ws, group_w: int, splits: int = 0
     nbytes = splitk_workspace_bytes(M, N, K, group_a, group_w, splits)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 16) // 4,), dtype=torch.float32, device=xq.device)
-    elif workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError(f"workspace must hold {nbytes} bytes")
-    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    else:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != xq.device:
+            raise ValueError("workspace must be a tensor on the inputs' device")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace must hold {nbytes} bytes")
+    y = _y_out(out, M, N, out_dtype, xq.device)
     call("w4a4_gemm_splitk", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(), group_w,
          M, N, K, splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
          y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
@@ -118,9 +157,18 @@ def w4a4_gemm_splitk(xq, xs, group_a: int, wq, ws, group_w: int, splits: int = 0
 
 def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int, mc: int, n0: int, nc: int):
     """Exact int32 group partials P_b for the window; shape [K/g, mc, nc]."""
+    for t, dt, n in ((xq, torch.uint8, "xq"), (wq, torch.uint8, "wq"),
+                     (xs, torch.float32, "xs"), (ws, torch.float32, "ws")):
+        _need(t, dt, n)
     M, K = xq.shape[0], xq.shape[1] * 2
     N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("K of xq and wq differ")
+    _need_scales(xs, K, group_a, M, "xs")
+    _need_scales(ws, K, group_w, N, "ws")
     g = min(group_a, group_w)
+    if g <= 0 or K % g:
+        raise ValueError("the finer group must divide K")
     part = torch.empty((K // g, mc, nc), dtype=torch.int32, device=xq.device)
     call("w4a4_gemm_debug_partials", xq.data_ptr(), xs.data_ptr(), group_a, wq.data_ptr(), ws.data_ptr(),
          group_w, M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
@@ -178,8 +226,8 @@ def mxfp4_quantize(x: torch.Tensor, out=None):
         e = torch.empty((R * (K // 32),), dtype=torch.uint8, device=x.device)
     else:
         q, e = out
-    if e.numel() != R * (K // 32) or not e.is_contiguous():
-        raise ValueError("e8m0 must be contiguous with rows*K/32 bytes")
+        _check_out(q, "codes", (R, K // 2), torch.uint8, x.device)
+        _check_out(e, "e8m0", (R * (K // 32),), torch.uint8, x.device)
     call("mxfp4_quantize", x.data_ptr(), R, K, x.stride(0), q.data_ptr(), e.data_ptr(), _stream(x))
     return q, e
 
@@ -194,8 +242,8 @@ def _mxfp4_quantize_wide(fn: str, x: torch.Tensor, out):
         e = torch.empty((R * (2 * K // 32),), dtype=torch.uint8, device=x.device)
     else:
         q, e = out
-    if e.numel() != R * (2 * K // 32) or not e.is_contiguous():
-        raise ValueError("e8m0 must be contiguous with rows*2K/32 bytes")
+        _check_out(q, "codes", (R, K), torch.uint8, x.device)
+        _check_out(e, "e8m0", (R * (2 * K // 32),), torch.uint8, x.device)
     call(fn, x.data_ptr(), R, K, x.stride(0), q.data_ptr(), e.data_ptr(), _stream(x))
     return q, e
 
@@ -213,8 +261,7 @@ def mxfp4_quantize_append_copy(w: torch.Tensor, out=None):
     return _mxfp4_quantize_wide("mxfp4_quantize_append_copy", w, out)
 
 
-def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
-    """Y[M, N] = block-scaled FP4 GEMM of MXFP4 X and W."""
+def _mx_shapes(xq, xe, wq, we):
     for t, n in ((xq, "xq"), (xe, "xe"), (wq, "wq"), (we, "we")):
         _need(t, torch.uint8, n)
     M, K = xq.shape[0], xq.shape[1] * 2
@@ -223,7 +270,13 @@ def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
         raise ValueError("K of xq and wq differ")
     if xe.numel() != M * (K // 32) or we.numel() != N * (K // 32):
         raise ValueError("scale tensors must hold rows*K/32 bytes (panel layout)")
-    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    return M, N, K
+
+
+def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
+    """Y[M, N] = block-scaled FP4 GEMM of MXFP4 X and W."""
+    M, N, K = _mx_shapes(xq, xe, wq, we)
+    y = _y_out(out, M, N, out_dtype, xq.device)
     call("mxfp4_gemm", xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(), M, N, K,
          y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
     return y
@@ -231,8 +284,7 @@ def mxfp4_gemm(xq, xe, wq, we, out_dtype=torch.float32, out=None):
 
 def mxfp4_gemm_debug_partials(xq, xe, wq, we, m0: int, mc: int, n0: int, nc: int):
     """Exact int32 block integers I_b = sum (2va)(2vw) for the window; [K/32, mc, nc]."""
-    M, K = xq.shape[0], xq.shape[1] * 2
-    N = wq.shape[0]
+    M, N, K = _mx_shapes(xq, xe, wq, we)
     part = torch.empty((K // 32, mc, nc), dtype=torch.int32, device=xq.device)
     call("mxfp4_gemm_debug_partials", xq.data_ptr(), xe.data_ptr(), wq.data_ptr(), we.data_ptr(),
          M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
@@ -288,7 +340,7 @@ def nvfp4_global_scale(x: torch.Tensor, out=None):
     if x.dim() != 2 or (x.shape[0] > 0 and x.stride(1) != 1):
         raise ValueError("x must be 2-D with unit column stride")
     g = torch.empty((1,), dtype=torch.float32, device=x.device) if out is None else out
-    _need_scalar(g, "out")
+    _check_out(g, "out", (1,), torch.float32, x.device)
     ldx = x.stride(0) if x.shape[0] > 0 else x.shape[1]
     call("nvfp4_global_scale", x.data_ptr(), x.shape[0], x.shape[1], ldx, g.data_ptr(), _stream(x))
     return g
@@ -308,8 +360,8 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: torch.Tensor, out=None):
         s = torch.empty((R * (K // 16),), dtype=torch.uint8, device=x.device)
     else:
         q, s = out
-    if s.numel() != R * (K // 16) or not s.is_contiguous():
-        raise ValueError("scales must be contiguous with rows*K/16 bytes")
+        _check_out(q, "codes", (R, K // 2), torch.uint8, x.device)
+        _check_out(s, "scales", (R * (K // 16),), torch.uint8, x.device)
     call("nvfp4_quantize", x.data_ptr(), R, K, x.stride(0), global_scale.data_ptr(),
          q.data_ptr(), s.data_ptr(), _stream(x))
     return q, s
@@ -332,7 +384,7 @@ def nvfp4_gemm(xq, xs, x_global, wq, ws, w_global, out_dtype=torch.float32, out=
     M, N, K = _nv_shapes(xq, xs, wq, ws)
     _need_scalar(x_global, "x_global")
     _need_scalar(w_global, "w_global")
-    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    y = _y_out(out, M, N, out_dtype, xq.device)
     call("nvfp4_gemm", xq.data_ptr(), xs.data_ptr(), x_global.data_ptr(), wq.data_ptr(), ws.data_ptr(),
          w_global.data_ptr(), M, N, K, y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(xq))
     return y

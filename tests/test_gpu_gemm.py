@@ -1,7 +1,9 @@
 """GPU parity of the W4A4 GEMM against the oracle.
 
-Per-group int32 partials must match bit for bit (debug entry point, same
-load/unpack/MFMA code); Y must satisfy |Y_gpu - Y| <= 1e-5 * T + 1e-6 with
+Per-group int32 partials must match bit for bit. The debug entry point runs
+the kernel configuration the plain launch of the same shape runs (tile height
+chosen from M, the same loads, ring depth and ten-chunk g = 128 pipeline),
+with each epilogue fma replaced by a store of its partials. Y must satisfy |Y_gpu - Y| <= 1e-5 * T + 1e-6 with
 T = sum_b |s_a s_w P_b|. Small cases span several tiles with ragged edges and
 are checked in full; the workload shapes run at full size in the production
 launch configuration and are checked on a seeded sample of outputs."""
@@ -216,3 +218,30 @@ def test_splitk_llama70b_m256(N, K):
     Y, T = oracle.w4a4_gemm(qa, sa, ga, qw, sw, gw)
     assert_y_close(y[np.ix_(rows, cols)], Y, T, f"splitk M=256 N={N} K={K}")
     assert_y_close(y1[np.ix_(rows, cols)], Y, T, f"plain M=256 N={N} K={K}")
+
+
+# ------------------------------------------- partials of the production tiles
+@pytest.mark.parametrize("M,N,K,window", [
+    (4096, 28672, 8192, (248, 16, 120, 16)),    # 256-row tiles: the window straddles rows 255/256
+    (4096, 8192, 28672, (3832, 24, 8060, 8)),   # and the 128-column edge at 8064
+    (256, 8192, 28672, (0, 256, 4090, 12)),     # one 256-row tile, every row
+    (128, 4096, 1024, (0, 128, 0, 4096)),       # 128-row tiles (M <= 128), whole output
+    (96, 2048, 512, (40, 56, 1000, 200)),       # 128-row tiles, partial window
+])
+def test_partials_production_tiles(M, N, K, window):
+    """Bit-exact P_b from the tile height and g = 128 pipeline the bench runs
+    (256-row tiles for M > 128, 128-row tiles below), windows across tile edges."""
+    o = ops()
+    x = synth.activations(M, K, dist="t3", seed=11)
+    xq, xs = o.w4a4_quantize_act(dev(x), 128)
+    m0, mc, n0, nc = window
+    w = synth.weights(N, K, seed=0, rows=np.arange(n0, n0 + nc))
+    if N == 28672 or N == 8192:
+        wq, ws = _weights_dev(N, K, 128)
+    else:
+        wq, ws = o.w4a4_pack_weight(dev(synth.weights(N, K, seed=0)), 128)
+    part = host(o.w4a4_gemm_debug_partials(xq, xs, 128, wq, ws, 128, m0, mc, n0, nc))
+    qa, _ = oracle.int4_quantize(x[m0:m0 + mc], 128)
+    qw, _ = oracle.int4_quantize(w, 128)
+    for b, P in oracle.w4a4_block_partials(qa, qw, 128):
+        assert np.array_equal(part[b], P), f"partials block {b}, M={M} window={window}"

@@ -228,8 +228,9 @@ void k_w4a4_gemm(Params p) {
   // Two register sets of staged global data: stage kt+2 is fetched while
   // stage kt is computed and stage kt+1 (fetched one stage earlier) is
   // unpacked into LDS, so every load has two stages to land. The g = 64 mode
-  // and the partials export keep one set (one stage ahead) to stay in registers.
-  constexpr int kAhead = (MODE == G64 || PARTIALS) ? 1 : 2;
+  // keeps one set (one stage ahead) to stay in registers. The partials export
+  // runs each mode's schedule unchanged (same loads, ring depth and pipeline).
+  constexpr int kAhead = (MODE == G64) ? 1 : 2;
   // scale of group column c for the thread's row: a per-stage scalar resource
   auto load_scale = [&](int c) -> float {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sbase + c * sgs, 4 * snr);
@@ -332,10 +333,22 @@ void k_w4a4_gemm(Params p) {
     __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);                                   \
     __builtin_amdgcn_sched_barrier(0);                                                   \
   }
-  // Half H (registers 8H .. 8H+7) of the epilogue of tile (I, J), no partials export.
-#define EPI_HALF(I, J, T, H)                                                             \
+  // Half H (registers 8H .. 8H+7) of the epilogue of tile (I, J) for the group
+  // with index GI; the partials export stores those registers instead (a
+  // carried tile of the first stage, GI = -1, holds nothing).
+#define EPI_HALF(I, J, T, H, GI)                                                         \
   {                                                                                      \
-    if constexpr (ROWA) {                                                                \
+    if constexpr (PARTIALS) {                                                            \
+      if ((GI) >= 0) {                                                                   \
+        _Pragma("unroll") for (int r = 8 * (H); r < 8 * (H) + 8; ++r) {                  \
+          const int m = tile_m + wm * 64 + (I) * 32 + 8 * (r >> 2) + 4 * lhi + (r & 3);  \
+          const int n = tile_n + wn * 64 + (J) * 32 + l32;                               \
+          if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)              \
+            p.partials[((int64_t)(GI) * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] =        \
+                (int32_t)P[I][J][r];                                                     \
+        }                                                                                \
+      }                                                                                  \
+    } else if constexpr (ROWA) {                                                         \
       const float swj_ = (J) == 0 ? (T).sw0 : (T).sw1;                                   \
       _Pragma("unroll") for (int r = 8 * (H); r < 8 * (H) + 8; ++r)                      \
         acc[I][J][r] = fmaf(P[I][J][r], swj_, acc[I][J][r]);                             \
@@ -392,7 +405,7 @@ void k_w4a4_gemm(Params p) {
         __builtin_amdgcn_sched_barrier(0);                                               \
       }                                                                                  \
     };                                                                                   \
-    if constexpr (MODE == G128 && !PARTIALS) {                                           \
+    if constexpr (MODE == G128) {                                                        \
       a[0][0] = load_op(bA + rdA[0], cA + rtA[0]);                                       \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       b[0][0] = load_op(bW + rdW[0], cW + rtW[0]);                                       \
@@ -423,7 +436,7 @@ void k_w4a4_gemm(Params p) {
         __builtin_amdgcn_sched_barrier(0);                                               \
         ++gidx;                                                                          \
       }                                                                                  \
-    } else if constexpr (MODE == G128 && !PARTIALS) {                                    \
+    } else if constexpr (MODE == G128) {                                                 \
       /* Software pipeline: ten chunks, each one MFMA issued first and the     */    \
       /* vector work that runs under it. An epilogue reads partials finished  */    \
       /* two MFMAs or more earlier (no dependency wait); tiles (1,1) and      */    \
@@ -435,22 +448,22 @@ void k_w4a4_gemm(Params p) {
       const float gsw0_ = sSW[BUF][0][wn * 64 + l32];                                    \
       const float gsw1_ = sSW[BUF][0][wn * 64 + 32 + l32];                               \
       P[0][0] = mma(a[0][0], b[0][0], zero16);                                           \
-      EPI_HALF(1, 1, Tc, 0);                                                             \
+      EPI_HALF(1, 1, Tc, 0, gidx - 1);                                                   \
       a[0][1] = load_op(bA + rdA[1], cA + rtA[1]);                                       \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       b[0][1] = load_op(bW + rdW[1], cW + rtW[1]);                                       \
       CHUNK_END(8);                                                                      \
       P[1][0] = mma(a[1][0], b[0][0], zero16);                                           \
-      EPI_HALF(1, 1, Tc, 1);                                                             \
+      EPI_HALF(1, 1, Tc, 1, gidx - 1);                                                   \
       LST_A0((BUF) ^ 1, RS);                                                             \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       a[1][1] = load_op(bA + rdA[1] + 32 * PM, cA + rtA[1] + 32 * PT);                   \
       CHUNK_END(16);                                                                     \
       P[0][0] = mma(a[0][1], b[0][1], P[0][0]);                                          \
-      EPI_HALF(0, 1, Tc, 0);                                                             \
+      EPI_HALF(0, 1, Tc, 0, gidx - 1);                                                   \
       CHUNK_END(8);                                                                      \
       P[1][0] = mma(a[1][1], b[0][1], P[1][0]);                                          \
-      EPI_HALF(0, 1, Tc, 1);                                                             \
+      EPI_HALF(0, 1, Tc, 1, gidx - 1);                                                   \
       LST_A1((BUF) ^ 1, RS);                                                             \
       CHUNK_END(16);                                                                     \
       GroupScales T0 = TPRODV(gsa_, gsw0_, gsw1_);                                       \
@@ -459,17 +472,17 @@ void k_w4a4_gemm(Params p) {
       load_w1();                                                                         \
       CHUNK_END(16);                                                                     \
       P[1][1] = mma(a[1][0], b[1][0], zero16);                                           \
-      EPI_HALF(0, 0, T0, 0);                                                             \
+      EPI_HALF(0, 0, T0, 0, gidx);                                                       \
       CHUNK_END(8);                                                                      \
       P[0][1] = mma(a[0][0], b[1][0], zero16);                                           \
-      EPI_HALF(0, 0, T0, 1);                                                             \
+      EPI_HALF(0, 0, T0, 1, gidx);                                                       \
       LST_W0((BUF) ^ 1, RS);                                                             \
       CHUNK_END(16);                                                                     \
       P[1][1] = mma(a[1][1], b[1][1], P[1][1]);                                          \
-      EPI_HALF(1, 0, T0, 0);                                                             \
+      EPI_HALF(1, 0, T0, 0, gidx);                                                       \
       CHUNK_END(8);                                                                      \
       P[0][1] = mma(a[0][1], b[1][1], P[0][1]);                                          \
-      EPI_HALF(1, 0, T0, 1);                                                             \
+      EPI_HALF(1, 0, T0, 1, gidx);                                                       \
       LST_W1((BUF) ^ 1, RS);                                                             \
       CHUNK_END(16);                                                                     \
       Tc = TPRODV(gsa_, gsw1_, gsw1_);                                                   \
@@ -477,24 +490,6 @@ void k_w4a4_gemm(Params p) {
       CHUNK_END(16);                                                                     \
       /* keep Tc's MFMA here (it would sink into the next stage) */                     \
       if constexpr (!ROWA) asm volatile("" : "+v"(Tc.t));   /* no product with per-token A scales */ \
-      ++gidx;                                                                            \
-    } else if constexpr (MODE == G128) {                                                 \
-      const GroupScales T0 = TPROD(BUF, 0, 0);                                           \
-      P[0][0] = mma(a[0][1], b[0][1], mma(a[0][0], b[0][0], zero16));                    \
-      P[1][0] = mma(a[1][1], b[0][1], mma(a[1][0], b[0][0], zero16));                    \
-      __builtin_amdgcn_sched_barrier(0);                                                 \
-      EPI(0, 0, T0);                                                                     \
-      P[1][1] = mma(a[1][1], b[1][1], mma(a[1][0], b[1][0], zero16));                    \
-      __builtin_amdgcn_sched_barrier(0);                                                 \
-      EPI(1, 0, T0);                                                                     \
-      const GroupScales T1 = TPROD(BUF, 0, 1);                                           \
-      P[0][1] = mma(a[0][1], b[1][1], mma(a[0][0], b[1][0], zero16));                    \
-      __builtin_amdgcn_sched_barrier(0);                                                 \
-      EPI(1, 1, T1);                                                                     \
-      LSTORE((BUF) ^ 1, RS);                                                             \
-      __builtin_amdgcn_sched_barrier(0);                                                 \
-      EPI(0, 1, T1);                                                                     \
-      __builtin_amdgcn_sched_barrier(0);                                                 \
       ++gidx;                                                                            \
     } else {                                                                             \
       /* partials accumulate over stages_per_group stages, then one epilogue */          \
@@ -532,11 +527,11 @@ void k_w4a4_gemm(Params p) {
     STAGE(kt + 1, 1, RX, R0);
   }
   if (kt < ke) STAGE(kt, 0, R0, RX);
-  if constexpr (MODE == G128 && !PARTIALS) {   // the last stage's carried tiles
-    EPI_HALF(1, 1, Tc, 0);
-    EPI_HALF(1, 1, Tc, 1);
-    EPI_HALF(0, 1, Tc, 0);
-    EPI_HALF(0, 1, Tc, 1);
+  if constexpr (MODE == G128) {   // the last stage's carried tiles
+    EPI_HALF(1, 1, Tc, 0, gidx - 1);
+    EPI_HALF(1, 1, Tc, 1, gidx - 1);
+    EPI_HALF(0, 1, Tc, 0, gidx - 1);
+    EPI_HALF(0, 1, Tc, 1, gidx - 1);
   }
 #undef GLOAD
 #undef LSTORE
@@ -855,16 +850,20 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     p.tile_n0 = (int)(g.n0 / SM_TILE);
     p.tiles_m = (int)((g.m0 + g.mc - 1) / SM_TILE) - p.tile_m0 + 1;
     p.tiles_n = (int)((g.n0 + g.nc - 1) / SM_TILE) - p.tile_n0 + 1;
-    const int nwg = p.tiles_m * p.tiles_n;
-    const dim3 grid((unsigned)nwg);
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     const int spg = (int)(gmin / 64);
+    // waves per workgroup from the whole product's grid, so a partials window
+    // runs the configuration the plain launch of this shape runs
+    const int64_t nwg = ((g.M + SM_TILE - 1) / SM_TILE) * ((g.N + SM_TILE - 1) / SM_TILE);
     if (nwg < 512)
       launch_small<8>(g, p, grid, spg, stream);
     else
       launch_small<4>(g, p, grid, spg, stream);
     return;
   }
-  const int BM = tile_rows(g.mc, gmin);
+  // tile height from the whole product (a partials window gets the tiles the
+  // plain launch of this shape runs)
+  const int BM = tile_rows(g.M, gmin);
   p.tile_m0 = (int)(g.m0 / BM);
   p.tile_n0 = (int)(g.n0 / BN);
   p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;

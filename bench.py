@@ -141,13 +141,15 @@ def quant_standalone(shapes, ga, fmt, reps: int = 24, nrot: int = 6):
 
 
 def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
-    """Time the CPU oracle on n_rows tokens x n_cols output features per linear."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
+    """Time the CPU oracle (C++, std::thread over every core this process may
+    use) on n_rows tokens x n_cols output features per linear, all of K:
+    act-quant + GEMM, weights quantized untimed. Also states the full step's
+    time extrapolated from the sample's rate (the oracle's cost is linear in
+    M * N * K)."""
     import oracle
     from w4a4_quantized_gemm_quantize_amd import synth
 
+    oracle.set_threads(0)
     rows = synth.sample_rows(M, n_rows, seed=11)
     work = []
     for li, (K, N) in enumerate(wl):
@@ -178,11 +180,13 @@ def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
             oracle.mxfp4_gemm(ca, ea, wpk[0], wpk[1])
         ops += 2 * len(rows) * nc * K
     dt = time.perf_counter() - t0
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    full_ops = sum(2 * M * N * K for K, N in wl)
     return {
-        "value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+        "value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.cores(), "kind": "oracle",
         "sample": (f"{len(rows)} of {M} tokens x {min(n_cols, wl[0][1])}-col sample of each linear's N "
                    f"(all K), act-quant + GEMM, {dt:.1f} s on the host"),
+        "implementation": "C++ (oracle/orc.cpp, -O2 -ffp-contract=off), std::thread over rows",
+        "extrapolated_full_step_s": dt * full_ops / ops,
     }
 
 

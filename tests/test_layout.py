@@ -63,3 +63,43 @@ def test_nvfp4_panel_layout(rows, K):
     flat = ops.nvfp4_scales_to_panels(s_rows)
     assert np.array_equal(flat, nv_panels_by_definition(s_rows))
     assert np.array_equal(ops.nvfp4_scales_to_rows(flat, rows, K), s_rows)
+
+
+# ------------------------------------------------ the oracle's layout module
+import oracle  # noqa: E402
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (3, 384), (5, 256), (2, 96), (7, 1152)])
+def test_oracle_e8m0_panels_match_definition(rows, K):
+    rng = np.random.default_rng(7 * rows + K)
+    e_rows = rng.integers(0, 255, size=(rows, K // 32), dtype=np.uint8)
+    offs = oracle.e8m0_panel_offsets(rows, K)
+    assert np.array_equal(oracle.to_panels(e_rows, offs), panels_by_definition(e_rows))
+    assert np.array_equal(oracle.from_panels(oracle.to_panels(e_rows, offs), offs), e_rows)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 256), (5, 512), (3, 3584)])
+def test_oracle_e4m3_panels_match_definition(rows, K):
+    rng = np.random.default_rng(rows * 3 + K)
+    s_rows = rng.integers(0, 256, (rows, K // 16), dtype=np.uint8)
+    offs = oracle.e4m3_panel_offsets(rows, K)
+    assert np.array_equal(oracle.to_panels(s_rows, offs), nv_panels_by_definition(s_rows))
+
+
+def test_twos_complement_nibbles():
+    """Canonical INT4 storage: byte = (c[2i] & 0xF) | (c[2i+1] & 0xF) << 4,
+    worked by hand for codes (-8, 7), (-1, 0), (3, -4)."""
+    c = np.array([[-8, 7, -1, 0, 3, -4]], np.int8)
+    assert oracle.pack_int4_twos(c).tolist() == [[0x78, 0x0F, 0xC3]]
+    assert np.array_equal(oracle.unpack_int4_twos(oracle.pack_int4_twos(c)), c)
+    every = np.arange(-8, 8, dtype=np.int8).reshape(1, 16)
+    assert np.array_equal(oracle.unpack_int4_twos(oracle.pack_int4_twos(every)), every)
+    with pytest.raises(ValueError):
+        oracle.pack_int4_twos(np.array([[8, 0]], np.int16))
+
+
+def test_group_major_is_transpose():
+    s = np.arange(12, dtype=np.float32).reshape(3, 4)      # [rows=3][groups=4]
+    gm = oracle.group_major(s)
+    assert gm.shape == (4, 3) and gm.flags["C_CONTIGUOUS"]
+    assert gm[2, 1] == s[1, 2]

@@ -328,6 +328,67 @@ w4a4_status_t nvfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xs,
                                         int64_t m0, int64_t mc, int64_t n0, int64_t nc,
                                         int32_t* partials, void* stream);
 
+/*
+ * ---- Storage conversions ------------------------------------------------
+ * The pages fix no storage layout ("drop-in replacement in unmodified vLLM",
+ * APEX4 abstract, asks only that a linear layer's quantized data can be fed
+ * in). The canonical forms below are the plain ones: INT4 codes as
+ * two's-complement nibbles, two per byte with the even k in the low nibble;
+ * scales row-major [rows][K / block]. The GEMMs read the layouts documented
+ * above (folded sign-magnitude INT4, group-major INT4 scales, 256-k scale
+ * panels), chosen for the matrix cores and the L2 request count; these calls
+ * convert on the device, value for value, in one pass over the bytes.
+ * Asynchronous on `stream`, no allocation; in and out must not overlap.
+ */
+
+/*
+ * Canonical INT4 codes -> the GEMM's INT4 layout.
+ *   nibbles       u8 [rows][K/2] two's-complement codes in [-8, 7], even k in
+ *                 the low nibble; 8-byte aligned; K % 16 == 0
+ *   packed        out: u8 [rows][K/2] in the layout above, 8-byte aligned
+ *   minus8_count  NULL, or ONE device int32 (4-byte aligned) that receives the
+ *                 number of codes equal to -8. Those have no sign-magnitude
+ *                 form in this layout (the symmetric quantizer of this
+ *                 library never produces them) and are stored as 0: the
+ *                 caller must check the count before using `packed`.
+ */
+w4a4_status_t w4a4_repack_int4(const uint8_t* nibbles, int64_t rows, int64_t K, uint8_t* packed,
+                               int32_t* minus8_count, void* stream);
+
+/*
+ * The GEMM's INT4 layout -> canonical two's-complement nibbles (a stored -0
+ * becomes 0). Shapes and alignment as for w4a4_repack_int4.
+ */
+w4a4_status_t w4a4_unpack_int4(const uint8_t* packed, int64_t rows, int64_t K, uint8_t* nibbles, void* stream);
+
+/*
+ * INT4 scales: row-major f32 [rows][groups] <-> the GEMM's group-major
+ * [groups][rows] (groups = K / group size). 4-byte aligned; rows <= 2097120.
+ */
+w4a4_status_t w4a4_scales_to_group_major(const float* scales_rows, int64_t rows, int64_t groups,
+                                         float* scales_gm, void* stream);
+w4a4_status_t w4a4_scales_to_row_major(const float* scales_gm, int64_t rows, int64_t groups,
+                                       float* scales_rows, void* stream);
+
+/*
+ * MXFP4 E8M0 scales: row-major u8 [rows][K/32] <-> the 256-k panel layout of
+ * mxfp4_quantize (K % 32 == 0). MXFP4 codes need no conversion: the canonical
+ * nibble order is the GEMM's.
+ */
+w4a4_status_t mxfp4_scales_to_panels(const uint8_t* e8m0_rows, int64_t rows, int64_t K, uint8_t* e8m0,
+                                     void* stream);
+w4a4_status_t mxfp4_scales_to_rows(const uint8_t* e8m0, int64_t rows, int64_t K, uint8_t* e8m0_rows,
+                                   void* stream);
+
+/*
+ * NVFP4 E4M3 scales: row-major u8 [rows][K/16] <-> the 256-k panel layout of
+ * nvfp4_quantize (K % 256 == 0).
+ */
+w4a4_status_t nvfp4_scales_to_panels(const uint8_t* scales_rows, int64_t rows, int64_t K, uint8_t* scales,
+                                     void* stream);
+w4a4_status_t nvfp4_scales_to_rows(const uint8_t* scales, int64_t rows, int64_t K, uint8_t* scales_rows,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

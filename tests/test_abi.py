@@ -197,3 +197,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libw4a4.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load_library()
+
+
+def test_storage_conversion_validation(lib):
+    st = _lib.status_of
+    assert st("w4a4_repack_int4", P, 4, 24, P, None, None) == E_SHAPE          # K % 16
+    assert st("w4a4_repack_int4", P, -1, 32, P, None, None) == E_SHAPE
+    assert st("w4a4_repack_int4", None, 4, 32, P, None, None) == E_NULL
+    assert st("w4a4_repack_int4", P + 4, 4, 32, P, None, None) == E_ALIGN
+    assert st("w4a4_repack_int4", P, 4, 32, P, P + 2, None) == E_ALIGN        # the count word
+    assert st("w4a4_repack_int4", None, 0, 32, None, None, None) == OK          # empty, nothing counted
+    assert st("w4a4_unpack_int4", P, 4, 40, P, None) == E_SHAPE
+    assert st("w4a4_unpack_int4", P, 4, 32, None, None) == E_NULL
+    assert st("w4a4_unpack_int4", P, 4, 32, P + 1, None) == E_ALIGN
+    assert st("w4a4_scales_to_group_major", P, -1, 4, P, None) == E_SHAPE
+    assert st("w4a4_scales_to_group_major", P, 65535 * 32 + 1, 4, P, None) == E_SHAPE
+    assert st("w4a4_scales_to_group_major", P, 0, 4, None, None) == OK
+    assert st("w4a4_scales_to_group_major", None, 3, 4, P, None) == E_NULL
+    assert st("w4a4_scales_to_row_major", P + 2, 3, 4, P, None) == E_ALIGN
+    assert st("mxfp4_scales_to_panels", P, 3, 48, P, None) == E_SHAPE          # K % 32
+    assert st("mxfp4_scales_to_rows", None, 3, 64, P, None) == E_NULL
+    assert st("nvfp4_scales_to_panels", P, 3, 128, P, None) == E_SHAPE         # K % 256
+    assert st("nvfp4_scales_to_rows", P, 0, 256, None, None) == OK

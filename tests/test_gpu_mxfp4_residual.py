@@ -30,7 +30,7 @@ def res_check(x16, ldx_pad=0, fn="mxfp4_quantize_residual"):
         codes, e8 = oracle.mxfp4_quantize_residual(x16)
     else:
         codes, e8 = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(x16))
-    assert np.array_equal(ops().mxfp4_scales_to_rows(host(e), R, 2 * K), e8), f"{fn} E8M0 (R={R} K={K})"
+    assert np.array_equal(oracle.from_panels(host(e), oracle.e8m0_panel_offsets(R, 2 * K)), e8), f"{fn} E8M0 (R={R} K={K})"
     bad = np.argwhere(host(q) != oracle.pack_nibbles(codes))
     assert bad.size == 0, f"{fn} codes differ at {bad[:5].tolist()} (R={R} K={K})"
 

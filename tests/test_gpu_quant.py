@@ -124,7 +124,7 @@ def mx_check(x16, ldx_pad=0):
         xt = dev(x16)
     q, e = ops().mxfp4_quantize(xt)
     codes, e8 = oracle.mxfp4_quantize(x16)
-    assert np.array_equal(ops().mxfp4_scales_to_rows(host(e), R, K), e8), f"E8M0 differ (R={R} K={K})"
+    assert np.array_equal(oracle.from_panels(host(e), oracle.e8m0_panel_offsets(R, K)), e8), f"E8M0 differ (R={R} K={K})"
     gq = host(q)
     want = oracle.pack_nibbles(codes)   # E2M1 fields, even k low
     bad = np.argwhere(gq != want)
@@ -162,7 +162,7 @@ def test_mxfp4_rows_beyond_one_grid_dimension():
     q, e = ops().mxfp4_quantize(dev(x))
     rows = np.concatenate([synth.sample_rows(R, 48, seed=3), np.arange(R - 40, R)])
     codes, e8 = oracle.mxfp4_quantize(x[rows])
-    assert np.array_equal(ops().mxfp4_scales_to_rows(host(e), R, K)[rows], e8)
+    assert np.array_equal(oracle.from_panels(host(e), oracle.e8m0_panel_offsets(R, K))[rows], e8)
     assert np.array_equal(host(q)[rows], oracle.pack_nibbles(codes))
 
 

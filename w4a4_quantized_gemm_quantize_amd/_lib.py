@@ -45,6 +45,14 @@ SIGNATURES = {
     "nvfp4_gemm": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p],
     "nvfp4_gemm_debug_partials": [_p, _p, _p, _p, _i64, _i64, _i64,
                                   _i64, _i64, _i64, _i64, _p, _p],
+    "w4a4_repack_int4": [_p, _i64, _i64, _p, _p, _p],
+    "w4a4_unpack_int4": [_p, _i64, _i64, _p, _p],
+    "w4a4_scales_to_group_major": [_p, _i64, _i64, _p, _p],
+    "w4a4_scales_to_row_major": [_p, _i64, _i64, _p, _p],
+    "mxfp4_scales_to_panels": [_p, _i64, _i64, _p, _p],
+    "mxfp4_scales_to_rows": [_p, _i64, _i64, _p, _p],
+    "nvfp4_scales_to_panels": [_p, _i64, _i64, _p, _p],
+    "nvfp4_scales_to_rows": [_p, _i64, _i64, _p, _p],
 }
 
 

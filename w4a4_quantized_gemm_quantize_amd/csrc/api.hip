@@ -315,4 +315,77 @@ w4a4_status_t nvfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xs,
   return launched();
 }
 
+// ---------------------------------------------------------- storage conversions
+
+w4a4_status_t w4a4_repack_int4(const uint8_t* nibbles, int64_t rows, int64_t K, uint8_t* packed,
+                               int32_t* minus8_count, void* stream) {
+  if (rows < 0 || K <= 0 || K % 16) return W4A4_E_SHAPE;
+  if (rows == 0) {
+    if (minus8_count) w4a4::launch_repack_int4(nullptr, 0, K, nullptr, minus8_count, as_stream(stream));
+    return minus8_count ? launched() : W4A4_OK;
+  }
+  if (!nibbles || !packed) return W4A4_E_NULL;
+  if (!aligned(nibbles, 8) || !aligned(packed, 8) || (minus8_count && !aligned(minus8_count, 4))) return W4A4_E_ALIGN;
+  w4a4::launch_repack_int4(nibbles, rows, K, packed, minus8_count, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t w4a4_unpack_int4(const uint8_t* packed, int64_t rows, int64_t K, uint8_t* nibbles, void* stream) {
+  if (rows < 0 || K <= 0 || K % 16) return W4A4_E_SHAPE;
+  if (rows == 0) return W4A4_OK;
+  if (!nibbles || !packed) return W4A4_E_NULL;
+  if (!aligned(nibbles, 8) || !aligned(packed, 8)) return W4A4_E_ALIGN;
+  w4a4::launch_unpack_int4(packed, rows, K, nibbles, as_stream(stream));
+  return launched();
+}
+
+// [rows][cols] -> [cols][rows]; the grid's second dimension covers 32 rows per block
+static w4a4_status_t transpose_scales(const float* in, int64_t rows, int64_t cols, float* out, void* stream) {
+  if (rows < 0 || cols < 0 || rows > 65535LL * 32 || cols > (int64_t{1} << 31)) return W4A4_E_SHAPE;
+  if (rows == 0 || cols == 0) return W4A4_OK;
+  if (!in || !out) return W4A4_E_NULL;
+  if (!aligned(in, 4) || !aligned(out, 4)) return W4A4_E_ALIGN;
+  w4a4::launch_transpose_f32(in, rows, cols, out, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t w4a4_scales_to_group_major(const float* scales_rows, int64_t rows, int64_t groups,
+                                         float* scales_gm, void* stream) {
+  return transpose_scales(scales_rows, rows, groups, scales_gm, stream);
+}
+
+w4a4_status_t w4a4_scales_to_row_major(const float* scales_gm, int64_t rows, int64_t groups,
+                                       float* scales_rows, void* stream) {
+  return transpose_scales(scales_gm, groups, rows, scales_rows, stream);
+}
+
+static w4a4_status_t scale_panels(int fmt, bool to_panels, const uint8_t* in, int64_t rows, int64_t K,
+                                  int64_t kmul, uint8_t* out, void* stream) {
+  if (rows < 0 || K <= 0 || K % kmul) return W4A4_E_SHAPE;
+  if (rows == 0) return W4A4_OK;
+  if (!in || !out) return W4A4_E_NULL;
+  w4a4::launch_scale_panels(fmt, to_panels, in, rows, K / (fmt == 0 ? 32 : 16), out, as_stream(stream));
+  return launched();
+}
+
+w4a4_status_t mxfp4_scales_to_panels(const uint8_t* e8m0_rows, int64_t rows, int64_t K, uint8_t* e8m0,
+                                     void* stream) {
+  return scale_panels(0, true, e8m0_rows, rows, K, 32, e8m0, stream);
+}
+
+w4a4_status_t mxfp4_scales_to_rows(const uint8_t* e8m0, int64_t rows, int64_t K, uint8_t* e8m0_rows,
+                                   void* stream) {
+  return scale_panels(0, false, e8m0, rows, K, 32, e8m0_rows, stream);
+}
+
+w4a4_status_t nvfp4_scales_to_panels(const uint8_t* scales_rows, int64_t rows, int64_t K, uint8_t* scales,
+                                     void* stream) {
+  return scale_panels(1, true, scales_rows, rows, K, 256, scales, stream);
+}
+
+w4a4_status_t nvfp4_scales_to_rows(const uint8_t* scales, int64_t rows, int64_t K, uint8_t* scales_rows,
+                                   void* stream) {
+  return scale_panels(1, false, scales, rows, K, 256, scales_rows, stream);
+}
+
 }  // extern "C"

@@ -54,4 +54,14 @@ void launch_nvfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx, con
 // (unused by the partials export)
 void launch_nvfp4_gemm(const GemmArgs& a, const float* ga, const float* gw, hipStream_t stream);
 
+// Storage conversions (layout.hip). count: device int32 receiving the number
+// of -8 codes (none may be NULL: not counted).
+void launch_repack_int4(const uint8_t* nibbles, int64_t rows, int64_t K, uint8_t* packed, int32_t* count,
+                        hipStream_t stream);
+void launch_unpack_int4(const uint8_t* packed, int64_t rows, int64_t K, uint8_t* nibbles, hipStream_t stream);
+void launch_transpose_f32(const float* in, int64_t rows, int64_t cols, float* out, hipStream_t stream);
+// fmt 0: E8M0 (blocks of 32), 1: E4M3 (blocks of 16); nb = blocks per row
+void launch_scale_panels(int fmt, bool to_panels, const uint8_t* in, int64_t rows, int64_t nb, uint8_t* out,
+                         hipStream_t stream);
+
 }  // namespace w4a4

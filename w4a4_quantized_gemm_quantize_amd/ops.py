@@ -175,48 +175,10 @@ def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int
     return part
 
 
-def mxfp4_scale_offsets(rows: int, K: int):
-    """Byte offset of the scale of (row r, block b) in the 256-k panel layout
-    of the C header: ``8*rows*p + w_p*r + pos`` with ``p = b // 8``,
-    ``w_p = min(8, K/32 - 8p)``, ``j = b % 8`` and ``pos = j // 2`` for even
-    j, ``ceil(w_p / 2) + j // 2`` for odd j. Returns an int64 tensor [rows, K/32]."""
-    nb = K // 32
-    b = torch.arange(nb, dtype=torch.int64)
-    p = b // 8
-    w = torch.clamp(nb - 8 * p, max=8)
-    j = b % 8
-    pos = torch.where(j % 2 == 0, j // 2, (w + 1) // 2 + j // 2)
-    r = torch.arange(rows, dtype=torch.int64)[:, None]
-    return 8 * rows * p[None, :] + w[None, :] * r + pos[None, :]
-
-
-def mxfp4_scales_to_rows(e, rows: int, K: int):
-    """Panel-layout scale bytes (flat, ``rows*K/32``) -> row-major [rows, K/32]
-    (torch tensor on its device, or numpy array)."""
-    idx = mxfp4_scale_offsets(rows, K)
-    if isinstance(e, torch.Tensor):
-        return e.reshape(-1)[idx.to(e.device)]
-    return e.reshape(-1)[idx.numpy()]
-
-
-def mxfp4_scales_to_panels(e_rows):
-    """Row-major [rows, K/32] scale bytes -> the flat panel layout."""
-    rows, nb = e_rows.shape
-    idx = mxfp4_scale_offsets(rows, 32 * nb).reshape(-1)
-    if isinstance(e_rows, torch.Tensor):
-        out = torch.empty(rows * nb, dtype=e_rows.dtype, device=e_rows.device)
-        out[idx.to(e_rows.device)] = e_rows.reshape(-1)
-        return out
-    import numpy as np
-    out = np.empty(rows * nb, dtype=e_rows.dtype)
-    out[idx.numpy()] = e_rows.reshape(-1)
-    return out
-
-
 def mxfp4_quantize(x: torch.Tensor, out=None):
     """MXFP4 quantization of fp16 X[rows, K]: ``(codes uint8 [rows, K/2],
     e8m0 uint8 [rows*K/32] in the 256-k panel layout)``; see
-    :func:`mxfp4_scales_to_rows` for the row-major view."""
+    :func:`mxfp4_scales_to_rows` for the row-major form."""
     _need(x, torch.float16, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
@@ -293,40 +255,6 @@ def mxfp4_gemm_debug_partials(xq, xe, wq, we, m0: int, mc: int, n0: int, nc: int
 
 # ------------------------------------------------------------------- NVFP4
 
-def nvfp4_scale_offsets(rows: int, K: int):
-    """Byte offset of the E4M3 scale of (row r, block b) in the 256-k panel
-    layout of the C header: ``16*rows*p + 16*r + 8*((j>>1)&1) + 2*(j>>2) +
-    (j&1)`` with ``p = b // 16``, ``j = b % 16``. Returns int64 [rows, K/16]."""
-    b = torch.arange(K // 16, dtype=torch.int64)
-    p, j = b // 16, b % 16
-    pos = 8 * ((j >> 1) & 1) + 2 * (j >> 2) + (j & 1)
-    r = torch.arange(rows, dtype=torch.int64)[:, None]
-    return 16 * rows * p[None, :] + 16 * r + pos[None, :]
-
-
-def nvfp4_scales_to_rows(s, rows: int, K: int):
-    """Panel-layout scale bytes (flat, ``rows*K/16``) -> row-major [rows, K/16]
-    (torch tensor on its device, or numpy array)."""
-    idx = nvfp4_scale_offsets(rows, K)
-    if isinstance(s, torch.Tensor):
-        return s.reshape(-1)[idx.to(s.device)]
-    return s.reshape(-1)[idx.numpy()]
-
-
-def nvfp4_scales_to_panels(s_rows):
-    """Row-major [rows, K/16] scale bytes -> the flat panel layout."""
-    rows, nb = s_rows.shape
-    idx = nvfp4_scale_offsets(rows, 16 * nb).reshape(-1)
-    if isinstance(s_rows, torch.Tensor):
-        out = torch.empty(rows * nb, dtype=s_rows.dtype, device=s_rows.device)
-        out[idx.to(s_rows.device)] = s_rows.reshape(-1)
-        return out
-    import numpy as np
-    out = np.empty(rows * nb, dtype=s_rows.dtype)
-    out[idx.numpy()] = s_rows.reshape(-1)
-    return out
-
-
 def _need_scalar(t, name: str) -> None:
     _need(t, torch.float32, name)
     if t.numel() != 1:
@@ -397,3 +325,89 @@ def nvfp4_gemm_debug_partials(xq, xs, wq, ws, m0: int, mc: int, n0: int, nc: int
     call("nvfp4_gemm_debug_partials", xq.data_ptr(), xs.data_ptr(), wq.data_ptr(), ws.data_ptr(),
          M, N, K, m0, mc, n0, nc, part.data_ptr(), _stream(xq))
     return part
+
+
+# -------------------------------------------------------- storage conversions
+# Canonical storage (two's-complement INT4 nibbles, row-major scales) <-> the
+# layouts the GEMMs read; every conversion runs in the library's kernels.
+
+def w4a4_repack_int4(nibbles: torch.Tensor, check: bool = True):
+    """Canonical INT4 codes (uint8 [rows, K/2], two's-complement nibbles, even
+    k low) -> the GEMM's INT4 layout. Returns ``(packed, minus8_count)``, the
+    count a one-element int32 device tensor. With ``check`` (default) the call
+    synchronizes and raises if any code is -8 (no sign-magnitude form)."""
+    _need(nibbles, torch.uint8, "nibbles")
+    if nibbles.dim() != 2 or not nibbles.is_contiguous():
+        raise ValueError("nibbles must be a contiguous 2-D tensor")
+    rows, K = nibbles.shape[0], nibbles.shape[1] * 2
+    packed = torch.empty_like(nibbles)
+    count = torch.empty((1,), dtype=torch.int32, device=nibbles.device)
+    call("w4a4_repack_int4", nibbles.data_ptr(), rows, K, packed.data_ptr(), count.data_ptr(), _stream(nibbles))
+    if check and int(count.item()) != 0:
+        raise ValueError(f"{int(count.item())} INT4 codes are -8: the GEMM layout holds [-7, 7] only")
+    return packed, count
+
+
+def w4a4_unpack_int4(packed: torch.Tensor):
+    """The GEMM's INT4 layout -> canonical two's-complement nibbles (-0 -> 0)."""
+    _need(packed, torch.uint8, "packed")
+    if packed.dim() != 2 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous 2-D tensor")
+    out = torch.empty_like(packed)
+    call("w4a4_unpack_int4", packed.data_ptr(), packed.shape[0], packed.shape[1] * 2, out.data_ptr(),
+         _stream(packed))
+    return out
+
+
+def w4a4_scales_to_group_major(scales_rows: torch.Tensor):
+    """Row-major INT4 scales float32 [rows, groups] -> group-major [groups, rows]."""
+    _need(scales_rows, torch.float32, "scales_rows")
+    if scales_rows.dim() != 2 or not scales_rows.is_contiguous():
+        raise ValueError("scales_rows must be a contiguous 2-D tensor")
+    rows, groups = scales_rows.shape
+    out = torch.empty((groups, rows), dtype=torch.float32, device=scales_rows.device)
+    call("w4a4_scales_to_group_major", scales_rows.data_ptr(), rows, groups, out.data_ptr(), _stream(scales_rows))
+    return out
+
+
+def w4a4_scales_to_row_major(scales_gm: torch.Tensor):
+    """Group-major INT4 scales float32 [groups, rows] -> row-major [rows, groups]."""
+    _need(scales_gm, torch.float32, "scales_gm")
+    if scales_gm.dim() != 2 or not scales_gm.is_contiguous():
+        raise ValueError("scales_gm must be a contiguous 2-D tensor")
+    groups, rows = scales_gm.shape
+    out = torch.empty((rows, groups), dtype=torch.float32, device=scales_gm.device)
+    call("w4a4_scales_to_row_major", scales_gm.data_ptr(), rows, groups, out.data_ptr(), _stream(scales_gm))
+    return out
+
+
+def _panels(fn: str, src: torch.Tensor, rows: int, K: int, block: int, to_panels: bool):
+    _need(src, torch.uint8, "scales")
+    if not src.is_contiguous() or src.numel() != rows * (K // block):
+        raise ValueError(f"scales must be contiguous with rows*K/{block} bytes")
+    shape = (rows * (K // block),) if to_panels else (rows, K // block)
+    out = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    call(fn, src.data_ptr(), rows, K, out.data_ptr(), _stream(src))
+    return out
+
+
+def mxfp4_scales_to_panels(e_rows: torch.Tensor):
+    """Row-major E8M0 bytes [rows, K/32] -> the flat 256-k panel layout."""
+    rows, nb = e_rows.shape
+    return _panels("mxfp4_scales_to_panels", e_rows, rows, 32 * nb, 32, True)
+
+
+def mxfp4_scales_to_rows(e: torch.Tensor, rows: int, K: int):
+    """Panel-layout E8M0 bytes (flat, rows*K/32) -> row-major [rows, K/32]."""
+    return _panels("mxfp4_scales_to_rows", e, rows, K, 32, False)
+
+
+def nvfp4_scales_to_panels(s_rows: torch.Tensor):
+    """Row-major E4M3 bytes [rows, K/16] -> the flat 256-k panel layout (K % 256 == 0)."""
+    rows, nb = s_rows.shape
+    return _panels("nvfp4_scales_to_panels", s_rows, rows, 16 * nb, 16, True)
+
+
+def nvfp4_scales_to_rows(s: torch.Tensor, rows: int, K: int):
+    """Panel-layout E4M3 bytes (flat, rows*K/16) -> row-major [rows, K/16]."""
+    return _panels("nvfp4_scales_to_rows", s, rows, K, 16, False)

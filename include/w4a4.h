@@ -64,7 +64,8 @@ typedef enum {
   W4A4_E_GROUP = 3,  /* unsupported group size, group does not divide K, or groups do not nest */
   W4A4_E_ALIGN = 4,  /* a pointer or leading dimension breaks the alignment rule of the call */
   W4A4_E_DTYPE = 5,  /* unknown output dtype */
-  W4A4_E_HIP = 6     /* the HIP runtime reported an error for the launch */
+  W4A4_E_HIP = 6,    /* the HIP runtime reported an error for the launch */
+  W4A4_E_SCRATCH = 7 /* the call needs more than the library's static scratch buffer */
 } w4a4_status_t;
 
 typedef enum {
@@ -161,6 +162,31 @@ w4a4_status_t w4a4_gemm_splitk(const uint8_t* xq, const float* xs, int32_t group
  */
 int64_t w4a4_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w,
                                    int32_t splits);
+
+/*
+ * w4a4_gemm_splitk for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and split plan, with the splits' fp32 partial outputs in a
+ * static device buffer of the library instead of a caller workspace. Calls no
+ * hipMalloc, hipFree or other allocating routine.
+ *   - The buffer holds w4a4_gemm_splitk_noalloc_max_bytes() bytes (32 MiB)
+ *     per GPU, for the life of the process. A plan needing more
+ *     (splits * M * N * 4 bytes) returns W4A4_E_SCRATCH and launches nothing;
+ *     one that needs no split runs w4a4_gemm.
+ *   - Every call on a GPU shares that GPU's buffer: calls that overlap on one
+ *     GPU (two streams, two host threads) race and must be ordered by the
+ *     caller. Each call overwrites what it uses; nothing must start at zero.
+ *   - The first call on a device looks up the buffer's address there (a
+ *     runtime failure returns W4A4_E_HIP).
+ * Other arguments and the result are those of w4a4_gemm_splitk.
+ */
+w4a4_status_t w4a4_gemm_splitk_noalloc(const uint8_t* xq, const float* xs, int32_t group_a,
+                                       const uint8_t* wq, const float* ws, int32_t group_w,
+                                       int64_t M, int64_t N, int64_t K, int32_t splits,
+                                       void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/* Bytes of the static buffer behind w4a4_gemm_splitk_noalloc (host-only). */
+int64_t w4a4_gemm_splitk_noalloc_max_bytes(void);
 
 /*
  * Debug export of the integer group partials P_b of w4a4_gemm, computed by the

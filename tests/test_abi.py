@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in range(7):
+    for st in range(8):
         s = lib.w4a4_status_str(st)
         assert s and s != b"unknown status"
     assert lib.w4a4_status_str(99) == b"unknown status"
@@ -219,3 +219,19 @@ def test_storage_conversion_validation(lib):
     assert st("mxfp4_scales_to_rows", None, 3, 64, P, None) == E_NULL
     assert st("nvfp4_scales_to_panels", P, 3, 128, P, None) == E_SHAPE         # K % 256
     assert st("nvfp4_scales_to_rows", P, 0, 256, None, None) == OK
+
+
+def test_noalloc_splitk_validation(lib):
+    """The no-allocation split-K entry point validates like w4a4_gemm_splitk and
+    refuses a plan larger than its static buffer before any HIP call."""
+    st = _lib.status_of
+    M, N, K = 16, 32, 256
+    assert lib.w4a4_gemm_splitk_noalloc_max_bytes() == 32 << 20
+    assert st("w4a4_gemm_splitk_noalloc", P, P, 128, P, P, 128, M, N, 200, 0, P, 0, N, None) == E_SHAPE
+    assert st("w4a4_gemm_splitk_noalloc", P, P, 96, P, P, 128, M, N, K, 0, P, 0, N, None) == E_GROUP
+    assert st("w4a4_gemm_splitk_noalloc", P, P, 128, P, P, 128, M, N, K, -1, P, 0, N, None) == E_SHAPE
+    assert st("w4a4_gemm_splitk_noalloc", P, P, 128, P, P, 128, M, N, K, 0, None, 0, N, None) == E_NULL
+    assert st("w4a4_gemm_splitk_noalloc", P, P, 128, P, P, 128, 0, N, K, 0, None, 0, N, None) == OK
+    # 8 splits of 512 x 8192 fp32 = 128 MiB > 32 MiB: W4A4_E_SCRATCH
+    assert st("w4a4_gemm_splitk_noalloc", P, P, 128, P, P, 128, 512, 8192, 4096, 8, P, 0, 8192, None) == 7
+    assert lib.w4a4_status_str(7) != b"unknown status"

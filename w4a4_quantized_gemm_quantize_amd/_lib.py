@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libw4a4.so")
 W4A4_OK = 0
 STATUS_NAMES = {
     0: "W4A4_OK", 1: "W4A4_E_NULL", 2: "W4A4_E_SHAPE", 3: "W4A4_E_GROUP",
-    4: "W4A4_E_ALIGN", 5: "W4A4_E_DTYPE", 6: "W4A4_E_HIP",
+    4: "W4A4_E_ALIGN", 5: "W4A4_E_DTYPE", 6: "W4A4_E_HIP", 7: "W4A4_E_SCRATCH",
 }
 Y_F32 = 0
 Y_F16 = 1
@@ -45,6 +45,8 @@ SIGNATURES = {
     "nvfp4_gemm": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p],
     "nvfp4_gemm_debug_partials": [_p, _p, _p, _p, _i64, _i64, _i64,
                                   _i64, _i64, _i64, _i64, _p, _p],
+    "w4a4_gemm_splitk_noalloc": [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _i32,
+                                 _p, _i32, _i64, _p],
     "w4a4_repack_int4": [_p, _i64, _i64, _p, _p, _p],
     "w4a4_unpack_int4": [_p, _i64, _i64, _p, _p],
     "w4a4_scales_to_group_major": [_p, _i64, _i64, _p, _p],
@@ -86,6 +88,8 @@ def load_library() -> ctypes.CDLL:
         lib.w4a4_status_str.restype = ctypes.c_char_p
         lib.w4a4_gemm_splitk_workspace.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
         lib.w4a4_gemm_splitk_workspace.restype = ctypes.c_int64
+        lib.w4a4_gemm_splitk_noalloc_max_bytes.argtypes = []
+        lib.w4a4_gemm_splitk_noalloc_max_bytes.restype = ctypes.c_int64
         _lib = lib
         return lib
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "w4a4.h"
 
@@ -71,6 +73,7 @@ const char* w4a4_status_str(int status) {
     case W4A4_E_ALIGN: return "misaligned pointer or leading dimension";
     case W4A4_E_DTYPE: return "unknown output dtype";
     case W4A4_E_HIP: return "HIP launch error";
+    case W4A4_E_SCRATCH: return "needs more scratch memory than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -312,6 +315,66 @@ w4a4_status_t nvfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xs,
   g.y = nullptr; g.ydtype = 0; g.ldy = 0;
   g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc; g.partials = partials;
   w4a4::launch_nvfp4_gemm(g, nullptr, nullptr, as_stream(stream));
+  return launched();
+}
+
+// ------------------------------------------------------ no-allocation split-K
+}  // extern "C"
+
+namespace {
+
+// Split-K partial outputs of w4a4_gemm_splitk_noalloc: a file-scope device
+// array, one copy per GPU, alive until the process ends. Its name is a host
+// stand-in, not a device address: host code only ever uses the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchBytes = int64_t{32} << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up once per device), or
+// nullptr when the runtime reports an error.
+float* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t w4a4_gemm_splitk_noalloc_max_bytes(void) { return kScratchBytes; }
+
+w4a4_status_t w4a4_gemm_splitk_noalloc(const uint8_t* xq, const float* xs, int32_t group_a,
+                                       const uint8_t* wq, const float* ws, int32_t group_w,
+                                       int64_t M, int64_t N, int64_t K, int32_t splits,
+                                       void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  GemmArgs g = {};
+  w4a4_status_t st = gemm_common(xq, xs, group_a, wq, ws, group_w, M, N, K, g);
+  if (st != W4A4_OK || M == 0 || N == 0) return st;
+  if (splits < 0) return W4A4_E_SHAPE;
+  if ((st = check_y(y, y_dtype, N, ldy)) != W4A4_OK) return st;
+  g.y = y; g.ydtype = y_dtype; g.ldy = ldy;
+  g.m0 = 0; g.mc = M; g.n0 = 0; g.nc = N; g.partials = nullptr;
+  const w4a4::SplitPlan pl = w4a4::plan_w4a4_splitk(M, N, K, group_a, group_w, splits);
+  if (pl.splits == 1) {
+    w4a4::launch_w4a4_gemm(g, as_stream(stream));
+    return launched();
+  }
+  // every split writes its whole [M][N] partial output: nothing needs clearing
+  if ((int64_t)pl.splits * M * N * 4 > kScratchBytes) return W4A4_E_SCRATCH;
+  float* ws_dev = device_scratch();
+  if (!ws_dev) return W4A4_E_HIP;
+  w4a4::launch_w4a4_gemm_splitk(g, pl, ws_dev, as_stream(stream));
   return launched();
 }
 

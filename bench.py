@@ -63,6 +63,22 @@ def source_sha256(fmt: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def gemm_alg_bytes(fmt: str, M: int, layers, kmul: int, ydt, ga: int = 128, gw: int = 128) -> float:
+    """Mean algorithmic HBM bytes of one GEMM launch: codes and scales of both
+    operands read once, Y written once."""
+    import torch
+    ybytes = 4 if ydt == torch.float32 else 2
+    tot = 0
+    for L in layers:
+        K, N = kmul * L["K"], L["N"]
+        if fmt == "int4":
+            tot += (M + N) * (K // 2) + M * 4 * (K // ga) + N * 4 * (K // gw) + ybytes * M * N
+        else:
+            sb = K // 16 if fmt == "nvfp4" else K // 32
+            tot += (M + N) * (K // 2 + sb) + ybytes * M * N
+    return tot / len(layers)
+
+
 def measured_traffic(fmt: str, workload: str, tokens: int):
     """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE record, scaled by the copy-kernel calibration; None when there is
@@ -140,6 +156,52 @@ def quant_standalone(shapes, ga, fmt, reps: int = 24, nrot: int = 6):
     return rows, tot_bytes / tot_s / 1e9
 
 
+PROBE_KINDS = {"int8": 0, "fp8": 1, "fp6": 2, "fp4": 3, "fp16": 4}
+VENDOR_PEAKS = {"int8_tops": PEAK_INT8_TOPS, "fp8_tflops": 5000.0, "fp6_tflops": PEAK_FP4_TFLOPS,
+                "fp4_tflops": PEAK_FP4_TFLOPS, "fp16_tflops": PEAK_FP16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+
+
+def measure_peaks(iters: int = 16000, reps: int = 3, hbm_bytes: int = 2 << 30):
+    """The box's own peaks, from the library's probe kernels (w4a4_probe.h):
+    back-to-back MFMAs of each kind on pseudo-random operands, and HBM read /
+    copy streams over buffers 8x the 256 MB last-level cache. Best of ``reps``
+    HIP-event-timed launches after one warm-up; units TOPS / TFLOP/s / GB/s."""
+    import torch
+    from w4a4_quantized_gemm_quantize_amd import _lib
+    lib = _lib.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.empty(lib.w4a4_probe_sink_bytes() // 4, dtype=torch.float32, device="cuda:0")
+    out = {}
+
+    def best_seconds(launch):
+        launch()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            dt = e0.elapsed_time(e1) / 1e3
+            best = dt if best is None else min(best, dt)
+        return best
+
+    for name, kind in PROBE_KINDS.items():
+        sec = best_seconds(lambda: _lib.call("w4a4_probe_mfma", kind, iters, sink.data_ptr(), stream))
+        unit = "tops" if name == "int8" else "tflops"
+        out[f"{name}_{unit}"] = lib.w4a4_probe_mfma_ops(kind, iters) / sec / 1e12
+    buf = torch.empty(hbm_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    sec = best_seconds(lambda: _lib.call("w4a4_probe_hbm_read", buf.data_ptr(), hbm_bytes, sink.data_ptr(), stream))
+    out["hbm_read_gbs"] = hbm_bytes / sec / 1e9
+    half = hbm_bytes // 2
+    dst = torch.empty(half // 4, dtype=torch.float32, device="cuda:0")
+    sec = best_seconds(lambda: _lib.call("w4a4_probe_hbm_copy", buf.data_ptr(), half, dst.data_ptr(), stream))
+    out["hbm_copy_gbs"] = 2 * half / sec / 1e9
+    del buf, dst
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
     """Time the CPU oracle (C++, std::thread over every core this process may
     use) on n_rows tokens x n_cols output features per linear, all of K:
@@ -204,6 +266,9 @@ def main() -> int:
     ap.add_argument("--cpu-cols", type=int, default=4096)
     ap.add_argument("--quant-only", action="store_true",
                     help="only the standalone activation-quantization timing (for profiling)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the box's matrix-core and HBM peaks with the probe kernels")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak probes in a bench run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -216,6 +281,10 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration()
+    if args.peaks:
+        pk = measure_peaks()
+        print(json.dumps({"peaks_measured": pk, "peaks_vendor": VENDOR_PEAKS}), flush=True)
+        return 0
 
     import numpy as np
     import torch
@@ -346,6 +415,9 @@ def main() -> int:
 
     q_rows, q_gbs = quant_standalone(act_shapes, ga, fmt)
     log(f"standalone act-quant: {q_gbs:.0f} GB/s")
+    peaks = None if args.no_peaks else measure_peaks()
+    if peaks:
+        log("measured peaks: " + ", ".join(f"{k} {v:.0f}" for k, v in peaks.items()))
 
     result = {
         "metric": (METRIC if args.workload == "llama2_70b_ffn"
@@ -381,6 +453,24 @@ def main() -> int:
         "per_linear": per_linear,
         "fraction_of_mfma_peak_incl_quant": value / peak,
     }
+    if peaks:
+        # the same achieved rate against the box's measured peaks: the graded
+        # peak's instruction, and the instruction the GEMM actually issues
+        graded = {"int4": "int8_tops", "nvfp4": "fp16_tflops"}.get(fmt, "fp4_tflops")
+        issued = {"int4": "fp6_tflops", "nvfp4": "fp16_tflops"}.get(fmt, "fp4_tflops")
+        result["peaks_measured"] = peaks
+        result["roofline_vs_measured"] = {
+            "graded_peak": graded, "graded_peak_measured": peaks[graded],
+            "frac_of_measured": achieved / peaks[graded],
+            "issued_instruction": issued, "issued_peak_vendor": VENDOR_PEAKS[issued],
+            "issued_peak_measured": peaks[issued],
+            "frac_of_issued_vendor": achieved / VENDOR_PEAKS[issued],
+            "frac_of_issued_measured": achieved / peaks[issued],
+            "act_quant_standalone_frac_of_measured_copy": q_gbs / peaks["hbm_copy_gbs"],
+        }
+        if result["roofline"]["traffic"]:
+            result["roofline_vs_measured"]["traffic_over_algorithmic"] = (
+                result["roofline"]["traffic"] / gemm_alg_bytes(fmt, M, layers, kmul, ydt, ga, gw))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, M, ga, gw, fmt, args.cpu_rows, args.cpu_cols)

@@ -6,6 +6,7 @@ The validation calls below return before any HIP call, so they run without a
 GPU. Pointers passed are fake but never dereferenced on those paths.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -14,14 +15,14 @@ import pytest
 from w4a4_quantized_gemm_quantize_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "w4a4.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, E_NULL, E_SHAPE, E_GROUP, E_ALIGN, E_DTYPE = 0, 1, 2, 3, 4, 5
 P = 0x10000          # a fake, 64 KiB-aligned "device pointer"
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     out = {}
     for m in re.finditer(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(([^;]*?)\)\s*;", text, flags=re.M | re.S):
@@ -235,3 +236,17 @@ def test_noalloc_splitk_validation(lib):
     # 8 splits of 512 x 8192 fp32 = 128 MiB > 32 MiB: W4A4_E_SCRATCH
     assert st("w4a4_gemm_splitk_noalloc", P, P, 128, P, P, 128, 512, 8192, 4096, 8, P, 0, 8192, None) == 7
     assert lib.w4a4_status_str(7) != b"unknown status"
+
+
+def test_probe_validation(lib):
+    st = _lib.status_of
+    assert lib.w4a4_probe_sink_bytes() >= 4 * 2048 * 256
+    assert lib.w4a4_probe_mfma_ops(0, 10) == 2 * 32 * 32 * 32 * 4 * 10 * 4 * 2048
+    assert lib.w4a4_probe_mfma_ops(2, 10) == 2 * lib.w4a4_probe_mfma_ops(0, 10)
+    assert lib.w4a4_probe_mfma_ops(9, 10) == -1
+    assert st("w4a4_probe_mfma", 5, 10, P, None) == E_SHAPE
+    assert st("w4a4_probe_mfma", 0, 0, P, None) == E_SHAPE
+    assert st("w4a4_probe_mfma", 0, 10, None, None) == E_NULL
+    assert st("w4a4_probe_hbm_read", P, 24, P, None) == E_SHAPE
+    assert st("w4a4_probe_hbm_read", P + 8, 32, P, None) == E_ALIGN
+    assert st("w4a4_probe_hbm_copy", P, 32, None, None) == E_NULL

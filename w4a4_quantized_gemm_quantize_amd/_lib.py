@@ -48,6 +48,9 @@ SIGNATURES = {
     "w4a4_gemm_splitk_noalloc": [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _i32,
                                  _p, _i32, _i64, _p],
     "w4a4_repack_int4": [_p, _i64, _i64, _p, _p, _p],
+    "w4a4_probe_mfma": [_i32, _i64, _p, _p],
+    "w4a4_probe_hbm_read": [_p, _i64, _p, _p],
+    "w4a4_probe_hbm_copy": [_p, _i64, _p, _p],
     "w4a4_unpack_int4": [_p, _i64, _i64, _p, _p],
     "w4a4_scales_to_group_major": [_p, _i64, _i64, _p, _p],
     "w4a4_scales_to_row_major": [_p, _i64, _i64, _p, _p],
@@ -88,6 +91,10 @@ def load_library() -> ctypes.CDLL:
         lib.w4a4_status_str.restype = ctypes.c_char_p
         lib.w4a4_gemm_splitk_workspace.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
         lib.w4a4_gemm_splitk_workspace.restype = ctypes.c_int64
+        lib.w4a4_probe_sink_bytes.argtypes = []
+        lib.w4a4_probe_sink_bytes.restype = ctypes.c_int64
+        lib.w4a4_probe_mfma_ops.argtypes = [_i32, _i64]
+        lib.w4a4_probe_mfma_ops.restype = ctypes.c_int64
         lib.w4a4_gemm_splitk_noalloc_max_bytes.argtypes = []
         lib.w4a4_gemm_splitk_noalloc_max_bytes.restype = ctypes.c_int64
         _lib = lib

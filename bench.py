@@ -269,6 +269,8 @@ def main() -> int:
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the box's matrix-core and HBM peaks with the probe kernels")
     ap.add_argument("--no-peaks", action="store_true", help="skip the peak probes in a bench run")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="few tokens: quantize and multiply in two launches even where the fused path applies")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -297,7 +299,7 @@ def main() -> int:
         ga = args.group_a
     ydt = torch.float32 if args.ydtype == "f32" else torch.float16
     dev = torch.device("cuda:0")
-    _lib.load_library()
+    lib = _lib.load_library()
     log(f"workload {args.workload}: M={M} linears={wl} ga={ga} gw={gw} fmt={fmt}")
     act_shapes = sorted({(M, K) for K, _ in wl})
     if args.quant_only:
@@ -342,12 +344,21 @@ def main() -> int:
             layers[-1].update(gx=gxt, gw=gwt)
         log(f"linear {li}: K={K} N={N} ready")
     torch.cuda.synchronize()
+    # few tokens: one fused launch per linear (activation quantization inside
+    # the GEMM) when every linear takes it and --no-fused is not given
+    for L in layers:
+        L["fused"] = fmt == "int4" and not args.no_fused and ops.use_fused(M, L["N"], L["K"], ga, gw)
+    fused = [L["fused"] for L in layers]
+    if any(fused):
+        log(f"int4 path: fused quantization + GEMM (one launch) for linears {[i for i, f in enumerate(fused) if f]}")
 
     def step(ev=None):
         for li, L in enumerate(layers):
             if ev is not None:
                 ev[li][0].record()
-            if fmt == "int4":
+            if fmt == "int4" and L["fused"]:
+                pass                          # quantized inside the fused launch below
+            elif fmt == "int4":
                 ops.w4a4_quantize_act(L["x"], ga, out=(L["xq"], L["xs"]))
             elif fmt == "mxfp4":
                 ops.mxfp4_quantize(L["x"], out=(L["xq"], L["xs"]))
@@ -357,7 +368,9 @@ def main() -> int:
                 ops.mxfp4_quantize_residual(L["x"], out=(L["xq"], L["xs"]))
             if ev is not None:
                 ev[li][1].record()
-            if fmt == "int4":
+            if fmt == "int4" and L["fused"]:
+                ops.w4a4_linear(L["x"], L["wq"], L["ws"], ga, gw, out=L["y"], fused=True)
+            elif fmt == "int4":
                 ops.w4a4_gemm_splitk(L["xq"], L["xs"], ga, L["wq"], L["ws"], gw, out=L["y"], workspace=L["wsp"])
             elif fmt == "nvfp4":
                 ops.nvfp4_gemm(L["xq"], L["xs"], L["gx"], L["wq"], L["ws"], L["gw"], out=L["y"])
@@ -371,18 +384,32 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    def timed(per_launch_events):
+        """args.steps steps between two HIP events on the launch stream. A spin
+        kernel holds the stream while the host enqueues them, so they run back
+        to back as a captured graph would (at few tokens a launch takes longer
+        to enqueue than to run); the start event is queued behind the spin,
+        which is not timed. Returns (seconds, per-step launch events or None)."""
+        evs = ([[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
+                for _ in range(args.steps)] if per_launch_events else None)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e6) * args.steps)
+        start.record()
+        for s in range(args.steps):
+            step(evs[s] if evs else None)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / 1e3, evs
+
+    # the step time (value) from a pass with no events between launches (an
+    # event pair costs a few microseconds, as much as a decode-sized launch);
+    # per-launch times (roofline, per-linear figures) from a second pass
     t0 = time.perf_counter()
-    start.record()
-    for s in range(args.steps):
-        step(evs[s])
-    end.record()
-    torch.cuda.synchronize()
+    elapsed, _ = timed(False)
     wall = time.perf_counter() - t0
-    elapsed = start.elapsed_time(end) / 1e3
     log(f"timed {args.steps} steps: {elapsed * 1e3:.2f} ms (wall {wall * 1e3:.2f} ms)")
+    _, evs = timed(True)
 
     ops_per_step = sum(2 * M * L["N"] * L["K"] for L in layers)
     value = ops_per_step * args.steps / elapsed / 1e12
@@ -440,6 +467,8 @@ def main() -> int:
             "linears_KxN": [f"{K}x{N}" for K, N in wl],
             "group_a": ga if fmt in ("int4", "nvfp4") else 32, "group_w": gw if fmt in ("int4", "nvfp4") else 32,
             "y_dtype": args.ydtype, "parallelism": "single GPU",
+            "int4_path": (["fused quantization + GEMM" if f else "quantize, then GEMM" for f in fused]
+                          if fmt == "int4" else None),
         },
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

@@ -164,6 +164,30 @@ int64_t w4a4_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t grou
                                    int32_t splits);
 
 /*
+ * Fused decode path: w4a4_quantize_act of X followed by w4a4_gemm, in ONE
+ * launch, for few tokens (load balancing and launch count at decode; COMET
+ * abstract on the "Daily Papers" page: fine-grained scheduling of W4A4
+ * kernels). Every workgroup quantizes X itself (the same rule and arithmetic
+ * as w4a4_quantize_act) into on-chip memory and runs the few-token GEMM on
+ * it, so the path only serves tiny M x K; w4a4_linear_fused_supported says
+ * when. Y is bit-identical to w4a4_gemm(w4a4_quantize_act(X), ...).
+ *
+ *   x        fp16 [M][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0
+ *   group_a  64, 128, 256 or 512; group_w and wq, ws as for w4a4_gemm
+ *   M, N, K  1 <= M <= 32 and 24 M K/32 + 4 M K/group_a + the cross-wave
+ *            reduction buffer (12 or 28 KiB) within 64 KiB (LLaMA-2-70B
+ *            FFN: M <= 8 for w1/w3, K = 8192; M = 1 for w2, K = 28672);
+ *            otherwise W4A4_E_SHAPE
+ *   y        as for w4a4_gemm
+ */
+w4a4_status_t w4a4_linear_fused(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group_a,
+                                const uint8_t* wq, const float* ws, int32_t group_w, int64_t N,
+                                void* y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/* 1 if w4a4_linear_fused takes these extents and groups, else 0 (host-only). */
+int32_t w4a4_linear_fused_supported(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w);
+
+/*
  * w4a4_gemm_splitk for callers that cannot allocate memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same kernels and split plan, with the splits' fp32 partial outputs in a

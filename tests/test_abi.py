@@ -250,3 +250,23 @@ def test_probe_validation(lib):
     assert st("w4a4_probe_hbm_read", P, 24, P, None) == E_SHAPE
     assert st("w4a4_probe_hbm_read", P + 8, 32, P, None) == E_ALIGN
     assert st("w4a4_probe_hbm_copy", P, 32, None, None) == E_NULL
+
+
+def test_fused_linear_validation(lib):
+    st = _lib.status_of
+    sup = lib.w4a4_linear_fused_supported
+    assert sup(1, 28672, 8192, 128, 128) == 1 and sup(8, 28672, 8192, 128, 128) == 1
+    assert sup(9, 28672, 8192, 128, 128) == 0          # the LDS copy of X would not fit
+    assert sup(1, 8192, 28672, 128, 128) == 1 and sup(2, 8192, 28672, 128, 128) == 0
+    assert sup(33, 64, 256, 128, 128) == 0 and sup(4, 64, 1024, 1024, 128) == 0   # per-token A: not fused
+    assert sup(4, 64, 1024, 96, 128) == 0 and sup(0, 64, 256, 128, 128) == 0
+    f = "w4a4_linear_fused"
+    assert st(f, P, 2, 200, 200, 128, P, P, 128, 64, P, 0, 64, None) == E_SHAPE     # K % 128
+    assert st(f, P, 2, 256, 248, 128, P, P, 128, 64, P, 0, 64, None) == E_SHAPE     # ldx < K
+    assert st(f, P, 2, 256, 260, 128, P, P, 128, 64, P, 0, 64, None) == E_ALIGN     # ldx % 8
+    assert st(f, P, 2, 256, 256, 96, P, P, 128, 64, P, 0, 64, None) == E_GROUP
+    assert st(f, P, 40, 256, 256, 128, P, P, 128, 64, P, 0, 64, None) == E_SHAPE    # M > 32
+    assert st(f, P, 2, 256, 256, 128, P, P, 128, 64, P, 0, 32, None) == E_SHAPE     # ldy < N
+    assert st(f, None, 2, 256, 256, 128, P, P, 128, 64, P, 0, 64, None) == E_NULL
+    assert st(f, P + 8, 2, 256, 256, 128, P, P, 128, 64, P, 0, 64, None) == E_ALIGN
+    assert st(f, None, 0, 256, 256, 128, None, None, 128, 64, None, 0, 64, None) == OK   # empty

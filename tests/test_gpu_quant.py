@@ -145,6 +145,35 @@ def test_mxfp4_exhaustive_fp16():
     mx_check(x)
 
 
+def test_mxfp4_every_value_under_every_block_exponent():
+    """Every pair (x, E) of a finite fp16 value and a block exponent it can be
+    quantized under. A block's exponent depends only on the binade of its
+    absmax a (E = floor(log2 a) - 2, E in [-26, 13] for fp16), and x can share
+    a block with exponent E exactly when |x| <= a; so for each E the block
+    absmax is the largest fp16 of binade E + 2 and the other 31 elements sweep
+    every fp16 of magnitude up to it, both signs."""
+    f16 = np.arange(1, 0x7C00, dtype=np.uint16)                # positive finite fp16, increasing
+    v = f16.view(np.float16).astype(np.float64)
+    blocks = []
+    for E in range(-26, 14):
+        in_binade = (v >= 2.0 ** (E + 2)) & (v < 2.0 ** (E + 3))
+        a_bits = int(f16[in_binade].max())
+        xs = np.concatenate([np.arange(0, a_bits + 1, dtype=np.uint16),
+                             np.arange(0, a_bits + 1, dtype=np.uint16) | np.uint16(0x8000)])
+        n = -(-xs.size // 31)
+        pad = np.full(n * 31, 0, np.uint16)
+        pad[:xs.size] = xs
+        b = np.empty((n, 32), np.uint16)
+        b[:, 0] = a_bits
+        b[:, 1:] = pad.reshape(n, 31)
+        blocks.append(b)
+    x = np.concatenate(blocks)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 32, 32), np.uint16)]).reshape(-1, 1024).view(np.float16)
+    e8 = oracle.mxfp4_quantize(x)[1].reshape(-1)
+    assert set(np.unique(e8[e8 > 0]).tolist()) == set(range(127 - 26, 127 + 14))   # all 40 exponents occur
+    mx_check(x)
+
+
 def test_mxfp4_shapes():
     mx_check(synth.activations(16, 256, dist="normal", seed=0))
     mx_check(synth.activations(33, 3584, dist="t3", seed=5), ldx_pad=32)

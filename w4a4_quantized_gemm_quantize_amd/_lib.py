@@ -47,6 +47,7 @@ SIGNATURES = {
                                   _i64, _i64, _i64, _i64, _p, _p],
     "w4a4_gemm_splitk_noalloc": [_p, _p, _i32, _p, _p, _i32, _i64, _i64, _i64, _i32,
                                  _p, _i32, _i64, _p],
+    "w4a4_linear_fused": [_p, _i64, _i64, _i64, _i32, _p, _p, _i32, _i64, _p, _i32, _i64, _p],
     "w4a4_repack_int4": [_p, _i64, _i64, _p, _p, _p],
     "w4a4_probe_mfma": [_i32, _i64, _p, _p],
     "w4a4_probe_hbm_read": [_p, _i64, _p, _p],
@@ -91,6 +92,8 @@ def load_library() -> ctypes.CDLL:
         lib.w4a4_status_str.restype = ctypes.c_char_p
         lib.w4a4_gemm_splitk_workspace.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
         lib.w4a4_gemm_splitk_workspace.restype = ctypes.c_int64
+        lib.w4a4_linear_fused_supported.argtypes = [_i64, _i64, _i64, _i32, _i32]
+        lib.w4a4_linear_fused_supported.restype = ctypes.c_int32
         lib.w4a4_probe_sink_bytes.argtypes = []
         lib.w4a4_probe_sink_bytes.restype = ctypes.c_int64
         lib.w4a4_probe_mfma_ops.argtypes = [_i32, _i64]

@@ -318,6 +318,30 @@ w4a4_status_t nvfp4_gemm_debug_partials(const uint8_t* xq, const uint8_t* xs,
   return launched();
 }
 
+// -------------------------------------------------------- fused decode path
+
+int32_t w4a4_linear_fused_supported(int64_t M, int64_t N, int64_t K, int32_t group_a, int32_t group_w) {
+  if (M < 1 || N < 1 || K <= 0 || K % 128 || K > kMaxGemmK) return 0;
+  if (!gemm_groups_ok(K, group_a, group_w)) return 0;
+  return w4a4::linear_small_supported(M, N, K, group_a, group_w) ? 1 : 0;
+}
+
+w4a4_status_t w4a4_linear_fused(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group_a,
+                                const uint8_t* wq, const float* ws, int32_t group_w, int64_t N,
+                                void* y, int32_t y_dtype, int64_t ldy, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128 || K > kMaxGemmK || ldx < K) return W4A4_E_SHAPE;
+  if (!gemm_groups_ok(K, group_a, group_w)) return W4A4_E_GROUP;
+  if (ldx % 8) return W4A4_E_ALIGN;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!w4a4_linear_fused_supported(M, N, K, group_a, group_w)) return W4A4_E_SHAPE;
+  w4a4_status_t st = check_y(y, y_dtype, N, ldy);
+  if (st != W4A4_OK) return st;
+  if (!x || !wq || !ws) return W4A4_E_NULL;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(ws, 4)) return W4A4_E_ALIGN;
+  w4a4::launch_w4a4_linear_small(x, M, K, ldx, group_a, wq, ws, group_w, N, y, y_dtype, ldy, as_stream(stream));
+  return launched();
+}
+
 // ------------------------------------------------------ no-allocation split-K
 }  // extern "C"
 

@@ -54,6 +54,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace w4a4 {
 
@@ -771,6 +772,147 @@ __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_gemm_small(Params p, int
   }
 }
 
+// ---- Few tokens, activations quantized in the GEMM (fused decode path) -------
+// At decode the activation quantization is a launch of its own in front of a
+// ~25-35 us W stream. Here each workgroup quantizes all M x K activations
+// itself -- dense lanes, one 32-element chunk per lane, the quantizer's
+// arithmetic (quant_common.h) -- into an LDS copy of their FP6 operand stream
+// and scales, then runs the few-token loop above with A operands read from
+// LDS. Every workgroup repeats the quantization (M x K elements), so the path
+// pays only for tiny M x K; its W loads are issued before the quantization so
+// the stream starts at once. Codes, scales, partials and the epilogue are the
+// quantizer's and k_w4a4_gemm_small's: Y is bit-identical to w4a4_quantize_act
+// followed by w4a4_gemm.
+struct LinParams {
+  const uint16_t* x;
+  int64_t ldx;
+  const uint8_t* w;
+  const float* sw;
+  int sha, shw;               // scale column of 64-k step h = h >> sh
+  int M, N, K;
+  void* y;
+  int ydtype;
+  int64_t ldy;
+};
+
+template <int G, int SM_WAVES>
+__global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_linear_small(LinParams p, int steps_per_group) {
+  constexpr int LPG = G / 32;                   // lanes (32-element chunks) per activation group
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int cpr = p.K >> 5;                     // chunks per row
+  const int gpr = p.K / G;                      // activation groups per row
+  uint4* qm = reinterpret_cast<uint4*>(lds);                          // [M][cpr] operand words 0..3
+  uint2* qt = reinterpret_cast<uint2*>(lds + 16 * p.M * cpr);         // [M][cpr] operand words 4, 5
+  float* ss = reinterpret_cast<float*>(lds + 24 * p.M * cpr);         // [M][gpr] scales
+  float* red = ss + p.M * gpr;                                        // [SM_WAVES - 1][16][64]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int tile_n = (int)blockIdx.x * SM_TILE;
+  const int row_bytes = p.K >> 1;
+  const int w_rows = min(SM_TILE, p.N - tile_n);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
+  const int voff = l32 * row_bytes + 16 * lhi;
+  const int groups = p.K / (64 * steps_per_group);
+  const int h0 = groups * wave / SM_WAVES * steps_per_group;
+  const int h1 = groups * (wave + 1) / SM_WAVES * steps_per_group;
+
+  struct Step {
+    uint4 w;
+    float sw;
+  };
+  auto load = [&](Step& st, int h) {
+    st.w = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, voff, h * 32, 0));
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.sw + (int64_t)(h >> p.shw) * p.N + tile_n, 4 * w_rows);
+    st.sw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * l32, 0, 0));
+  };
+  Step ring[SM_RING];
+#pragma unroll
+  for (int u = 0; u < SM_RING; ++u)
+    if (h0 + u < h1) load(ring[u], h0 + u);
+
+  // ---- prologue: the workgroup's copy of the quantized activations
+  {
+    const float nz = opaque_neg_zero();
+    const int total = p.M * cpr;                // a multiple of LPG: groups stay whole
+    for (int c = threadIdx.x; c < total; c += 64 * SM_WAVES) {
+      const int row = c / cpr, col = c - row * cpr;
+      const uint4* src = reinterpret_cast<const uint4*>(p.x + row * p.ldx + col * 32);
+      uint4 raw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) raw[j] = src[j];
+      uint32_t wd[16];
+      words16(raw, wd);
+      const float a = group_max<LPG>(absmax_words<16>(wd));
+      float sc, r8, s8;
+      group_scale(a, sc, r8, s8);
+      const v6u f = int4_stream<16>(wd, r8, s8, nz);
+      qm[c] = uint4{f[0], f[1], f[2], f[3]};
+      qt[c] = uint2{f[4], f[5]};
+      if (col % LPG == 0) ss[row * gpr + col / LPG] = sc;
+    }
+  }
+  __syncthreads();
+
+  const bool arow = l32 < p.M;                  // the lane's A row exists
+  const int abase = l32 * cpr + lhi;            // chunk of step h: abase + 2 h
+  const v16f zero16 = {};
+  const v32f zero32 = {};
+  v16f acc = zero16, P = zero16;
+  int in_group = 0;
+  for (int h = h0; h < h1; h += SM_RING) {
+#pragma unroll
+    for (int u = 0; u < SM_RING; ++u) {
+      if (h + u < h1) {
+        v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (arow) {
+          const uint4 m4 = qm[abase + 2 * (h + u)];
+          const uint2 t2 = qt[abase + 2 * (h + u)];
+          a = v8i{(int)m4.x, (int)m4.y, (int)m4.z, (int)m4.w, (int)t2.x, (int)t2.y, 0, 0};
+        }
+        P = mma(a, widen(ring[u].w), P);
+        if (++in_group == steps_per_group) {
+          in_group = 0;
+          const float sa = arow ? ss[l32 * gpr + ((h + u) >> p.sha)] : 0.0f;
+          // s_a x s_w for the tile: block 0 of the two-block rank-1 product
+          const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(sa, ring[u].sw, zero32, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = fmaf(P[r], t[r], acc[r]);
+          P = zero16;
+        }
+      }
+      if ((u & 3) == 3) {
+#pragma unroll
+        for (int v = u - 3; v <= u; ++v)
+          if (h + SM_RING + v < h1) load(ring[v], h + SM_RING + v);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < SM_WAVES - 1; ++w)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += red[(w * 16 + r) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * lhi + (r & 3);
+      const int n = tile_n + l32;
+      if (m < p.M && n < p.N) {
+        if (p.ydtype == 0)
+          static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[r];
+        else
+          static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[r]);
+      }
+    }
+  }
+}
+
 template <int NW>
 void launch_small(const GemmArgs& g, const Params& p, dim3 grid, int spg, hipStream_t stream) {
   if (g.partials)
@@ -804,6 +946,10 @@ void launch_mode_tm(int mode, const Params& p, dim3 grid, hipStream_t stream) {
 // one-stage-ahead loads and per-k-step epilogue measured 6-10 % slower on 256
 // rows at LLaMA-2-70B FFN shapes), else 256.
 int tile_rows(int64_t M, int64_t gmin) { return M > 128 && gmin != 64 ? 256 : 128; }
+
+// Waves per workgroup of the few-token kernels for an N-column output (the
+// grid is one 32-column tile per workgroup): 8 below 512 workgroups, else 4.
+int small_waves(int64_t tiles) { return tiles < 512 ? 8 : 4; }
 
 template <bool PARTIALS, bool ROWA>
 void launch_mode(int mode, int tm, const Params& p, dim3 grid, hipStream_t stream) {
@@ -855,7 +1001,7 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     // waves per workgroup from the whole product's grid, so a partials window
     // runs the configuration the plain launch of this shape runs
     const int64_t nwg = ((g.M + SM_TILE - 1) / SM_TILE) * ((g.N + SM_TILE - 1) / SM_TILE);
-    if (nwg < 512)
+    if (small_waves(nwg) == 8)
       launch_small<8>(g, p, grid, spg, stream);
     else
       launch_small<4>(g, p, grid, spg, stream);
@@ -875,6 +1021,60 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     launch_mode<false, true>(mode, BM, p, grid, stream);
   else
     launch_mode<false, false>(mode, BM, p, grid, stream);
+}
+
+int64_t linear_small_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t ga) {
+  const int nw = small_waves((N + SM_TILE - 1) / SM_TILE);
+  return 24 * M * (K / 32) + 4 * M * (K / ga) + 4 * 16 * 64 * (nw - 1);
+}
+
+template <int NW>
+void launch_linear_waves(int ga, dim3 grid, size_t lds, const LinParams& p, int spg, hipStream_t stream) {
+  const dim3 block(64 * NW);
+  switch (ga) {
+    case 64: hipLaunchKernelGGL((k_w4a4_linear_small<64, NW>), grid, block, lds, stream, p, spg); break;
+    case 128: hipLaunchKernelGGL((k_w4a4_linear_small<128, NW>), grid, block, lds, stream, p, spg); break;
+    case 256: hipLaunchKernelGGL((k_w4a4_linear_small<256, NW>), grid, block, lds, stream, p, spg); break;
+    default: hipLaunchKernelGGL((k_w4a4_linear_small<512, NW>), grid, block, lds, stream, p, spg); break;
+  }
+}
+
+bool linear_small_supported(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw) {
+  if (M < 1 || M > SM_TILE || N < 1) return false;
+  if (ga != 64 && ga != 128 && ga != 256 && ga != 512) return false;
+  if (K % ga || K % gw || K % 128) return false;
+  const int64_t gmin = ga < gw ? ga : gw;
+  if ((ga > gw ? ga : gw) % gmin) return false;
+  return linear_small_lds_bytes(M, N, K, ga) <= kLinearSmallLds;
+}
+
+void launch_w4a4_linear_small(const void* x, int64_t M, int64_t K, int64_t ldx, int ga, const uint8_t* wq,
+                              const float* ws, int gw, int64_t N, void* y, int ydtype, int64_t ldy,
+                              hipStream_t stream) {
+  LinParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.ldx = ldx;
+  p.w = wq;
+  p.sw = ws;
+  p.sha = scale_shift(ga, K);
+  p.shw = scale_shift(gw, K);
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.y = y;
+  p.ydtype = ydtype;
+  p.ldy = ldy;
+  const int64_t gmin = ga < gw ? ga : gw;
+  const int spg = (int)(gmin / 64);
+  const int tiles_n = (int)((N + SM_TILE - 1) / SM_TILE);
+  const size_t lds = (size_t)linear_small_lds_bytes(M, N, K, ga);
+  const dim3 grid((unsigned)tiles_n);
+  // the same wave count as the few-token GEMM of this shape, so the waves'
+  // K ranges and the fixed-order sum of their accumulators are the same
+  if (small_waves(tiles_n) == 8)
+    launch_linear_waves<8>(ga, grid, lds, p, spg, stream);
+  else
+    launch_linear_waves<4>(ga, grid, lds, p, spg, stream);
 }
 
 SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int requested) {

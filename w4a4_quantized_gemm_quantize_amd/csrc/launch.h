@@ -45,6 +45,15 @@ SplitPlan plan_w4a4_splitk(int64_t M, int64_t N, int64_t K, int ga, int gw, int 
 void launch_w4a4_gemm_splitk(const GemmArgs& a, const SplitPlan& plan, float* workspace, hipStream_t stream);
 void launch_mxfp4_gemm(const GemmArgs& a, hipStream_t stream);
 
+// Fused decode path: activation quantization in the few-token GEMM (one
+// launch). Supported when M <= 32, the activation group is 64/128/256/512 and
+// the workgroup's LDS copy of the quantized activations fits kLinearSmallLds.
+constexpr int64_t kLinearSmallLds = 64 * 1024;
+bool linear_small_supported(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw);
+void launch_w4a4_linear_small(const void* x, int64_t M, int64_t K, int64_t ldx, int ga, const uint8_t* wq,
+                              const float* ws, int gw, int64_t N, void* y, int ydtype, int64_t ldy,
+                              hipStream_t stream);
+
 // NVFP4: *gscale = fl32(max|x| / 2688) (0 for rows == 0)
 void launch_nvfp4_global_scale(const void* x, int64_t rows, int64_t K, int64_t ldx, float* gscale,
                                hipStream_t stream);

@@ -61,56 +61,18 @@ constexpr int64_t kMaxGridY = 65535;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Correctly rounded x / d given r = RN(1/d) (d normal, no overflow/underflow).
-__device__ __forceinline__ float div_rn(float x, float d, float r) {
-  const float q0 = x * r;
-  const float e = fmaf(-q0, d, x);
-  return fmaf(e, r, q0);
-}
-
 // Bits of a word at positions 3, 4 (mod 6), where the stream's first word is
 // zero, and at 0, 5 (mod 6), where its third word is zero; together they cover
 // every bit the second word can have set.
 constexpr uint32_t kFoldX = 0x18618618u;
 constexpr uint32_t kFoldY = 0x61861861u;
 
-// Group scale s, and r8 = RN(1/s) / 8, s8 = 8 s for the scaled division
-// (r8 = 0 for an all-zero group, so every code is a zero of the input's sign).
-__device__ __forceinline__ void group_scale(float a, float& s, float& r8, float& s8) {
-  constexpr float r7 = 1.0f / 7.0f;      // RN(1/7), folded at compile time
-  s = div_rn(a, 7.0f, r7);
-  r8 = ((s == 0.0f) ? 0.0f : 1.0f / s) * 0.125f;   // correctly rounded division
-  s8 = s * 8.0f;
-}
-
-// t / 8 with t = RN(x / s), sign of x kept on zero results. nz is -0.0 held in a
-// register (an fma with a literal -0 addend would be rewritten as a multiply,
-// which cannot read the fp16 operand directly).
-__device__ __forceinline__ float quot8(_Float16 h, float r8, float s8, float nz) {
-  const float x = (float)h;
-  const float q0 = fmaf(x, r8, nz);
-  const float en = fmaf(q0, s8, -x);
-  return fmaf(-en, r8, q0);
-}
-
 // Codes of the 2 NW fp16 values of w[0..NW) (NW = 16 or 8): the 192-bit FP6
-// stream of up to 32 codes, folded into 8-byte units (out.x/y: codes 0..15,
-// out.z/w: codes 16..31).
+// stream of up to 32 codes (int4_stream), folded into 8-byte units (out.x/y:
+// codes 0..15, out.z/w: codes 16..31).
 template <int NW>
 __device__ __forceinline__ uint4 int4_codes(const uint32_t* w, float r8, float s8, float nz) {
-  v16f ev, od;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i < NW) {
-      const h2 v = __builtin_bit_cast(h2, w[i]);
-      ev[i] = quot8(v.x, r8, s8, nz);   // k = 2i   -> field 2i
-      od[i] = quot8(v.y, r8, s8, nz);   // k = 2i+1 -> field 2i+1
-    } else {
-      ev[i] = 0.0f;
-      od[i] = 0.0f;
-    }
-  }
-  const auto f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  const v6u f = int4_stream<NW>(w, r8, s8, nz);
   return uint4{f[0] | (f[1] & kFoldX), f[2] | (f[1] & kFoldY),
                f[3] | (f[4] & kFoldX), f[5] | (f[4] & kFoldY)};
 }

@@ -56,4 +56,60 @@ __device__ __forceinline__ uint4 e2m1_codes32_f32(const float v[32]) {
   return uint4{o[0], o[1], o[2], o[3]};
 }
 
+// ---- INT4 rule (symmetric, s = fl32(a / 7), q = rne(fl32(x / s))): shared by
+// the quantizer and the GEMM kernels that quantize their own activations, so
+// both take every decision with the same instructions.
+
+typedef float v16f_q __attribute__((ext_vector_type(16)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+
+// Correctly rounded x / d given r = RN(1/d) (d normal, no overflow/underflow).
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+  const float q0 = x * r;
+  const float e = fmaf(-q0, d, x);
+  return fmaf(e, r, q0);
+}
+
+// Group scale s, and r8 = RN(1/s) / 8, s8 = 8 s for the scaled division
+// (r8 = 0 for an all-zero group, so every code is a zero of the input's sign).
+__device__ __forceinline__ void group_scale(float a, float& s, float& r8, float& s8) {
+  constexpr float r7 = 1.0f / 7.0f;      // RN(1/7), folded at compile time
+  s = div_rn(a, 7.0f, r7);
+  r8 = ((s == 0.0f) ? 0.0f : 1.0f / s) * 0.125f;   // correctly rounded division
+  s8 = s * 8.0f;
+}
+
+// t / 8 with t = RN(x / s), sign of x kept on zero results. nz is -0.0 held in a
+// register (an fma with a literal -0 addend would be rewritten as a multiply,
+// which cannot read the fp16 operand directly).
+__device__ __forceinline__ float quot8(_Float16 h, float r8, float s8, float nz) {
+  const float x = (float)h;
+  const float q0 = fmaf(x, r8, nz);
+  const float en = fmaf(q0, s8, -x);
+  return fmaf(-en, r8, q0);
+}
+
+// The 192-bit FP6 E2M3 stream of the codes of the 2 NW fp16 values of
+// w[0..NW) (NW = 16 or 8; missing values are zero codes): field k (bits 6k ..
+// 6k+5) is sign << 5 | |q_k|, the operand form of the block-scaled FP6 matrix
+// instruction. v_cvt_scalef32_2xpk16_fp6_f32 rounds t/8 (|t| <= 7 (1 + 2^-23),
+// the subnormal range of FP6 E2M3, spaced 1/8) to nearest even: rne(t) / 8.
+template <int NW>
+__device__ __forceinline__ v6u int4_stream(const uint32_t* w, float r8, float s8, float nz) {
+  v16f_q ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < NW) {
+      const h2 v = __builtin_bit_cast(h2, w[i]);
+      ev[i] = quot8(v.x, r8, s8, nz);   // k = 2i   -> field 2i
+      od[i] = quot8(v.y, r8, s8, nz);   // k = 2i+1 -> field 2i+1
+    } else {
+      ev[i] = 0.0f;
+      od[i] = 0.0f;
+    }
+  }
+  const auto f = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  return v6u{f[0], f[1], f[2], f[3], f[4], f[5]};
+}
+
 }  // namespace w4a4

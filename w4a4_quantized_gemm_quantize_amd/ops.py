@@ -155,6 +155,53 @@ def w4a4_gemm_splitk(xq, xs, group_a: int, wq, ws, group_w: int, splits: int = 0
     return y
 
 
+# Largest M * K for which w4a4_linear picks the fused launch by itself: every
+# workgroup of the fused kernel quantizes all of X, so the saved launch only
+# pays for tiny inputs (LLaMA-2-70B FFN decode, measured: M = 1 and M = 4 of
+# w1/w3 faster fused, M = 8 slower).
+FUSED_MAX_ELEMENTS = 32768
+
+
+def use_fused(M: int, N: int, K: int, group_a: int, group_w: int) -> bool:
+    """Whether w4a4_linear takes the fused launch for this shape by default."""
+    from ._lib import load_library
+    return (0 < M * K <= FUSED_MAX_ELEMENTS and N > 0 and
+            bool(load_library().w4a4_linear_fused_supported(M, N, K, group_a, group_w)))
+
+
+def w4a4_linear(x: torch.Tensor, wq, ws, group_a: int = 128, group_w: int = 128, out_dtype=torch.float32,
+                out=None, fused: bool | None = None):
+    """A W4A4 linear layer on fp16 activations: Y = Q(X) Q(W)^T with X quantized
+    per group of ``group_a`` here. For few tokens (tiny M x K) one fused launch
+    quantizes and multiplies (``w4a4_linear_fused``); otherwise the activation
+    quantizer runs first and the GEMM (with its automatic K split) after it.
+    ``fused``: None picks (:func:`use_fused`), True requires the fused path,
+    False forbids it."""
+    from ._lib import load_library
+    _need(x, torch.float16, "x")
+    _need(wq, torch.uint8, "wq")
+    _need(ws, torch.float32, "ws")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] * 2 != K:
+        raise ValueError("K of x and wq differ")
+    _need_scales(ws, K, group_w, N, "ws")
+    ok = M > 0 and N > 0 and bool(load_library().w4a4_linear_fused_supported(M, N, K, group_a, group_w))
+    if fused and not ok:
+        raise ValueError(f"the fused path does not take M={M} N={N} K={K} group_a={group_a}")
+    if fused is None:
+        fused = use_fused(M, N, K, group_a, group_w)
+    if fused:
+        y = _y_out(out, M, N, out_dtype, x.device)
+        call("w4a4_linear_fused", x.data_ptr(), M, K, x.stride(0), group_a, wq.data_ptr(), ws.data_ptr(),
+             group_w, N, y.data_ptr(), _ydtype(y.dtype), y.stride(0), _stream(x))
+        return y
+    xq, xs = w4a4_quantize_act(x, group_a)
+    return w4a4_gemm_splitk(xq, xs, group_a, wq, ws, group_w, out_dtype=out_dtype, out=out)
+
+
 def w4a4_gemm_debug_partials(xq, xs, group_a: int, wq, ws, group_w: int, m0: int, mc: int, n0: int, nc: int):
     """Exact int32 group partials P_b for the window; shape [K/g, mc, nc]."""
     for t, dt, n in ((xq, torch.uint8, "xq"), (wq, torch.uint8, "wq"),

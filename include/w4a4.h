@@ -269,6 +269,22 @@ w4a4_status_t mxfp4_quantize_residual(const void* x, int64_t rows, int64_t K, in
                                       uint8_t* q, uint8_t* e8m0, void* stream);
 
 /*
+ * Two-pass MXFP4 with the second scale tied to the first: the reading of the
+ * Multi-Scale Dequant abstract (APEX4 page) under which its "error bound 1/64
+ * per block" holds. Per 32-block with absmax a:
+ *   first pass:  E1 = the smallest integer with a <= 6 2^E1 (so no element
+ *                clips; an all-zero block takes E1 = -125), codes =
+ *                E2M1(x / 2^E1) (nearest, ties to even, sign kept);
+ *   second pass: r = x - deq(first) (exact), E2 = E1 - 2 (|r| <= 2^E1 keeps
+ *                |r| / 2^E2 <= 4: no clipping), codes = E2M1(r / 2^E2);
+ * so |x - deq(first) - deq(second)| <= 2^(E1 + 3) / 64 per element.
+ * Shapes, layouts and the GEMM use as for mxfp4_quantize_residual (the first
+ * pass differs from mxfp4_quantize's OCP exponent when a / 2^E would clip).
+ */
+w4a4_status_t mxfp4_quantize_residual_tied(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                           uint8_t* q, uint8_t* e8m0, void* stream);
+
+/*
  * The weight side of the appended-residual GEMM: the MXFP4 quantization of
  * the rows of W written twice along K, [Q(w) | Q(w)] (shapes and layouts as
  * for mxfp4_quantize_residual, K' = 2K). Offline, like weight packing.

@@ -45,6 +45,7 @@ from .mxfp4 import (  # noqa: F401
     e2m1_decode,
     mxfp4_quantize,
     mxfp4_quantize_residual,
+    mxfp4_quantize_residual_tied,
     mxfp4_append_copy,
     mxfp4_dequantize,
     mxfp4_block_partials,

@@ -33,6 +33,7 @@ _SIGS = {
     "orc_e2m1_value": ([ctypes.c_uint8], _f64),
     "orc_mxfp4_quantize": ([_p, _i64, _i64, _p, _p, _i32], _i32),
     "orc_mxfp4_quantize_residual": ([_p, _i64, _i64, _p, _p, _i32], _i32),
+    "orc_mxfp4_quantize_residual_tied": ([_p, _i64, _i64, _p, _p, _i32], _i32),
     "orc_mxfp4_dequantize": ([_p, _p, _i64, _i64, _p], None),
     "orc_fp4_block_partials": ([_p, _p, _i64, _i64, _i64, _i64, _p, _i32], _i32),
     "orc_mxfp4_gemm": ([_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _i32], _i32),

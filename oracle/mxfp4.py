@@ -90,6 +90,26 @@ def mxfp4_quantize_residual(x: np.ndarray):
     return codes, e8m0
 
 
+def mxfp4_quantize_residual_tied(x: np.ndarray):
+    """Two-pass MXFP4 with the second scale tied to the first: the reading under
+    which the Multi-Scale Dequant abstract's "error bound 1/64 per block"
+    holds. First pass: the smallest block exponent E1 with max|x| <= 6 2^E1
+    (no element clips, so the residual r = x - deq(Q1(x)) satisfies
+    |r| <= 2^E1); second pass: r at the fixed exponent E2 = E1 - 2 (no element
+    clips either). Then |x - deq(Q1) - deq(Q2)| <= 2^(E1 - 3) = 2^(E1 + 3) / 64
+    per element. An all-zero block takes E1 = -125. Returns ``(codes, e8m0)``
+    as :func:`mxfp4_quantize_residual` ([Q1 | Q2] along K)."""
+    xb = _f16_bits(x)
+    R, K = xb.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    codes = np.empty((R, 2 * K), dtype=np.uint8)
+    e8m0 = np.empty((R, 2 * K // MX_BLOCK), dtype=np.uint8)
+    nat.check(nat.lib().orc_mxfp4_quantize_residual_tied(nat.ptr(xb), R, K, nat.ptr(codes), nat.ptr(e8m0),
+                                                         nat.threads))
+    return codes, e8m0
+
+
 def mxfp4_append_copy(codes: np.ndarray, e8m0: np.ndarray):
     """The weight side of the appended-residual GEMM: each row's codes and
     scales twice along K, so that [Q(x) | Q(R)] @ [Q(w) | Q(w)]^T =

@@ -313,6 +313,47 @@ int mxfp4_quantize_residual(const uint16_t* x, int64_t R, int64_t K, uint8_t* co
   return 0;
 }
 
+// Two passes with the second scale tied to the first (the reading under which
+// the Multi-Scale Dequant abstract's "error bound 1/64 per block" holds): the
+// first pass takes the smallest E1 with max|x| <= 6 2^E1 (nothing clips, so
+// |r| <= 2^E1, half the widest E2M1 spacing), the second quantizes
+// r = x - deq(Q1(x)) at the fixed scale E2 = E1 - 2 (|r| 2^-E2 <= 4: nothing
+// clips), so |x - deq(Q1) - deq(Q2)| <= 2^(E1-3) = 2^(E1+3) / 64. An all-zero
+// block takes E1 = -125 (bytes 2 and 0: both scales in range, codes 0).
+// Layout as mxfp4_quantize_residual: [Q1(x) | Q2(r)] along K.
+int mxfp4_quantize_residual_tied(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* e8m0,
+                                 int threads) {
+  if (R < 0 || K <= 0 || K % 32) return 2;
+  for (int64_t i = 0; i < R * K; ++i)
+    if (!finite16(x[i])) return 1;
+  const int64_t nb = K / 32;
+  parallel_rows(R, threads, [&](int64_t r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      double v[32], a = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        v[i] = (double)f16_to_f32(x[r * K + b * 32 + i]);
+        a = std::max(a, std::fabs(v[i]));
+      }
+      int E1 = -125;
+      if (a > 0.0) {
+        E1 = -125;
+        while (a > 6.0 * std::ldexp(1.0, E1)) ++E1;     // smallest E1 with a <= 6 2^E1
+      }
+      const int E2 = E1 - 2;
+      uint8_t* c1 = codes + r * 2 * K + b * 32;
+      uint8_t* c2 = codes + r * 2 * K + K + b * 32;
+      for (int i = 0; i < 32; ++i) {
+        c1[i] = (uint8_t)((std::signbit(v[i]) ? 8 : 0) | e2m1_nearest(std::fabs(std::ldexp(v[i], -E1))));
+        const double res = v[i] - std::ldexp(e2m1_value(c1[i]), E1);
+        c2[i] = (uint8_t)((std::signbit(res) ? 8 : 0) | e2m1_nearest(std::fabs(std::ldexp(res, -E2))));
+      }
+      e8m0[r * 2 * nb + b] = (uint8_t)(E1 + 127);
+      e8m0[r * 2 * nb + nb + b] = (uint8_t)(E2 + 127);
+    }
+  }, K);
+  return 0;
+}
+
 // x_hat = v 2^E (binary64, exact)
 void mxfp4_dequantize(const uint8_t* codes, const uint8_t* e8m0, int64_t R, int64_t K, double* out) {
   for (int64_t r = 0; r < R; ++r)
@@ -516,6 +557,10 @@ int orc_mxfp4_quantize(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, 
 int orc_mxfp4_quantize_residual(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* e8m0,
                                 int threads) {
   return mxfp4_quantize_residual(x, R, K, codes, e8m0, threads);
+}
+int orc_mxfp4_quantize_residual_tied(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* e8m0,
+                                     int threads) {
+  return mxfp4_quantize_residual_tied(x, R, K, codes, e8m0, threads);
 }
 void orc_mxfp4_dequantize(const uint8_t* codes, const uint8_t* e8m0, int64_t R, int64_t K, double* out) {
   mxfp4_dequantize(codes, e8m0, R, K, out);

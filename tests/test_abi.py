@@ -122,7 +122,7 @@ def test_mxfp4_validation(lib):
     assert mq(P, 4, 64, 68, P, P, None) == E_ALIGN
     assert mq(P, 0, 64, 64, None, None, None) == OK
     assert mq(None, 4, 64, 64, P, P, None) == E_NULL
-    for fn in ("mxfp4_quantize_residual", "mxfp4_quantize_append_copy"):
+    for fn in ("mxfp4_quantize_residual", "mxfp4_quantize_append_copy", "mxfp4_quantize_residual_tied"):
         r = lambda *a: _lib.status_of(fn, *a)
         assert r(P, 4, 48, 48, P, P, None) == E_SHAPE
         assert r(P, 4, 64, 68, P, P, None) == E_ALIGN

@@ -28,6 +28,8 @@ def res_check(x16, ldx_pad=0, fn="mxfp4_quantize_residual"):
     q, e = getattr(ops(), fn)(xt)
     if fn == "mxfp4_quantize_residual":
         codes, e8 = oracle.mxfp4_quantize_residual(x16)
+    elif fn == "mxfp4_quantize_residual_tied":
+        codes, e8 = oracle.mxfp4_quantize_residual_tied(x16)
     else:
         codes, e8 = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(x16))
     assert np.array_equal(oracle.from_panels(host(e), oracle.e8m0_panel_offsets(R, 2 * K)), e8), f"{fn} E8M0 (R={R} K={K})"
@@ -35,7 +37,8 @@ def res_check(x16, ldx_pad=0, fn="mxfp4_quantize_residual"):
     assert bad.size == 0, f"{fn} codes differ at {bad[:5].tolist()} (R={R} K={K})"
 
 
-@pytest.mark.parametrize("fn", ["mxfp4_quantize_residual", "mxfp4_quantize_append_copy"])
+@pytest.mark.parametrize("fn", ["mxfp4_quantize_residual", "mxfp4_quantize_append_copy",
+                                "mxfp4_quantize_residual_tied"])
 def test_shapes(fn):
     res_check(synth.activations(16, 256, dist="normal", seed=0), fn=fn)
     res_check(synth.activations(33, 3584, dist="t3", seed=5), ldx_pad=32, fn=fn)
@@ -102,3 +105,41 @@ def test_qwen_w13_sampled():
     cw, ew = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w[cols]))
     Y, T = oracle.mxfp4_gemm(ca, ea, cw, ew)
     assert_y_close(y[np.ix_(rows, cols)], Y, T, "qwen w13 appended")
+
+
+def test_tied_every_value_under_every_first_exponent():
+    """The tied two-pass quantizer bit for bit over every (x, E1) pair an fp16
+    block can produce (the blocks of the oracle pin that proves the 1/64 bound)."""
+    f16 = np.arange(1, 0x7C00, dtype=np.uint16)
+    v = f16.view(np.float16).astype(np.float64)
+    blocks = []
+    for E1 in range(-25, 15):
+        sel = (v <= 6 * 2.0 ** E1) & (v > 6 * 2.0 ** (E1 - 1))
+        a = int(f16[sel].max())
+        xs = np.concatenate([np.arange(0, a + 1, dtype=np.uint16),
+                             np.arange(0, a + 1, dtype=np.uint16) | np.uint16(0x8000)])
+        n = -(-xs.size // 31)
+        pad = np.zeros(n * 31, np.uint16)
+        pad[:xs.size] = xs
+        b = np.empty((n, 32), np.uint16)
+        b[:, 0] = a
+        b[:, 1:] = pad.reshape(n, 31)
+        blocks.append(b)
+    x = np.concatenate(blocks)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 32, 32), np.uint16)]).reshape(-1, 1024).view(np.float16)
+    res_check(x, fn="mxfp4_quantize_residual_tied")
+
+
+def test_tied_gemm():
+    """The unchanged block-scaled GEMM over the tied activation side and the
+    appended weight copy: Y within the oracle bound."""
+    M, N, K = 130, 200, 768
+    x = synth.activations(M, K, dist="t3", seed=12)
+    w = synth.weights(N, K, seed=13)
+    q, e = ops().mxfp4_quantize_residual_tied(dev(x))
+    wq, we = ops().mxfp4_quantize_append_copy(dev(w))
+    y = host(ops().mxfp4_gemm(q, e, wq, we))
+    ca, ea = oracle.mxfp4_quantize_residual_tied(x)
+    cw, ew = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w))
+    Y, T = oracle.mxfp4_gemm(ca, ea, cw, ew)
+    assert_y_close(y, Y, T, "tied two-pass GEMM")

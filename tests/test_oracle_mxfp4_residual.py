@@ -85,3 +85,95 @@ def test_appended_gemm_is_the_sum_of_two_gemms():
     wd = oracle.mxfp4_dequantize(cw, ew)
     ref = xf @ wd.T
     assert np.abs(Y - ref).mean() < 0.5 * np.abs(Y1 - ref).mean()
+
+
+# ------------------------------------------ second scale tied to the first
+def test_tied_worked_block():
+    """One block worked by hand under the tied reading. absmax 7: the smallest
+    E1 with 7 <= 6 2^E1 is 1 (6 2^0 = 6 < 7), so v1 = x / 2: 3.5 is a tie
+    between 3 and 4 and goes to the even code 4 (code 6); 0.2998046875 / 2 =
+    0.1499 rounds to 0 (code 0); -2.599609375 / 2 = -1.2998 to -1.5 (code
+    8|3); -0 stays -0 (code 8); 2.5 is a tie between 2 and 3 and goes to 2
+    (code 4). Residuals: -1, 0.2998046875, 0.400390625, 0, 1; E2 = E1 - 2 =
+    -1, so v2 = 2r: -2 (code 8|4), 0.599609375 to 0.5 (code 1), 0.80078125
+    to 1 (code 2), 0 (code 0), 2 (code 4)."""
+    x = np.zeros((1, 32), np.float16)
+    x[0, :5] = [7.0, 0.3, -2.6, -0.0, 5.0]
+    codes, e8 = oracle.mxfp4_quantize_residual_tied(x)
+    assert list(e8[0]) == [128, 126]
+    assert list(codes[0, :5]) == [6, 0, 11, 8, 4] and not codes[0, 5:32].any()
+    assert list(codes[0, 32:37]) == [12, 1, 2, 0, 4] and not codes[0, 37:].any()
+    deq = oracle.mxfp4_dequantize(codes, e8)
+    assert list((deq[:, :32] + deq[:, 32:])[0, :5]) == [7.0, 0.25, -2.5, 0.0, 5.0]
+
+
+def _tied_blocks():
+    """Every finite fp16 x under every first-pass exponent E1 it can meet: for
+    each E1 the block absmax is the largest fp16 a with a <= 6 2^E1 and
+    a > 6 2^(E1-1) (so the rule picks exactly E1), the other 31 elements sweep
+    every fp16 of magnitude up to a, both signs."""
+    f16 = np.arange(1, 0x7C00, dtype=np.uint16)
+    v = f16.view(np.float16).astype(np.float64)
+    blocks = []
+    for E1 in range(-25, 15):
+        sel = (v <= 6 * 2.0 ** E1) & (v > 6 * 2.0 ** (E1 - 1))
+        if not sel.any():
+            continue
+        a = int(f16[sel].max())
+        xs = np.concatenate([np.arange(0, a + 1, dtype=np.uint16),
+                             np.arange(0, a + 1, dtype=np.uint16) | np.uint16(0x8000)])
+        n = -(-xs.size // 31)
+        pad = np.zeros(n * 31, np.uint16)
+        pad[:xs.size] = xs
+        b = np.empty((n, 32), np.uint16)
+        b[:, 0] = a
+        b[:, 1:] = pad.reshape(n, 31)
+        blocks.append(b)
+    x = np.concatenate(blocks)
+    return np.concatenate([x, np.zeros(((-x.shape[0]) % 8, 32), np.uint16)]).reshape(-1, 256).view(np.float16)
+
+
+def test_tied_bound_one_64th_of_the_block_range_exhaustive():
+    """The Multi-Scale Dequant abstract's "error bound 1/64 per block" under the
+    tied reading, over every (x, E1) pair an fp16 block can produce:
+    |x - deq(Q1) - deq(Q2)| <= 2^(E1 + 3) / 64, E1 is the smallest exponent with
+    max|x| <= 6 2^E1, E2 = E1 - 2, and neither pass clips (|v1| <= 6, |v2| <= 4)."""
+    x = _tied_blocks()
+    codes, e8 = oracle.mxfp4_quantize_residual_tied(x)
+    R, K = x.shape
+    E1 = e8[:, :K // 32].astype(np.int64) - 127
+    E2 = e8[:, K // 32:].astype(np.int64) - 127
+    xf = x.astype(np.float64).reshape(R, K // 32, 32)
+    a = np.abs(xf).max(axis=2)
+    nz = a > 0
+    assert np.all(E2[nz] == E1[nz] - 2)
+    assert np.all(a[nz] <= 6 * np.ldexp(1.0, E1[nz])) and np.all(a[nz] > 6 * np.ldexp(1.0, E1[nz] - 1))
+    assert set(np.unique(E1[nz]).tolist()) == set(range(-25, 15))
+    d = oracle.mxfp4_dequantize(codes, e8)
+    d1 = d[:, :K].reshape(R, K // 32, 32)
+    d2 = d[:, K:].reshape(R, K // 32, 32)
+    err = np.abs(xf - d1 - d2)
+    bound = np.ldexp(1.0, E1 + 3)[:, :, None] / 64
+    assert np.all(err <= bound)
+    assert err.max() == 0 or np.any(err == bound)            # the bound is reached: it is tight
+    # no clipping in either pass: |v1| <= 6, |v2| <= 4 before rounding
+    r = xf - d1
+    assert np.all(np.abs(xf) <= 6 * np.ldexp(1.0, E1)[:, :, None])
+    assert np.all(np.abs(r) <= 4 * np.ldexp(1.0, E2)[:, :, None])
+
+
+def test_tied_appended_gemm_and_accuracy():
+    """The tied activation side multiplies with the same appended weights, and
+    its worst element error (relative to the block absmax, below 1/24 since a
+    > 3 2^E1) is smaller than the own-scale reading's."""
+    x = synth.activations(64, 1024, dist="t3", seed=5)
+    ct, et = oracle.mxfp4_quantize_residual_tied(x)
+    cr, er = oracle.mxfp4_quantize_residual(x)
+    xf = x.astype(np.float64)
+    a = np.repeat(np.abs(xf.reshape(64, 32, 32)).max(axis=2), 32, axis=1)
+    a[a == 0] = 1
+    dt = oracle.mxfp4_dequantize(ct, et)
+    dr = oracle.mxfp4_dequantize(cr, er)
+    rel_t = (np.abs(xf - dt[:, :1024] - dt[:, 1024:]) / a).max()
+    rel_r = (np.abs(xf - dr[:, :1024] - dr[:, 1024:]) / a).max()
+    assert rel_t < 1 / 24 and rel_t < rel_r

@@ -37,6 +37,7 @@ SIGNATURES = {
     "mxfp4_quantize": [_p, _i64, _i64, _i64, _p, _p, _p],
     "mxfp4_quantize_residual": [_p, _i64, _i64, _i64, _p, _p, _p],
     "mxfp4_quantize_append_copy": [_p, _i64, _i64, _i64, _p, _p, _p],
+    "mxfp4_quantize_residual_tied": [_p, _i64, _i64, _i64, _p, _p, _p],
     "mxfp4_gemm": [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _i64, _p],
     "mxfp4_gemm_debug_partials": [_p, _p, _p, _p, _i64, _i64, _i64,
                                   _i64, _i64, _i64, _i64, _p, _p],

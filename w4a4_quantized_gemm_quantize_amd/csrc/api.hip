@@ -196,6 +196,11 @@ w4a4_status_t mxfp4_quantize_residual(const void* x, int64_t rows, int64_t K, in
   return mx_quant(x, rows, K, ldx, q, e8m0, 1, stream);
 }
 
+w4a4_status_t mxfp4_quantize_residual_tied(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                           uint8_t* q, uint8_t* e8m0, void* stream) {
+  return mx_quant(x, rows, K, ldx, q, e8m0, 3, stream);
+}
+
 w4a4_status_t mxfp4_quantize_append_copy(const void* w, int64_t rows, int64_t K, int64_t ldw,
                                          uint8_t* q, uint8_t* e8m0, void* stream) {
   return mx_quant(w, rows, K, ldw, q, e8m0, 2, stream);

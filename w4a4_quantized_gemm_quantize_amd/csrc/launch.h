@@ -11,7 +11,8 @@ void launch_int4_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int gro
                        uint8_t* q, float* s, hipStream_t stream);
 
 // mode 0: MXFP4 codes of x; 1: [Q(x) | Q(x - deq Q(x))] along K (width 2K);
-// 2: [Q(x) | Q(x)] (width 2K)
+// 2: [Q(x) | Q(x)] (width 2K); 3: as 1 with the second scale tied to the
+// first (first exponent: nothing clips; second: the first minus 2)
 void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
                         uint8_t* q, uint8_t* e8m0, int mode, hipStream_t stream);
 

@@ -210,7 +210,11 @@ __device__ __forceinline__ int64_t panel_offset(int rows, int nbo, int row, int 
 // matrix twice as wide along K (2 nb blocks per row): block b and, at b + nb,
 // the MX quantization of the residual x - deq(Q(x)) (the activation side of
 // the appended-residual GEMM), or a copy of Q(x) (its weight side).
-enum { MX_PLAIN = 0, MX_APPEND_RESIDUAL = 1, MX_APPEND_COPY = 2 };
+// APPEND_TIED is APPEND_RESIDUAL with the second scale tied to the first: the
+// first pass takes the smallest E1 with max|x| <= 6 2^E1 (nothing clips), the
+// second quantizes the residual at E2 = E1 - 2 (nothing clips either), which
+// bounds the error by 2^(E1 + 3) / 64 per element.
+enum { MX_PLAIN = 0, MX_APPEND_RESIDUAL = 1, MX_APPEND_COPY = 2, MX_APPEND_TIED = 3 };
 
 // The E2M1 values (unit scale) of the 8 codes of a word, element 2i from the
 // low nibble of byte i.
@@ -229,6 +233,15 @@ __device__ __forceinline__ void e2m1_values8(uint32_t w, float v[8]) {
 __device__ __forceinline__ int block_exponent(float a) {
   const int biased = (int)((__float_as_uint(a) >> 23) & 0xFF);
   return (a == 0.0f) ? -127 : biased - 127 - 2;
+}
+
+// Smallest E with a <= 6 2^E for a block with absmax a: with a = 2^e (1 + f),
+// e - 2 when f <= 1/2 (4 (1 + f) <= 6), else e - 1; -125 for an all-zero block
+// (2^-125 and 2^-127 are then the two scales, both normal in fp32).
+__device__ __forceinline__ int block_exponent_noclip(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const int e = (int)((u >> 23) & 0xFF) - 127;
+  return (a == 0.0f) ? -125 : ((u & 0x7FFFFFu) <= 0x400000u ? e - 2 : e - 1);
 }
 
 // Lane tile: a lane takes one 32-element block of a row (absmax within the
@@ -263,15 +276,16 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
     uint32_t w[16];
     words16(raw, w);
     const float a = absmax_words<16>(w);
-    const int E = block_exponent(a);
-    const float d = (a == 0.0f) ? 1.0f : __uint_as_float((uint32_t)(E + 127) << 23);   // 2^E, normal
+    const int E = MODE == MX_APPEND_TIED ? block_exponent_noclip(a) : block_exponent(a);
+    const float d = (a == 0.0f && MODE != MX_APPEND_TIED) ? 1.0f
+                                                          : __uint_as_float((uint32_t)(E + 127) << 23);   // 2^E, normal
     const uint4 c = e2m1_codes32(w, d);
     store_codes(row, b, c);
     e8m0[panel_offset(rows, nbo, row, b)] = (uint8_t)(E + 127);
     if constexpr (MODE == MX_APPEND_COPY) {
       store_codes(row, nb + b, c);
       e8m0[panel_offset(rows, nbo, row, nb + b)] = (uint8_t)(E + 127);
-    } else if constexpr (MODE == MX_APPEND_RESIDUAL) {
+    } else if constexpr (MODE == MX_APPEND_RESIDUAL || MODE == MX_APPEND_TIED) {
       // r = x - deq(Q(x)), exact in fp32 (at most 16 significant bits); the
       // E2M1 value of each code comes back from the reverse conversion
       const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
@@ -290,7 +304,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_mxfp4_quant(
           ar = fmaxf(ar, fmaxf(fabsf(r[k]), fabsf(r[k + 1])));
         }
       }
-      const int E2 = block_exponent(ar);
+      const int E2 = MODE == MX_APPEND_TIED ? E - 2 : block_exponent(ar);
 #pragma unroll
       for (int k = 0; k < 32; ++k) r[k] = ldexpf(r[k], -E2);   // exact
       store_codes(row, nb + b, e2m1_codes32_f32(r));
@@ -338,6 +352,10 @@ void launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ldx,
       return;
     case MX_APPEND_COPY:
       hipLaunchKernelGGL(k_mxfp4_quant<MX_APPEND_COPY>, grid, dim3(kQuantThreads), 0, stream,
+                         xp, ldx, (int)rows, nb, q16, qp, e8m0);
+      return;
+    case MX_APPEND_TIED:
+      hipLaunchKernelGGL(k_mxfp4_quant<MX_APPEND_TIED>, grid, dim3(kQuantThreads), 0, stream,
                          xp, ldx, (int)rows, nb, q16, qp, e8m0);
       return;
     default:

@@ -264,6 +264,13 @@ def mxfp4_quantize_residual(x: torch.Tensor, out=None):
     return _mxfp4_quantize_wide("mxfp4_quantize_residual", x, out)
 
 
+def mxfp4_quantize_residual_tied(x: torch.Tensor, out=None):
+    """Two-pass MXFP4 with the second scale tied to the first (no clipping in
+    either pass; per-element error <= 2^(E1 + 3) / 64): shapes and layouts as
+    :func:`mxfp4_quantize_residual`."""
+    return _mxfp4_quantize_wide("mxfp4_quantize_residual_tied", x, out)
+
+
 def mxfp4_quantize_append_copy(w: torch.Tensor, out=None):
     """``[Q(w) | Q(w)]`` along K (shapes as :func:`mxfp4_quantize_residual`):
     the weight side of the appended-residual GEMM."""

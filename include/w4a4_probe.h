@@ -25,7 +25,8 @@ enum {
   W4A4_PROBE_FP8 = 1,    /* v_mfma_scale_f32_32x32x64_f8f6f4, FP8 E4M3 operands */
   W4A4_PROBE_FP6 = 2,    /* the same, FP6 E2M3 operands (the INT4 GEMM's instruction) */
   W4A4_PROBE_FP4 = 3,    /* the same, FP4 E2M1 operands (the MXFP4 GEMM's instruction) */
-  W4A4_PROBE_FP16 = 4    /* v_mfma_f32_32x32x16_f16 (the NVFP4 GEMM's instruction) */
+  W4A4_PROBE_FP16 = 4,   /* v_mfma_f32_32x32x16_f16 (the NVFP4 GEMM's instruction) */
+  W4A4_PROBE_VALU_F32 = 5 /* v_fma_f32 on the vector unit (the INT4 GEMM's group epilogue) */
 };
 
 /* Bytes of device memory the `sink` of either probe must hold (host-only). */
@@ -37,7 +38,9 @@ int64_t w4a4_probe_mfma_ops(int32_t kind, int64_t iters);
 
 /*
  * A grid of waves issuing `iters` x 4 independent MFMAs of `kind` each on
- * pseudo-random operand bits (the matrix cores' clock depends on the data).
+ * pseudo-random operand bits (the matrix cores' clock depends on the data),
+ * or, for W4A4_PROBE_VALU_F32, 64 independent fp32 fmas per lane per
+ * iteration (w4a4_probe_mfma_ops counts 2 ops per fma).
  *   iters  > 0;  sink  out: w4a4_probe_sink_bytes() bytes, 4-byte aligned
  */
 w4a4_status_t w4a4_probe_mfma(int32_t kind, int64_t iters, void* sink, void* stream);

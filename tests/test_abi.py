@@ -244,7 +244,8 @@ def test_probe_validation(lib):
     assert lib.w4a4_probe_mfma_ops(0, 10) == 2 * 32 * 32 * 32 * 4 * 10 * 4 * 2048
     assert lib.w4a4_probe_mfma_ops(2, 10) == 2 * lib.w4a4_probe_mfma_ops(0, 10)
     assert lib.w4a4_probe_mfma_ops(9, 10) == -1
-    assert st("w4a4_probe_mfma", 5, 10, P, None) == E_SHAPE
+    assert st("w4a4_probe_mfma", 6, 10, P, None) == E_SHAPE
+    assert lib.w4a4_probe_mfma_ops(5, 10) == 2 * 64 * 64 * 10 * 4 * 2048   # 64 fmas per lane per iteration
     assert st("w4a4_probe_mfma", 0, 0, P, None) == E_SHAPE
     assert st("w4a4_probe_mfma", 0, 10, None, None) == E_NULL
     assert st("w4a4_probe_hbm_read", P, 24, P, None) == E_SHAPE

@@ -37,7 +37,7 @@ __device__ __forceinline__ uint32_t operand_word(int i) {
   return h & 0xBFBFBFBFu;
 }
 
-enum { P_INT8 = 0, P_FP8 = 1, P_FP6 = 2, P_FP4 = 3, P_FP16 = 4 };
+enum { P_INT8 = 0, P_FP8 = 1, P_FP6 = 2, P_FP4 = 3, P_FP16 = 4, P_VALU_F32 = 5 };
 
 template <int KIND>
 __global__ __launch_bounds__(256) void k_probe_mfma(int64_t iters, float* __restrict__ sink) {
@@ -48,7 +48,23 @@ __global__ __launch_bounds__(256) void k_probe_mfma(int64_t iters, float* __rest
     b[i] = (int)operand_word(8 + i);
   }
   float out = 0.0f;
-  if constexpr (KIND == P_INT8) {
+  if constexpr (KIND == P_VALU_F32) {
+    // 16 independent fp32 fma chains per lane, 4 steps each per iteration
+    // (64 v_fma_f32 per iteration, the same count as the MFMA loops' 4 per
+    // iteration times 16), scalar fp32: the vector unit's non-packed rate
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = __uint_as_float((operand_word(i) & 0x007FFFFFu) | 0x3F800000u);
+    const float m = __uint_as_float(0x3F7FFFF0u), c = 1.0e-7f;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = fmaf(f[i], m, c);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out += f[i];
+  } else if constexpr (KIND == P_INT8) {
     const v4i a4 = {a[0], a[1], a[2], a[3]}, b4 = {b[0], b[1], b[2], b[3]};
     v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
     for (int64_t it = 0; it < iters; ++it) {
@@ -127,6 +143,7 @@ int64_t probe_mfma_ops(int kind) {
     case P_INT8: return 2LL * 32 * 32 * 32;
     case P_FP16: return 2LL * 32 * 32 * 16;
     case P_FP8: case P_FP6: case P_FP4: return 2LL * 32 * 32 * 64;
+    case P_VALU_F32: return 2LL * 64 * 16;   // a lane's 64 fmas of one iteration = 4 x 16 (4 "instructions" per iteration below)
     default: return 0;
   }
 }
@@ -138,6 +155,7 @@ void launch_probe_mfma(int kind, int64_t iters, float* sink, hipStream_t stream)
     case P_FP8: hipLaunchKernelGGL((k_probe_mfma<P_FP8>), grid, block, 0, stream, iters, sink); break;
     case P_FP6: hipLaunchKernelGGL((k_probe_mfma<P_FP6>), grid, block, 0, stream, iters, sink); break;
     case P_FP4: hipLaunchKernelGGL((k_probe_mfma<P_FP4>), grid, block, 0, stream, iters, sink); break;
+    case P_VALU_F32: hipLaunchKernelGGL((k_probe_mfma<P_VALU_F32>), grid, block, 0, stream, iters, sink); break;
     default: hipLaunchKernelGGL((k_probe_mfma<P_FP16>), grid, block, 0, stream, iters, sink); break;
   }
 }
@@ -172,7 +190,7 @@ int64_t w4a4_probe_mfma_ops(int32_t kind, int64_t iters) {
 }
 
 w4a4_status_t w4a4_probe_mfma(int32_t kind, int64_t iters, void* sink, void* stream) {
-  if (kind < W4A4_PROBE_INT8 || kind > W4A4_PROBE_FP16 || iters <= 0) return W4A4_E_SHAPE;
+  if (kind < W4A4_PROBE_INT8 || kind > W4A4_PROBE_VALU_F32 || iters <= 0) return W4A4_E_SHAPE;
   if (!sink) return W4A4_E_NULL;
   if (reinterpret_cast<uintptr_t>(sink) % 4) return W4A4_E_ALIGN;
   w4a4::launch_probe_mfma(kind, iters, static_cast<float*>(sink), static_cast<hipStream_t>(stream));

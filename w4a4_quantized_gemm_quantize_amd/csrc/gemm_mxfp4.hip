@@ -25,6 +25,8 @@
 //
 // 32x32 MFMA output layout: D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
 // col l%32.
+#include <utility>
+
 #include "device.h"
 #include "launch.h"
 
@@ -34,7 +36,6 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
 constexpr int kFmtFp4 = 4;       // cbsz / blgp operand format code for FP4 E2M1
 constexpr int kUnitScale = 127;  // E8M0 byte of 2^0
 constexpr int kGroupRows = 4;    // tile-rows per raster group
@@ -59,6 +60,18 @@ __device__ __forceinline__ v8i as_operand(uint4 v) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in order: a
+// loop unrolled by construction (the step index stays a constant expression,
+// e.g. for the instruction's immediate byte select), whatever the body's size.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Direct buffer -> LDS copies: lane l's 16 (4) bytes from base + voff + soff
 // land at lds + 16 l (4 l). The buffer (MUBUF) form, unlike the global (FLAT)
@@ -275,12 +288,7 @@ void k_mxfp4_gemm(Params p) {
         }                                                                            \
       }                                                                              \
     } else {                                                                         \
-      switch (U) {   /* the byte select is an immediate */                           \
-        case 0: MMA_SEL(B, 0) break;                                                 \
-        case 1: MMA_SEL(B, 1) break;                                                 \
-        case 2: MMA_SEL(B, 2) break;                                                 \
-        default: MMA_SEL(B, 3) break;                                                \
-      }                                                                              \
+      MMA_SEL(B, U) /* U is a constant: the byte select is an immediate */           \
     }                                                                                \
   }
 #define MMA_SEL(B, SEL)                                                              \
@@ -333,12 +341,13 @@ void k_mxfp4_gemm(Params p) {
     LOAD_SCALES(KT, CUR);                                               \
     LOAD_OPS(CUR, 0, 0);                                                \
     if ((KT) + D < nk) ISSUE((KT) + D, NXT);                            \
-    _Pragma("unroll") for (int u_ = 0; u_ < NSTEP; ++u_) {              \
-      if (u_ + 1 < NSTEP) LOAD_OPS(CUR, u_ + 1, (u_ + 1) & 1);          \
+    static_for<NSTEP>([&](auto uc_) {                                   \
+      constexpr int u_ = decltype(uc_)::value;                          \
+      if constexpr (u_ + 1 < NSTEP) LOAD_OPS(CUR, u_ + 1, (u_ + 1) & 1); \
       PIPE_FENCE();                                                     \
       MMA_STEP(KT, u_, u_ & 1);                                         \
       PIPE_FENCE();                                                     \
-    }                                                                   \
+    });                                                                 \
   }
 
   ISSUE(0, sm0);

@@ -2,7 +2,7 @@
 quantization inside the few-token GEMM, one launch). Its output must be
 bit-identical to w4a4_quantize_act followed by w4a4_gemm (same quantizer
 arithmetic, same wave split and fixed-order sums) and within the oracle's
-bound; full-size LLaMA-2-70B decode shapes are checked on sampled columns."""
+bound; the full-size LLaMA-2-70B decode shapes are checked on every output."""
 import numpy as np
 import pytest
 
@@ -78,11 +78,10 @@ def test_fused_zero_rows_and_unsupported():
 def test_fused_llama70b_decode(M, N, K):
     o = ops()
     x = synth.activations(M, K, dist="t3", seed=0)
-    wq, ws = o.w4a4_pack_weight(dev(synth.weights(N, K, seed=0)), 128)
+    w = synth.weights(N, K, seed=0)
+    wq, ws = o.w4a4_pack_weight(dev(w), 128)
     xt = dev(x)
     y = host(o.w4a4_linear(xt, wq, ws, 128, 128, fused=True))
     assert np.array_equal(y, host(two_launch(o, xt, wq, ws, 128, 128))), "fused differs from quantize + gemm"
-    cols = synth.sample_rows(N, 384, seed=3)
-    Y, T = oracle.w4a4_gemm(*oracle.int4_quantize(x, 128), 128,
-                            *oracle.int4_quantize(synth.weights(N, K, seed=0, rows=cols), 128), 128)
-    assert_y_close(y[:, cols], Y, T, f"fused decode M={M} N={N} K={K}")
+    Y, T = oracle.w4a4_gemm(*oracle.int4_quantize(x, 128), 128, *oracle.int4_quantize(w, 128), 128)
+    assert_y_close(y, Y, T, f"fused decode M={M} N={N} K={K}")

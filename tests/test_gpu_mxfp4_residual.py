@@ -91,7 +91,7 @@ def test_appended_gemm(M, N, K):
 
 def test_qwen_w13_sampled():
     """Full-size Qwen2.5-7B w1 shape with the residual appended (K' = 7168),
-    production launch configuration; checked on sampled rows and columns."""
+    production launch configuration; checked on every column of 64 sampled rows."""
     o = ops()
     M, K, N = 4096, 3584, 18944
     x = synth.activations(M, K, dist="t3", seed=0)
@@ -99,12 +99,11 @@ def test_qwen_w13_sampled():
     xq, xe = o.mxfp4_quantize_residual(dev(x))
     wq, we = o.mxfp4_quantize_append_copy(dev(w))
     y = host(o.mxfp4_gemm(xq, xe, wq, we))
-    rows = synth.sample_rows(M, 8, seed=2)
-    cols = synth.sample_rows(N, 256, seed=3)
+    rows = synth.sample_rows(M, 64, seed=2)
     ca, ea = oracle.mxfp4_quantize_residual(x[rows])
-    cw, ew = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w[cols]))
+    cw, ew = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w))
     Y, T = oracle.mxfp4_gemm(ca, ea, cw, ew)
-    assert_y_close(y[np.ix_(rows, cols)], Y, T, "qwen w13 appended")
+    assert_y_close(y[rows], Y, T, "qwen w13 appended")
 
 
 def test_tied_every_value_under_every_first_exponent():

@@ -285,8 +285,9 @@ def test_empty_is_noop():
 
 @pytest.mark.parametrize("name", ["qwen25_7b_w13", "qwen25_7b_w2"])
 def test_qwen_shapes_sampled(name):
-    """The production launch at the Qwen2.5-7B FFN shapes, checked on a seeded
-    sample of outputs and bit-exact block integers in a window."""
+    """The production launch at the Qwen2.5-7B FFN shapes, checked on every
+    column of a seeded sample of 64 rows, and bit-exact block integers in a
+    window."""
     wl = synth.WORKLOADS[name]
     M, N, K = wl["M"], wl["N"], wl["K"]
     o = ops()
@@ -299,12 +300,11 @@ def test_qwen_shapes_sampled(name):
     sgx, sgw = oracle.nvfp4_global_scale(x), oracle.nvfp4_global_scale(w)
     del wt, xt
     y = host(o.nvfp4_gemm(xq, xs, gx, wq, ws, gw))
-    rows = synth.sample_rows(M, 8, seed=2)
-    cols = synth.sample_rows(N, 384, seed=3)
+    rows = synth.sample_rows(M, 64, seed=2)
     ca, sa = oracle.nvfp4_quantize(x[rows], sgx)
-    cw, sw = oracle.nvfp4_quantize(w[cols], sgw)
+    cw, sw = oracle.nvfp4_quantize(w, sgw)
     Y, T = oracle.nvfp4_gemm(ca, sa, sgx, cw, sw, sgw)
-    assert_y_close(y[np.ix_(rows, cols)], Y, T, name)
+    assert_y_close(y[rows], Y, T, name)
     m0, n0, win = M // 2 - 8, N // 2 - 8, 16
     part = host(o.nvfp4_gemm_debug_partials(xq, xs, wq, ws, m0, win, n0, win))
     ca2, _ = oracle.nvfp4_quantize(x[m0:m0 + win], sgx)

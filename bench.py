@@ -209,6 +209,69 @@ def cpu_baseline(wl, M, ga, gw, fmt, n_rows, n_cols):
     }
 
 
+# The configurations' oracle runs: (name, M, [(K, N), ...], g_a, format, full);
+# full = every output (the rest: a seeded 256-row sample x all N, its time
+# extrapolated to the whole problem).
+ORACLE_CONFIGS = [
+    ("C1 tiny", 16, [(256, 256)], 128, "int4", True),
+    ("C2 LLaMA-2-7B FFN", 2048, [(4096, 11008), (11008, 4096)], 128, "int4", True),
+    ("C3 LLaMA-2-70B FFN M=1", 1, [(8192, 28672), (28672, 8192)], 128, "int4", True),
+    ("C3 LLaMA-2-70B FFN M=16", 16, [(8192, 28672), (28672, 8192)], 128, "int4", True),
+    ("C3 LLaMA-2-70B FFN M=256", 256, [(8192, 28672), (28672, 8192)], 128, "int4", True),
+    ("C3 LLaMA-2-70B FFN M=4096", 4096, [(8192, 28672), (28672, 8192)], 128, "int4", False),
+    ("C4 granularity g_a=64", 4096, [(8192, 8192)], 64, "int4", False),
+    ("C4 granularity g_a=128", 4096, [(8192, 8192)], 128, "int4", False),
+    ("C4 granularity g_a=256", 4096, [(8192, 8192)], 256, "int4", False),
+    ("C4 granularity g_a=512", 4096, [(8192, 8192)], 512, "int4", False),
+    ("C4 granularity g_a=8192", 4096, [(8192, 8192)], 8192, "int4", False),
+    ("C5 Qwen2.5-7B FFN MXFP4", 4096, [(3584, 18944), (18944, 3584)], 32, "mxfp4", False),
+]
+
+
+def oracle_timing() -> int:
+    """Time the CPU oracle (every core) on each configuration, one JSON line
+    per linear: activation quantization and weight packing in full, the GEMM
+    in full where feasible, else on a seeded 256-row sample with all N and its
+    time extrapolated to the whole problem (the oracle's cost is linear in
+    M). Input generation is not timed. CPU only."""
+    import numpy as np
+    import oracle
+    from w4a4_quantized_gemm_quantize_amd import synth
+
+    oracle.set_threads(0)
+    for name, M, lin, ga, fmt, full in ORACLE_CONFIGS:
+        for li, (K, N) in enumerate(lin):
+            dist = "normal" if name.startswith("C1") else "t3"
+            x = synth.activations(M, K, dist=dist, seed=li)
+            w = synth.weights(N, K, seed=100 + li)
+            t0 = time.perf_counter()
+            if fmt == "int4":
+                qa, sa = oracle.int4_quantize(x, ga)
+            else:
+                qa, sa = oracle.mxfp4_quantize(x)
+            t_quant = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            wpk = oracle.int4_quantize(w, 128) if fmt == "int4" else oracle.mxfp4_quantize(w)
+            t_pack = time.perf_counter() - t0
+            rows = np.arange(M) if full else synth.sample_rows(M, 256, seed=11)
+            t0 = time.perf_counter()
+            if fmt == "int4":
+                oracle.w4a4_gemm(qa[rows], np.ascontiguousarray(sa[rows]), ga, wpk[0], wpk[1], 128)
+            else:
+                oracle.mxfp4_gemm(qa[rows], np.ascontiguousarray(sa[rows]), wpk[0], wpk[1])
+            t_gemm = time.perf_counter() - t0
+            macs = rows.size * N * K
+            print(json.dumps({
+                "config": name, "linear": f"K={K} N={N}", "M": M, "group_a": ga, "format": fmt,
+                "gemm_rows": int(rows.size), "gemm_full": bool(full), "threads": oracle.cores(),
+                "act_quant_s": t_quant, "weight_pack_s": t_pack, "gemm_s": t_gemm,
+                "gemm_mac_per_s": macs / t_gemm,
+                "gemm_full_s" + ("" if full else "_extrapolated"): t_gemm * M / rows.size,
+            }), flush=True)
+            del x, w, qa, sa, wpk
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +293,11 @@ def main() -> int:
                     help="few tokens: quantize and multiply in two launches even where the fused path applies")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the CPU oracle on every configuration (no GPU)")
     args = ap.parse_args()
+    if args.oracle_timing:
+        return oracle_timing()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -213,9 +213,11 @@ w4a4_status_t w4a4_gemm_splitk_noalloc(const uint8_t* xq, const float* xs, int32
 int64_t w4a4_gemm_splitk_noalloc_max_bytes(void);
 
 /*
- * Debug export of the integer group partials P_b of w4a4_gemm, computed by the
- * same load / unpack / matrix-core code, for the output window
- * [m0, m0+mc) x [n0, n0+nc):
+ * Debug export of the integer group partials P_b of w4a4_gemm for the output
+ * window [m0, m0+mc) x [n0, n0+nc), from the kernel configuration w4a4_gemm
+ * runs for the whole M x N x K product (same tile height or few-token path,
+ * same loads, widening, matrix instructions and stage schedule; the epilogue
+ * stores P_b instead of accumulating it):
  *   partials  out: int32 [K/g][mc][nc], g = min(group_a, group_w)
  * The window must lie inside [0,M) x [0,N); mc, nc > 0.
  */

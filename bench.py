@@ -290,7 +290,7 @@ def main() -> int:
     ap.add_argument("--quant-only", action="store_true",
                     help="only the standalone activation-quantization timing (for profiling)")
     ap.add_argument("--peaks", action="store_true",
-                    help="only measure the box's matrix-core and HBM peaks with the probe kernels")
+                    help="only measure this GPU's matrix-core and HBM peaks with the probe kernels")
     ap.add_argument("--no-peaks", action="store_true", help="skip the peak probes in a bench run")
     ap.add_argument("--no-fused", action="store_true",
                     help="few tokens: quantize and multiply in two launches even where the fused path applies")
@@ -304,7 +304,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
@@ -524,7 +524,7 @@ def main() -> int:
         "fraction_of_mfma_peak_incl_quant": value / peak,
     }
     if peaks:
-        # the same achieved rate against the box's measured peaks: the graded
+        # the same achieved rate against this GPU's measured peaks: the graded
         # peak's instruction, and the instruction the GEMM actually issues
         graded = {"int4": "int8_tops", "nvfp4": "fp16_tflops"}.get(fmt, "fp4_tflops")
         issued = {"int4": "fp6_tflops", "nvfp4": "fp16_tflops"}.get(fmt, "fp4_tflops")

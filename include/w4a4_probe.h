@@ -4,7 +4,7 @@
  * Measurement only, not part of the W4A4 computation: loops that reach the
  * matrix-core and HBM rates of the GPU they run on, so a kernel's roofline
  * fraction can be stated against the measured peak beside the data-sheet
- * one (the pages judge kernels by measured speedups alone: APEX4 abstract).
+ * one (the pages rate kernels by measured speedups alone: APEX4 abstract).
  * Conventions as in w4a4.h: device pointers owned by the caller, asynchronous
  * on `stream`, validation first, status codes of w4a4.h, no allocation.
  */

@@ -1,4 +1,4 @@
-// On-chip peak probes for gfx950: the rates a kernel on this machine can reach,
+// On-chip peak probes for gfx950: the rates a kernel on this GPU can reach,
 // measured rather than taken from a data sheet, so a roofline fraction can be
 // stated against both. Not part of the W4A4 computation.
 //

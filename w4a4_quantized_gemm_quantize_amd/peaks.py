@@ -1,4 +1,4 @@
-"""The box's own peaks, from the library's probe kernels (include/w4a4_probe.h):
+"""This GPU's own peaks, from the library's probe kernels (include/w4a4_probe.h):
 back-to-back MFMAs of each kind on pseudo-random operands, fp32 vector fmas,
 and HBM read / copy streams. Measurement only (roofline fractions against the
 measured peaks beside the data-sheet ones; the granularity policy's rho)."""
@@ -19,7 +19,7 @@ VENDOR_PEAKS = {"int8_tops": PEAK_INT8_TOPS, "fp8_tflops": 5000.0, "fp6_tflops":
 
 
 def measure_peaks(iters: int = 16000, reps: int = 3, hbm_bytes: int = 2 << 30):
-    """The box's own peaks, from the library's probe kernels (w4a4_probe.h):
+    """This GPU's own peaks, from the library's probe kernels (w4a4_probe.h):
     back-to-back MFMAs of each kind on pseudo-random operands, independent
     fp32 vector fmas, and HBM read / copy streams over buffers 8x the 256 MB
     last-level cache. Best of ``reps`` HIP-event-timed launches after one

@@ -15,7 +15,7 @@ g_a in {64, 128, 256, 512, K} and g_w in {group_w, K}.
 rate plus, unless g_a = K, the rank-1 scale products at the fp32 matrix rate)
 plus vector time (one fma per output per block at the vector unit's fp32 fma
 rate), added rather than overlapped (on this part a wave does not run its
-vector work under its own matrix instructions). The rates are the box's,
+vector work under its own matrix instructions). The rates are this GPU's,
 measured by the probe kernels (``peaks.measure_peaks``), so rho is measured,
 not assumed. The model ranks the candidates; the policy still times them.
 
@@ -49,7 +49,7 @@ F32_MATRIX_TFLOPS = 157.3
 
 
 def rho(rates) -> float:
-    """The box's matrix : vector throughput ratio: FP6 matrix ops (the
+    """This GPU's matrix : vector throughput ratio: FP6 matrix ops (the
     partials' instruction) per fp32 vector op."""
     return rates["fp6_tflops"] / rates["valu_f32_tflops"]
 

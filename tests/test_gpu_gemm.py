@@ -141,14 +141,17 @@ def _weights_oracle(N, K, gw):
     return _oracle_w[key]
 
 
-def sampled_case(M, N, K, ga, gw, n_rows=8, n_cols=384, window=16, full=False):
+def sampled_case(M, N, K, ga, gw, n_rows=8, n_cols=384, window=16, full=False, splitk=False):
     """The production launch at full size; Y checked against the oracle on a
-    seeded sample of outputs, or on every output (``full``)."""
+    seeded sample of outputs, or on every output (``full``). With ``splitk``
+    also w4a4_gemm_splitk's automatic plan (the benchmark's launch: a K split
+    or the plain launch, by shape)."""
     o = ops()
     wq, ws = _weights_dev(N, K, gw)
     x = synth.activations(M, K, dist="t3", seed=0)
     xq, xs = o.w4a4_quantize_act(dev(x), ga)
     y = o.w4a4_gemm(xq, xs, ga, wq, ws, gw)
+    y_auto = o.w4a4_gemm_splitk(xq, xs, ga, wq, ws, gw) if splitk else None
     if full:
         rows, cols = np.arange(M), np.arange(N)
         qw, sw = _weights_oracle(N, K, gw)
@@ -160,6 +163,8 @@ def sampled_case(M, N, K, ga, gw, n_rows=8, n_cols=384, window=16, full=False):
     Y, T = oracle.w4a4_gemm(qa, sa, ga, qw, sw, gw)
     yh = host(y)
     ratio = assert_y_close(yh[np.ix_(rows, cols)], Y, T, f"M={M} N={N} K={K} ga={ga}")
+    if splitk:
+        assert_y_close(host(y_auto)[np.ix_(rows, cols)], Y, T, f"automatic plan M={M} N={N} K={K} ga={ga}")
     # bit-exact partials on a window that straddles a tile corner
     m0 = max(0, min(M - window, M // 2 - window // 2))
     mc = min(window, M)
@@ -181,12 +186,12 @@ def test_llama7b_shapes(name):
 # the decode-to-prefill sweep, every output checked
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_llama70b_w13(M):
-    sampled_case(M, 28672, 8192, 128, 128, full=True)
+    sampled_case(M, 28672, 8192, 128, 128, full=True, splitk=True)
 
 
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_llama70b_w2(M):
-    sampled_case(M, 8192, 28672, 128, 128, full=True)
+    sampled_case(M, 8192, 28672, 128, 128, full=True, splitk=True)
 
 
 @pytest.mark.parametrize("ga", [64, 128, 256, 512, 8192])

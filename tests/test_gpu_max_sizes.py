@@ -79,3 +79,21 @@ def test_mxfp4_longest_k(data):
     cw, ew = oracle.mxfp4_quantize(w[cols])
     Y, T = oracle.mxfp4_gemm(ca, ea, cw, ew)
     assert_y_close(y[np.ix_(rows, cols)], Y, T, "MXFP4, K = 2^23")
+
+
+def test_nvfp4_longest_k(data):
+    x, w, rows, cols = data
+    o = ops()
+    print(f"nvfp4 M={M} N={N} K={KMAX}", flush=True)
+    xt, wt = dev(x), dev(w)
+    gx, gw = o.nvfp4_global_scale(xt), o.nvfp4_global_scale(wt)
+    xq, xs = o.nvfp4_quantize(xt, gx)
+    wq, ws = o.nvfp4_quantize(wt, gw)
+    del xt, wt
+    y = host(o.nvfp4_gemm(xq, xs, gx, wq, ws, gw))
+    sgx, sgw = oracle.nvfp4_global_scale(x), oracle.nvfp4_global_scale(w)
+    assert host(gx).view(np.uint32)[0] == np.float32(sgx).view(np.uint32), "global scale of X"
+    ca, sa = oracle.nvfp4_quantize(x[rows], sgx)
+    cw, sw = oracle.nvfp4_quantize(w[cols], sgw)
+    Y, T = oracle.nvfp4_gemm(ca, sa, sgx, cw, sw, sgw)
+    assert_y_close(y[np.ix_(rows, cols)], Y, T, "NVFP4, K = 2^23")

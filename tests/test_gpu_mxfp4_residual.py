@@ -106,6 +106,23 @@ def test_qwen_w13_sampled():
     assert_y_close(y[rows], Y, T, "qwen w13 appended")
 
 
+def test_qwen_w13_tied():
+    """Full-size Qwen2.5-7B w1 shape with the tied residual appended (K' = 7168):
+    every column of 64 sampled rows."""
+    o = ops()
+    M, K, N = 4096, 3584, 18944
+    x = synth.activations(M, K, dist="t3", seed=1)
+    w = synth.weights(N, K, seed=1)
+    xq, xe = o.mxfp4_quantize_residual_tied(dev(x))
+    wq, we = o.mxfp4_quantize_append_copy(dev(w))
+    y = host(o.mxfp4_gemm(xq, xe, wq, we))
+    rows = synth.sample_rows(M, 64, seed=4)
+    ca, ea = oracle.mxfp4_quantize_residual_tied(x[rows])
+    cw, ew = oracle.mxfp4_append_copy(*oracle.mxfp4_quantize(w))
+    Y, T = oracle.mxfp4_gemm(ca, ea, cw, ew)
+    assert_y_close(y[rows], Y, T, "qwen w13 tied")
+
+
 def test_tied_every_value_under_every_first_exponent():
     """The tied two-pass quantizer bit for bit over every (x, E1) pair an fp16
     block can produce (the blocks of the oracle pin that proves the 1/64 bound)."""

@@ -67,7 +67,11 @@ def test_mixed_granularity(ga, gw):
     (3, 64, 384, 384, 384),            # one per-token group on each side
     (32, 160, 512, 128, 128), (33, 160, 512, 128, 128),     # small-M path (M <= 64, few tiles)
     (65, 160, 512, 128, 128),                                # tiled path
-    (3, 16400, 512, 64, 128)])                               # 513 workgroups: four waves each
+    (3, 16400, 512, 64, 128),                                # 513 workgroups: four waves each
+    # 16-column tiles (M <= 16, groups >= 128, an uneven 32-column grid)
+    (16, 1000, 2048, 128, 128), (11, 530, 1024, 256, 128),  # ragged N; two steps per group
+    (9, 300, 2048, 128, 512), (1, 17, 256, 128, 128),       # coarser W groups; a 1-column tile
+    (2, 200, 4096, 512, 512)])                               # 4-step groups, 8 groups for 4 waves
 def test_small_m(M, N, K, ga, gw):
     run_case(M, N, K, ga, gw, seed=M + N, check_fp16=True)
 
@@ -88,6 +92,25 @@ def test_fp16_output_and_strided_y():
     assert np.all(yb[:, N:] == 7.0), "wrote outside the output window"
     y16 = o.w4a4_gemm(xq, xs, 128, wq, ws, 128, out_dtype=torch.float16)
     assert_y16_close(host(y16).astype(np.float64), Y, T, "fp16")
+
+
+def test_small_m16_fp16_and_strided_y():
+    """The 16-column few-token kernel's fp16 output and strided Y."""
+    import torch
+    M, N, K = 13, 530, 1024
+    x = synth.activations(M, K, seed=31)
+    w = synth.weights(N, K, seed=32)
+    o = ops()
+    xq, xs = o.w4a4_quantize_act(dev(x), 128)
+    wq, ws = o.w4a4_pack_weight(dev(w), 128)
+    Y, T = oracle.w4a4_gemm(*oracle.int4_quantize(x, 128), 128, *oracle.int4_quantize(w, 128), 128)
+    y16 = o.w4a4_gemm(xq, xs, 128, wq, ws, 128, out_dtype=torch.float16)
+    assert_y16_close(host(y16).astype(np.float64), Y, T, "fp16 Y, 16-column tiles")
+    big = torch.full((M, N + 24), 7.0, dtype=torch.float32, device="cuda")
+    o.w4a4_gemm(xq, xs, 128, wq, ws, 128, out=big[:, :N])
+    b = host(big)
+    assert np.all(b[:, N:] == 7.0), "padding columns written"
+    assert_y_close(b[:, :N], Y, T, "strided Y, 16-column tiles")
 
 
 def test_empty_is_noop():

@@ -772,6 +772,126 @@ __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_gemm_small(Params p, int
   }
 }
 
+// ---- Few tokens, 16-column tiles ----------------------------------------------
+// For M <= 16 and groups of 128 or more: one 16 x 16 output tile per workgroup
+// on the 16x16x128 FP6 instruction. Its operand lane layout (row l % 16,
+// 32-code chunk l / 16 of a 128-k step) makes each load instruction read 64
+// contiguous bytes from each of 16 W rows, where the 32 x 32 tile reads 32
+// bytes from each of 32 rows: measured on a W stream of the LLaMA-2-70B w1
+// shape, 6.5 against 5.35 TB/s. Twice as many workgroups also spread evenly
+// over the CUs where the 32-column grid does not (896 = 3.5 per CU for
+// N = 28672). Same K split between the waves (whole groups), same exact
+// integer partials and epilogue order as k_w4a4_gemm_small, so Y is
+// bit-identical to it; the scale product is one multiply per output.
+constexpr int SM16_TILE = 16;
+constexpr int SM16_RING = 8;        // 128-k steps in flight per wave (refilled two at a time)
+
+typedef float v4f_16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f_16 mma16(const v8i& a, const v8i& b, const v4f_16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtFp6, kFmtFp6, 0, kUnitScale, 0, kUnitScale);
+}
+
+template <bool PARTIALS, int SM_WAVES>
+__global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_gemm_small16(Params p, int steps_per_group) {
+  __shared__ float red[SM_WAVES - 1][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int tile_m = (p.tile_m0 + (int)blockIdx.x % p.tiles_m) * SM16_TILE;
+  const int tile_n = (p.tile_n0 + (int)blockIdx.x / p.tiles_m) * SM16_TILE;
+  const int row_bytes = p.K >> 1;
+  const int a_rows = min(SM16_TILE, p.M - tile_m), w_rows = min(SM16_TILE, p.N - tile_n);
+  // rows past the matrix lie past the resources and read as zero codes / scales
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
+  const int voff = l16 * row_bytes + 16 * lq;         // row l16, 32-code chunk lq of a 128-k step
+  const int groups = p.K / (128 * steps_per_group);
+  const int h0 = groups * wave / SM_WAVES * steps_per_group;
+  const int h1 = groups * (wave + 1) / SM_WAVES * steps_per_group;
+
+  struct Step {
+    uint4 a, w;
+    float4 sa;   // the scales of the lane's four output rows 4 lq .. 4 lq + 3
+    float sw;    // the scale of its output column l16
+  };
+  // operands of 128-k step h and the scales of its group's column
+  auto load = [&](Step& st, int h) {
+    st.a = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rA, voff, h * 64, 0));
+    st.w = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, voff, h * 64, 0));
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.sa + (int64_t)((2 * h) >> p.sha) * p.M + tile_m, 4 * a_rows);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.sw + (int64_t)((2 * h) >> p.shw) * p.N + tile_n, 4 * w_rows);
+    const v4u s4 = __builtin_amdgcn_raw_buffer_load_b128(ra, 16 * lq, 0, 0);
+    st.sa = float4{__uint_as_float(s4.x), __uint_as_float(s4.y), __uint_as_float(s4.z), __uint_as_float(s4.w)};
+    st.sw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * l16, 0, 0));
+  };
+
+  const v4f_16 zero4 = {};
+  v4f_16 acc = zero4, P = zero4;
+  int in_group = 0;
+  Step ring[SM16_RING];
+#pragma unroll
+  for (int u = 0; u < SM16_RING; ++u)
+    if (h0 + u < h1) load(ring[u], h0 + u);
+  for (int h = h0; h < h1; h += SM16_RING) {
+#pragma unroll
+    for (int u = 0; u < SM16_RING; ++u) {
+      if (h + u < h1) {
+        P = mma16(widen(ring[u].a), widen(ring[u].w), P);
+        if (++in_group == steps_per_group) {
+          in_group = 0;
+          if constexpr (PARTIALS) {
+            const int gidx = (h + u) / steps_per_group;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = tile_m + 4 * lq + i;
+              const int n = tile_n + l16;
+              if (m >= p.m0 && m < p.m0 + p.mc && n >= p.n0 && n < p.n0 + p.nc)
+                p.partials[((int64_t)gidx * p.mc + (m - p.m0)) * p.nc + (n - p.n0)] = (int32_t)P[i];
+            }
+          } else {
+            const float sa[4] = {ring[u].sa.x, ring[u].sa.y, ring[u].sa.z, ring[u].sa.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(P[i], sa[i] * ring[u].sw, acc[i]);
+          }
+          P = zero4;
+        }
+      }
+      // refill two steps at once: a row's two 64-byte pieces of one 128-byte
+      // W line go out back to back
+      if ((u & 1) == 1) {
+#pragma unroll
+        for (int v = u - 1; v <= u; ++v)
+          if (h + SM16_RING + v < h1) load(ring[v], h + SM16_RING + v);
+      }
+    }
+  }
+  if constexpr (!PARTIALS) {
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave - 1][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < SM_WAVES - 1; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += red[w][i][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = tile_m + 4 * lq + i;
+        const int n = tile_n + l16;
+        if (m < p.M && n < p.N) {
+          if (p.ydtype == 0)
+            static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i];
+          else
+            static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i]);
+        }
+      }
+    }
+  }
+}
+
 // ---- Few tokens, activations quantized in the GEMM (fused decode path) -------
 // At decode the activation quantization is a launch of its own in front of a
 // ~25-35 us W stream. Here each workgroup quantizes all M x K activations
@@ -923,6 +1043,14 @@ void launch_small(const GemmArgs& g, const Params& p, dim3 grid, int spg, hipStr
     hipLaunchKernelGGL((k_w4a4_gemm_small<false, false, NW>), grid, dim3(64 * NW), 0, stream, p, spg);
 }
 
+template <int NW>
+void launch_small16(const GemmArgs& g, const Params& p, dim3 grid, int spg, hipStream_t stream) {
+  if (g.partials)
+    hipLaunchKernelGGL((k_w4a4_gemm_small16<true, NW>), grid, dim3(64 * NW), 0, stream, p, spg);
+  else
+    hipLaunchKernelGGL((k_w4a4_gemm_small16<false, NW>), grid, dim3(64 * NW), 0, stream, p, spg);
+}
+
 // log2(group / 64) for a power-of-two group, 31 (a single column) for group == K.
 int scale_shift(int64_t group, int64_t K) {
   if (group == K && (group & (group - 1))) return 31;
@@ -992,15 +1120,32 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
   // tiles) would hold fewer than 128 tiles (measured crossovers on the LLaMA-2-70B FFN shapes).
   const int64_t big_tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
   if (g.M <= 32 || (g.M <= 64 && big_tiles < 128)) {
+    // waves per workgroup from the whole product's 32-column grid, so a
+    // partials window runs the configuration the plain launch of this shape
+    // runs, and both tile widths split K between the waves alike
+    const int64_t nwg = ((g.M + SM_TILE - 1) / SM_TILE) * ((g.N + SM_TILE - 1) / SM_TILE);
+    // 16-column tiles where the 32-column grid leaves the CUs unevenly loaded
+    // (LLaMA-2-70B w1: 896 workgroups; w2's 256 workgroups of 8 waves, one per
+    // CU, stream faster as they are)
+    if (g.M <= SM16_TILE && gmin >= 128 && g.ga != g.K && nwg % 256 != 0) {
+      p.tile_m0 = (int)(g.m0 / SM16_TILE);
+      p.tile_n0 = (int)(g.n0 / SM16_TILE);
+      p.tiles_m = (int)((g.m0 + g.mc - 1) / SM16_TILE) - p.tile_m0 + 1;
+      p.tiles_n = (int)((g.n0 + g.nc - 1) / SM16_TILE) - p.tile_n0 + 1;
+      const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+      const int spg = (int)(gmin / 128);
+      if (small_waves(nwg) == 8)
+        launch_small16<8>(g, p, grid, spg, stream);
+      else
+        launch_small16<4>(g, p, grid, spg, stream);
+      return;
+    }
     p.tile_m0 = (int)(g.m0 / SM_TILE);
     p.tile_n0 = (int)(g.n0 / SM_TILE);
     p.tiles_m = (int)((g.m0 + g.mc - 1) / SM_TILE) - p.tile_m0 + 1;
     p.tiles_n = (int)((g.n0 + g.nc - 1) / SM_TILE) - p.tile_n0 + 1;
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     const int spg = (int)(gmin / 64);
-    // waves per workgroup from the whole product's grid, so a partials window
-    // runs the configuration the plain launch of this shape runs
-    const int64_t nwg = ((g.M + SM_TILE - 1) / SM_TILE) * ((g.N + SM_TILE - 1) / SM_TILE);
     if (small_waves(nwg) == 8)
       launch_small<8>(g, p, grid, spg, stream);
     else

@@ -257,7 +257,9 @@ def test_fused_linear_validation(lib):
     st = _lib.status_of
     sup = lib.w4a4_linear_fused_supported
     assert sup(1, 28672, 8192, 128, 128) == 1 and sup(8, 28672, 8192, 128, 128) == 1
-    assert sup(9, 28672, 8192, 128, 128) == 0          # the LDS copy of X would not fit
+    # 16-column tiles (4 accumulators per lane to sum across waves): M = 9 fits
+    # 64 KiB, M = 10 does not; 32-column tiles (16 per lane): M = 2 at K = 28672 does not
+    assert sup(9, 28672, 8192, 128, 128) == 1 and sup(10, 28672, 8192, 128, 128) == 0
     assert sup(1, 8192, 28672, 128, 128) == 1 and sup(2, 8192, 28672, 128, 128) == 0
     assert sup(33, 64, 256, 128, 128) == 0 and sup(4, 64, 1024, 1024, 128) == 0   # per-token A: not fused
     assert sup(4, 64, 1024, 96, 128) == 0 and sup(0, 64, 256, 128, 128) == 0

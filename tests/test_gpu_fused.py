@@ -2,7 +2,8 @@
 quantization inside the few-token GEMM, one launch). Its output must be
 bit-identical to w4a4_quantize_act followed by w4a4_gemm (same quantizer
 arithmetic, same wave split and fixed-order sums) and within the oracle's
-bound; the full-size LLaMA-2-70B decode shapes are checked on every output."""
+bound; the full-size LLaMA-2-70B and 7B decode shapes (up to the largest M
+whose LDS copy of X fits) are checked on every output."""
 import numpy as np
 import pytest
 
@@ -74,8 +75,9 @@ def test_fused_zero_rows_and_unsupported():
         o.w4a4_linear(dev(np.zeros((2, 1024), np.float16)), wq1, ws1, 1024, 128, fused=True)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 28672, 8192), (8, 28672, 8192), (1, 8192, 28672)])
-def test_fused_llama70b_decode(M, N, K):
+@pytest.mark.parametrize("M,N,K", [(1, 28672, 8192), (8, 28672, 8192), (9, 28672, 8192), (1, 8192, 28672),
+                                   (7, 11008, 4096), (4, 4096, 11008)])   # last two: LLaMA-2-7B
+def test_fused_llama_decode(M, N, K):
     o = ops()
     x = synth.activations(M, K, dist="t3", seed=0)
     w = synth.weights(N, K, seed=0)

@@ -915,6 +915,34 @@ struct LinParams {
   int64_t ldy;
 };
 
+// The fused kernels' prologue: every 32-element chunk of X quantized into
+// the workgroup's LDS copy (FP6 operand words 0..3 in qm, 4..5 in qt, one
+// scale per group in ss) by NT threads, one chunk per thread per pass. A
+// version that fetched the next pass's chunk during this one measured no
+// faster at M = 1..4: the prologue's cost is its M x K re-read per workgroup.
+template <int LPG, int NT>
+__device__ __forceinline__ void quantize_to_lds(const LinParams& p, int cpr, int gpr, uint4* qm, uint2* qt,
+                                                float* ss) {
+  const float nz = opaque_neg_zero();
+  const int total = p.M * cpr;                  // a multiple of LPG: groups stay whole
+  for (int c = threadIdx.x; c < total; c += NT) {
+    const int row = c / cpr, col = c - row * cpr;
+    const uint4* src = reinterpret_cast<const uint4*>(p.x + row * p.ldx + col * 32);
+    uint4 raw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = src[j];
+    uint32_t wd[16];
+    words16(raw, wd);
+    const float a = group_max<LPG>(absmax_words<16>(wd));
+    float sc, r8, s8;
+    group_scale(a, sc, r8, s8);
+    const v6u f = int4_stream<16>(wd, r8, s8, nz);
+    qm[c] = uint4{f[0], f[1], f[2], f[3]};
+    qt[c] = uint2{f[4], f[5]};
+    if (col % LPG == 0) ss[row * gpr + col / LPG] = sc;
+  }
+}
+
 template <int G, int SM_WAVES>
 __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_linear_small(LinParams p, int steps_per_group) {
   constexpr int LPG = G / 32;                   // lanes (32-element chunks) per activation group
@@ -953,26 +981,7 @@ __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_linear_small(LinParams p
     if (h0 + u < h1) load(ring[u], h0 + u);
 
   // ---- prologue: the workgroup's copy of the quantized activations
-  {
-    const float nz = opaque_neg_zero();
-    const int total = p.M * cpr;                // a multiple of LPG: groups stay whole
-    for (int c = threadIdx.x; c < total; c += 64 * SM_WAVES) {
-      const int row = c / cpr, col = c - row * cpr;
-      const uint4* src = reinterpret_cast<const uint4*>(p.x + row * p.ldx + col * 32);
-      uint4 raw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) raw[j] = src[j];
-      uint32_t wd[16];
-      words16(raw, wd);
-      const float a = group_max<LPG>(absmax_words<16>(wd));
-      float sc, r8, s8;
-      group_scale(a, sc, r8, s8);
-      const v6u f = int4_stream<16>(wd, r8, s8, nz);
-      qm[c] = uint4{f[0], f[1], f[2], f[3]};
-      qt[c] = uint2{f[4], f[5]};
-      if (col % LPG == 0) ss[row * gpr + col / LPG] = sc;
-    }
-  }
+  quantize_to_lds<LPG, 64 * SM_WAVES>(p, cpr, gpr, qm, qt, ss);
   __syncthreads();
 
   const bool arow = l32 < p.M;                  // the lane's A row exists
@@ -1033,6 +1042,111 @@ __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_linear_small(LinParams p
   }
 }
 
+// The fused path on 16-column tiles: the quantization prologue and LDS copy
+// of k_w4a4_linear_small, the loads, instruction and epilogue of
+// k_w4a4_gemm_small16 (A operands from the LDS copy: lane row l % 16, chunk
+// 4 h + l / 16 of 128-k step h). Bit-identical to w4a4_quantize_act followed
+// by w4a4_gemm on the same tiles.
+template <int G, int SM_WAVES>
+__global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_linear_small16(LinParams p, int steps_per_group) {
+  constexpr int LPG = G / 32;                   // lanes (32-element chunks) per activation group
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int cpr = p.K >> 5;                     // chunks per row
+  const int gpr = p.K / G;                      // activation groups per row
+  uint4* qm = reinterpret_cast<uint4*>(lds);                          // [M][cpr] operand words 0..3
+  uint2* qt = reinterpret_cast<uint2*>(lds + 16 * p.M * cpr);         // [M][cpr] operand words 4, 5
+  float* ss = reinterpret_cast<float*>(lds + 24 * p.M * cpr);         // [M][gpr] scales
+  float* red = ss + p.M * gpr;                                        // [SM_WAVES - 1][4][64]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int tile_n = (int)blockIdx.x * SM16_TILE;
+  const int row_bytes = p.K >> 1;
+  const int w_rows = min(SM16_TILE, p.N - tile_n);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
+  const int voff = l16 * row_bytes + 16 * lq;
+  const int groups = p.K / (128 * steps_per_group);
+  const int h0 = groups * wave / SM_WAVES * steps_per_group;
+  const int h1 = groups * (wave + 1) / SM_WAVES * steps_per_group;
+
+  struct Step {
+    uint4 w;
+    float sw;
+  };
+  auto load = [&](Step& st, int h) {
+    st.w = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rW, voff, h * 64, 0));
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.sw + (int64_t)((2 * h) >> p.shw) * p.N + tile_n, 4 * w_rows);
+    st.sw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, 4 * l16, 0, 0));
+  };
+  Step ring[SM16_RING];
+#pragma unroll
+  for (int u = 0; u < SM16_RING; ++u)
+    if (h0 + u < h1) load(ring[u], h0 + u);
+
+  // ---- prologue: the workgroup's copy of the quantized activations
+  quantize_to_lds<LPG, 64 * SM_WAVES>(p, cpr, gpr, qm, qt, ss);
+  __syncthreads();
+
+  const bool arow = l16 < p.M;                  // the lane's A row exists
+  const int abase = l16 * cpr + lq;             // chunk of step h: abase + 4 h
+  const v4f_16 zero4 = {};
+  v4f_16 acc = zero4, P = zero4;
+  int in_group = 0;
+  for (int h = h0; h < h1; h += SM16_RING) {
+#pragma unroll
+    for (int u = 0; u < SM16_RING; ++u) {
+      if (h + u < h1) {
+        v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (arow) {
+          const uint4 m4 = qm[abase + 4 * (h + u)];
+          const uint2 t2 = qt[abase + 4 * (h + u)];
+          a = v8i{(int)m4.x, (int)m4.y, (int)m4.z, (int)m4.w, (int)t2.x, (int)t2.y, 0, 0};
+        }
+        P = mma16(a, widen(ring[u].w), P);
+        if (++in_group == steps_per_group) {
+          in_group = 0;
+          const int gcol = (2 * (h + u)) >> p.sha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * lq + i;
+            const float sa = m < p.M ? ss[m * gpr + gcol] : 0.0f;
+            acc[i] = fmaf(P[i], sa * ring[u].sw, acc[i]);
+          }
+          P = zero4;
+        }
+      }
+      if ((u & 1) == 1) {
+#pragma unroll
+        for (int v = u - 1; v <= u; ++v)
+          if (h + SM16_RING + v < h1) load(ring[v], h + SM16_RING + v);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave - 1) * 4 + i) * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < SM_WAVES - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += red[(w * 4 + i) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * lq + i;
+      const int n = tile_n + l16;
+      if (m < p.M && n < p.N) {
+        if (p.ydtype == 0)
+          static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i];
+        else
+          static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i]);
+      }
+    }
+  }
+}
+
 template <int NW>
 void launch_small(const GemmArgs& g, const Params& p, dim3 grid, int spg, hipStream_t stream) {
   if (g.partials)
@@ -1078,6 +1192,15 @@ int tile_rows(int64_t M, int64_t gmin) { return M > 128 && gmin != 64 ? 256 : 12
 // Waves per workgroup of the few-token kernels for an N-column output (the
 // grid is one 32-column tile per workgroup): 8 below 512 workgroups, else 4.
 int small_waves(int64_t tiles) { return tiles < 512 ? 8 : 4; }
+
+// Few-token tile width: 16 columns (k_w4a4_gemm_small16 and its fused twin)
+// for M <= 16 with groups of 128 or more and per-group activation scales where
+// the 32-column grid does not spread evenly over the 256 CUs, else 32.
+bool use_small16(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw) {
+  const int64_t gmin = ga < gw ? ga : gw;
+  const int64_t nwg = ((M + SM_TILE - 1) / SM_TILE) * ((N + SM_TILE - 1) / SM_TILE);
+  return M <= SM16_TILE && gmin >= 128 && ga != K && nwg % 256 != 0;
+}
 
 template <bool PARTIALS, bool ROWA>
 void launch_mode(int mode, int tm, const Params& p, dim3 grid, hipStream_t stream) {
@@ -1127,7 +1250,7 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     // 16-column tiles where the 32-column grid leaves the CUs unevenly loaded
     // (LLaMA-2-70B w1: 896 workgroups; w2's 256 workgroups of 8 waves, one per
     // CU, stream faster as they are)
-    if (g.M <= SM16_TILE && gmin >= 128 && g.ga != g.K && nwg % 256 != 0) {
+    if (use_small16(g.M, g.N, g.K, g.ga, g.gw)) {
       p.tile_m0 = (int)(g.m0 / SM16_TILE);
       p.tile_n0 = (int)(g.n0 / SM16_TILE);
       p.tiles_m = (int)((g.m0 + g.mc - 1) / SM16_TILE) - p.tile_m0 + 1;
@@ -1168,9 +1291,23 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     launch_mode<false, false>(mode, BM, p, grid, stream);
 }
 
-int64_t linear_small_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t ga) {
+// LDS of a fused launch: the FP6 operand copy (24 bytes per 32 elements), the
+// scales, and the cross-wave sum of the accumulators (16 floats per lane on
+// 32-column tiles, 4 on 16-column tiles) for every wave but the first.
+int64_t linear_small_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw) {
   const int nw = small_waves((N + SM_TILE - 1) / SM_TILE);
-  return 24 * M * (K / 32) + 4 * M * (K / ga) + 4 * 16 * 64 * (nw - 1);
+  const int acc = use_small16(M, N, K, ga, gw) ? 4 : 16;
+  return 24 * M * (K / 32) + 4 * M * (K / ga) + 4 * acc * 64 * (nw - 1);
+}
+
+template <int NW>
+void launch_linear16_waves(int ga, dim3 grid, size_t lds, const LinParams& p, int spg, hipStream_t stream) {
+  const dim3 block(64 * NW);
+  switch (ga) {
+    case 128: hipLaunchKernelGGL((k_w4a4_linear_small16<128, NW>), grid, block, lds, stream, p, spg); break;
+    case 256: hipLaunchKernelGGL((k_w4a4_linear_small16<256, NW>), grid, block, lds, stream, p, spg); break;
+    default: hipLaunchKernelGGL((k_w4a4_linear_small16<512, NW>), grid, block, lds, stream, p, spg); break;
+  }
 }
 
 template <int NW>
@@ -1190,7 +1327,7 @@ bool linear_small_supported(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t
   if (K % ga || K % gw || K % 128) return false;
   const int64_t gmin = ga < gw ? ga : gw;
   if ((ga > gw ? ga : gw) % gmin) return false;
-  return linear_small_lds_bytes(M, N, K, ga) <= kLinearSmallLds;
+  return linear_small_lds_bytes(M, N, K, ga, gw) <= kLinearSmallLds;
 }
 
 void launch_w4a4_linear_small(const void* x, int64_t M, int64_t K, int64_t ldx, int ga, const uint8_t* wq,
@@ -1212,10 +1349,18 @@ void launch_w4a4_linear_small(const void* x, int64_t M, int64_t K, int64_t ldx, 
   const int64_t gmin = ga < gw ? ga : gw;
   const int spg = (int)(gmin / 64);
   const int tiles_n = (int)((N + SM_TILE - 1) / SM_TILE);
-  const size_t lds = (size_t)linear_small_lds_bytes(M, N, K, ga);
+  const size_t lds = (size_t)linear_small_lds_bytes(M, N, K, ga, gw);
+  // the tile width and wave count of the few-token GEMM of this shape, so the
+  // waves' K ranges and the fixed-order sum of their accumulators are the same
+  if (use_small16(M, N, K, ga, gw)) {
+    const dim3 grid16((unsigned)((N + SM16_TILE - 1) / SM16_TILE));
+    if (small_waves(tiles_n) == 8)
+      launch_linear16_waves<8>(ga, grid16, lds, p, (int)(gmin / 128), stream);
+    else
+      launch_linear16_waves<4>(ga, grid16, lds, p, (int)(gmin / 128), stream);
+    return;
+  }
   const dim3 grid((unsigned)tiles_n);
-  // the same wave count as the few-token GEMM of this shape, so the waves'
-  // K ranges and the fixed-order sum of their accumulators are the same
   if (small_waves(tiles_n) == 8)
     launch_linear_waves<8>(ga, grid, lds, p, spg, stream);
   else

@@ -155,17 +155,25 @@ def w4a4_gemm_splitk(xq, xs, group_a: int, wq, ws, group_w: int, splits: int = 0
     return y
 
 
-# Largest M * K for which w4a4_linear picks the fused launch by itself: every
-# workgroup of the fused kernel quantizes all of X, so the saved launch only
-# pays for tiny inputs (LLaMA-2-70B FFN decode, measured: M = 1 and M = 4 of
-# w1/w3 faster fused, M = 8 slower).
-FUSED_MAX_ELEMENTS = 32768
+# When w4a4_linear picks the fused launch by itself. The fused launch saves the
+# activation quantizer's launch (about 5 us per linear at decode), but each of
+# its workgroups re-reads and re-quantizes all of X: on 16-column tiles that
+# is M/4 of the weight bytes again through L2, so its cost grows as M times the
+# GEMM's own time. Measured FFN decode steps, fused against quantize + GEMM:
+# LLaMA-2-70B (112 MiB of weights per linear) faster fused up to M = 3, slower
+# at M = 4; LLaMA-2-7B (21.5 MiB) faster up to M = 4, even at M = 6, slower at
+# M = 8. The rule M x (weight bytes + FUSED_FIXED_BYTES) <= FUSED_BUDGET_BYTES
+# (the fixed term stands for the GEMM's latency, which does not shrink with
+# the weights) takes M <= 3 and M <= 5 there; the kernel's own LDS limit
+# (w4a4_linear_fused_supported) applies on top.
+FUSED_FIXED_BYTES = 96 << 20
+FUSED_BUDGET_BYTES = 640 << 20
 
 
 def use_fused(M: int, N: int, K: int, group_a: int, group_w: int) -> bool:
     """Whether w4a4_linear takes the fused launch for this shape by default."""
     from ._lib import load_library
-    return (0 < M * K <= FUSED_MAX_ELEMENTS and N > 0 and
+    return (M > 0 and N > 0 and M * (N * K // 2 + FUSED_FIXED_BYTES) <= FUSED_BUDGET_BYTES and
             bool(load_library().w4a4_linear_fused_supported(M, N, K, group_a, group_w)))
 
 

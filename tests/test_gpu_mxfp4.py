@@ -109,3 +109,33 @@ def test_full_row_tiles_fp16_and_strided_y(M, N, K):
             assert_y_close(b[:, :N], Y, T, "strided fp32")
         else:
             assert_y16_close(b[:, :N], Y, T, "strided fp16")
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 33000, 1536), (512, 33280, 1024)])
+def test_persistent_schedule(M, N, K):
+    """More 256 x 256 tiles than CUs, M a multiple of 256 and an even number of
+    256-deep K stages: the persistent schedule (the ring running on across
+    tiles, the next tile's loads issued before this tile's Y stores). Its Y
+    must be bit-identical to the same product computed in two column halves,
+    each small enough for the one-tile-per-workgroup launch, in fp32 and fp16,
+    into a strided output whose padding stays untouched; sampled rows against
+    the oracle. Shapes: 4 and 6 stages, a ragged last column tile (N = 33000)
+    and workgroups that take one or two tiles (258 / 260 tiles)."""
+    import torch
+    o = ops()
+    x = synth.activations(M, K, dist="t3", seed=31)
+    w = synth.weights(N, K, seed=32)
+    xq, xe = o.mxfp4_quantize(dev(x))
+    h = N // 2
+    halves = [o.mxfp4_quantize(dev(w[:h])), o.mxfp4_quantize(dev(w[h:]))]
+    wq, we = o.mxfp4_quantize(dev(w))
+    for dt in (torch.float32, torch.float16):
+        big = torch.full((M, N + 40), 7.0, dtype=dt, device="cuda")
+        o.mxfp4_gemm(xq, xe, wq, we, out_dtype=dt, out=big[:, :N])
+        b = host(big)
+        assert np.all(b[:, N:] == 7.0), "padding columns written"
+        ref = np.concatenate([host(o.mxfp4_gemm(xq, xe, q, e, out_dtype=dt)) for q, e in halves], axis=1)
+        assert np.array_equal(b[:, :N], ref), f"persistent schedule differs from the plain launch ({dt})"
+    rows = synth.sample_rows(M, 12, seed=33)
+    Y, T = oracle.mxfp4_gemm(*oracle.mxfp4_quantize(x[rows]), *oracle.mxfp4_quantize(w))
+    assert_y_close(host(o.mxfp4_gemm(xq, xe, wq, we))[rows], Y, T, f"persistent M={M} N={N} K={K}")

@@ -102,7 +102,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // slots of a row are XOR-swizzled with (row >> log2(16/SL)) & (SL-1) so the 16
 // lanes that read one slot of 16 consecutive rows hit 16 distinct 16-byte bank
 // groups.
-template <int BM, int BN, int WM, int WN, int KB, int S, bool PARTIALS>
+template <int BM, int BN, int WM, int WN, int KB, int S, bool PARTIALS, bool PERSIST, int YT>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_mxfp4_gemm(Params p) {
   static_assert(S == 2 || S == 3, "ring depth");    // stages in LDS; S - 1 in flight
@@ -131,61 +131,68 @@ void k_mxfp4_gemm(Params p) {
   __shared__ __align__(16) uint8_t sm2[S == 3 ? STAGE : 16];
 
   const int nblk = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int per_group = kGroupRows * p.tiles_n;
-  const int grp = bid / per_group;
-  const int first_m = grp * kGroupRows;
-  const int gsize = min(p.tiles_m - first_m, kGroupRows);
-  const int rem = bid - grp * per_group;
-  const int tile_m = (p.tile_m0 + first_m + rem % gsize) * BM;
-  const int tile_n = (p.tile_n0 + rem / gsize) * BN;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int row_bytes = p.K >> 1;
   const int nk = p.K / KB;
-
-  // ---- buffer resources over this tile's rows (row offsets stay 32-bit; the
-  // host limits K so a tile's rows span < 2^31 bytes), per-lane row offsets
-  const int a_rows = min(BM, p.M - tile_m), w_rows = min(BN, p.N - tile_n);
-  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
-  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
-  int voffA[NA], voffW[NW];
   const int lrow = lane / SL, lslot = lane % SL;
+
+  // ---- the tile of logical index t: its origin, buffer resources over its
+  // rows (row offsets stay 32-bit; the host limits K so a tile's rows span
+  // < 2^31 bytes) and per-lane row offsets. Consecutive indices on one XCD
+  // (t % 8) take consecutive tiles of a raster of kGroupRows tile-rows.
+  int tile_m, tile_n, a_rows, w_rows;
+  __amdgpu_buffer_rsrc_t rA, rW;
+  int voffA[NA], voffW[NW];
+  constexpr int CA = NEW * BM / 64, CW = NEW * BN / 64;   // scale chunks per stage
+  static_assert(CA * 64 == NEW * BM && CW * 64 == NEW * BN, "scale chunks");
+  int voffE[NE], voffE4[NE];    // the lane's offset in an 8-byte / 4-byte pitch scale panel
+  auto setup = [&](int t) {
+    int bid = t;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int per_group = kGroupRows * p.tiles_n;
+    const int grp = bid / per_group;
+    const int first_m = grp * kGroupRows;
+    const int gsize = min(p.tiles_m - first_m, kGroupRows);
+    const int rem = bid - grp * per_group;
+    tile_m = (p.tile_m0 + first_m + rem % gsize) * BM;
+    tile_n = (p.tile_n0 + rem / gsize) * BN;
+    a_rows = min(BM, p.M - tile_m);
+    w_rows = min(BN, p.N - tile_n);
+    rA = buffer_rsrc(p.a + (int64_t)tile_m * row_bytes, a_rows * row_bytes);
+    rW = buffer_rsrc(p.w + (int64_t)tile_n * row_bytes, w_rows * row_bytes);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int row = RPK * (wave + NWAVE * i) + lrow;
-    const int seg = lslot ^ ((row >> SWS) & (SL - 1));
-    voffA[i] = min(row, a_rows - 1) * row_bytes + 16 * seg;
-  }
+    for (int i = 0; i < NA; ++i) {
+      const int row = RPK * (wave + NWAVE * i) + lrow;
+      const int seg = lslot ^ ((row >> SWS) & (SL - 1));
+      voffA[i] = min(row, a_rows - 1) * row_bytes + 16 * seg;
+    }
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int row = RPK * (wave + NWAVE * i) + lrow;
-    const int seg = lslot ^ ((row >> SWS) & (SL - 1));
-    voffW[i] = min(row, w_rows - 1) * row_bytes + 16 * seg;
-  }
+    for (int i = 0; i < NW; ++i) {
+      const int row = RPK * (wave + NWAVE * i) + lrow;
+      const int seg = lslot ^ ((row >> SWS) & (SL - 1));
+      voffW[i] = min(row, w_rows - 1) * row_bytes + 16 * seg;
+    }
+    // Scale dword e = NEW * r + w of a stage is dword w of the stage's scales
+    // of A row r (e < NEW * BM) or of W row r - BM; each wave load moves one
+    // 64-dword chunk of them, chunk c = NE * wave + j.
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int c = NE * wave + j;
+      const bool is_a = c < CA;
+      const int e = 64 * (is_a ? c : c - CA) + lane;
+      const int r = min(e / NEW, (is_a ? a_rows : w_rows) - 1), w = e % NEW;
+      voffE[j] = 8 * r + 4 * w;
+      voffE4[j] = 4 * r;
+    }
+  };
   // Scales are stored in panels of 8 blocks (256 k): panel q holds, row after
   // row, each row's 8 scale bytes of blocks 8q..8q+7 (a last panel of 4 blocks
-  // holds 4 bytes per row). Scale dword e = NEW * r + w of a stage is dword w of
-  // the stage's scales of A row r (e < NEW * BM) or of W row r - BM; each wave
-  // load moves one 64-dword chunk of them, chunk c = NE * wave + j, so
-  // consecutive lanes read consecutive dwords of one panel. A buffer resource
-  // is uniform, so a chunk lies wholly in the A part or the W part.
-  constexpr int CA = NEW * BM / 64, CW = NEW * BN / 64;   // chunks per stage
-  static_assert(CA * 64 == NEW * BM && CW * 64 == NEW * BN, "scale chunks");
-  int voffE[NE], voffE4[NE];    // the lane's offset in an 8-byte / 4-byte pitch panel
-#pragma unroll
-  for (int j = 0; j < NE; ++j) {
-    const int c = NE * wave + j;
-    const bool is_a = c < CA;
-    const int e = 64 * (is_a ? c : c - CA) + lane;
-    const int r = min(e / NEW, (is_a ? a_rows : w_rows) - 1), w = e % NEW;
-    voffE[j] = 8 * r + 4 * w;
-    voffE4[j] = 4 * r;
-  }
+  // holds 4 bytes per row); consecutive lanes read consecutive dwords of one
+  // panel. A buffer resource is uniform, so a chunk lies wholly in the A part
+  // or the W part.
   // a K that is 128 mod 256 ends in a 4-block panel (4 scale bytes per row)
   const bool half_tail = (p.K & 255) != 0;
   // Scale chunk j of stage kt: the rows of panel kt (KB = 256) or of panel
@@ -350,27 +357,205 @@ void k_mxfp4_gemm(Params p) {
     });                                                                 \
   }
 
-  ISSUE(0, sm0);
-  if (S == 3 && nk > 1) ISSUE(1, sm1);
-  // Unrolled by the ring depth, so every stage names its slot statically and
-  // the loop has one back edge: the accumulators stay in the registers the
-  // matrix instructions write, with no copies between stages.
-  if constexpr (S == 3) {
-    for (int kt = 0;; kt += 3) {
-      ITER(kt, sm0, sm2)
-      if (kt + 1 >= nk) break;
-      ITER(kt + 1, sm1, sm0)
-      if (kt + 2 >= nk) break;
-      ITER(kt + 2, sm2, sm1)
-      if (kt + 3 >= nk) break;
+  // Y stores of a finished tile with origin (tm, tn) and am valid rows. The
+  // persistent kernel takes only the full-tile path (its host side admits
+  // only M a multiple of BM): TI * TJ * 16 store instructions per wave.
+  auto store_tile = [&](int tm, int tn, int am) {
+    const int ydt = YT >= 0 ? YT : p.ydtype;      // Y dtype: fixed by YT >= 0, else from the call
+    const int esz = ydt == 0 ? 4 : 2;
+    if (!PERSIST && (am != BM || (int64_t)BM * p.ldy * esz >= (int64_t{1} << 31))) {
+      // last row tile of a ragged M (or a huge ldy): per-element checked stores
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = tm + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
+            const int n = tn + wn * (BN / WN) + 32 * j + l32;
+            if (m < p.M && n < p.N) {
+              if (ydt == 0)
+                static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i][j][r];
+              else
+                static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
+            }
+          }
+      return;
     }
+    // Every row of the tile is valid and the tile spans < 2^31 bytes: buffer
+    // stores with each register's row offset in the scalar offset. A lane
+    // whose column is >= N gets a vector offset past the resource, so the
+    // hardware drops its stores.
+    const int ldb = (int)(p.ldy * esz);
+    const __amdgpu_buffer_rsrc_t rY = buffer_rsrc(static_cast<uint8_t*>(p.y) + (int64_t)tm * ldb, BM * ldb);
+    const int row0 = wm * (BM / WM) + 4 * lhi;       // tile row of register 0, block 0
+    int voffY[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n = tn + wn * (BN / WN) + 32 * j + l32;
+      voffY[j] = n < p.N ? row0 * ldb + n * esz : kDroppedOffset;
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int soff = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          if (ydt == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rY, voffY[j], soff, kStoreNT);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(acc[i][j][r])), rY, voffY[j],
+                                                  soff, kStoreNT);
+        }
+      }
+  };
+
+  if constexpr (PERSIST) {
+    // Persistent schedule: workgroup b takes tiles b, b + G, b + 2G, ... (G
+    // workgroups, a multiple of 8, so all of them run on XCD b % 8) and the
+    // ring runs on across tile edges (K in an even number >= 4 of stages, so
+    // every tile starts in slot 0). During a tile's last stage the first
+    // stage of its next tile is issued; after the last stage's matrix work
+    // the second one; then the tile's Y stores. A wave's memory operations
+    // complete in issue order and it keeps at most 63 in flight, so it issues
+    // its last stores once the next tile's two stages and about half of the
+    // stores are done; the other half drain under those two stages' matrix
+    // work, and stage 2 waits for them. (Without this, every workgroup of a
+    // round writes its Y at the same moment and then refills its ring from
+    // nothing.) The first tile's first two stages are peeled and the tile
+    // loop starts at the last stage, so at every join of the control flow the
+    // same memory operations are in flight and the compiler's own waits for
+    // the ring's loads count exactly as the ones written here.
+    static_assert(S == 2 && !PARTIALS, "persistent schedule: 2-stage ring, Y output");
+    // Y stores per wave per tile. The waits count at most 63 operations (the
+    // counter's range; a wave does not issue beyond it): with in-order
+    // completion a clamped wait waits for more, never for less. With 128
+    // stores they clamp to no wait at all: once the stores are issued, at
+    // most 63 operations are outstanding and the two stages issued before
+    // them are complete.
+    constexpr int NST = TI * TJ * 16;
+    constexpr int W0 = PER_STAGE + NST < 63 ? PER_STAGE + NST : 63;
+    constexpr int W1 = NST < 63 ? NST : 63;
+    static_assert(PER_STAGE < 63, "vmcnt range");
+    const int G = gridDim.x;
+    int t = blockIdx.x;
+// Stage 0 of a tile (slot 0; stage 1 already in flight into slot 1): wait
+// until only the WAIT_ operations issued after stage 0 are outstanding.
+#define STAGE0(WAIT_)                                                   \
+  {                                                                     \
+    wait_vmcnt<WAIT_>();                                                \
+    STAGE_BARRIER();                                                    \
+    LOAD_SCALES(0, sm0);                                                \
+    LOAD_OPS(sm0, 0, 0);                                                \
+    static_for<NSTEP>([&](auto uc_) {                                   \
+      constexpr int u_ = decltype(uc_)::value;                          \
+      if constexpr (u_ + 1 < NSTEP) LOAD_OPS(sm0, u_ + 1, (u_ + 1) & 1); \
+      PIPE_FENCE();                                                     \
+      MMA_STEP(0, u_, u_ & 1);                                          \
+      PIPE_FENCE();                                                     \
+    });                                                                 \
+  }
+// Stage 1 (slot 1; WAIT_ operations issued after it) issues stage 2, then
+// the stages up to nk - 2 run as in the plain schedule.
+#define STAGE1_TO_NK2(WAIT_)                                            \
+  {                                                                     \
+    wait_vmcnt<WAIT_>();                                                \
+    STAGE_BARRIER();                                                    \
+    LOAD_SCALES(1, sm1);                                                \
+    LOAD_OPS(sm1, 0, 0);                                                \
+    ISSUE(2, sm0);                                                      \
+    static_for<NSTEP>([&](auto uc_) {                                   \
+      constexpr int u_ = decltype(uc_)::value;                          \
+      if constexpr (u_ + 1 < NSTEP) LOAD_OPS(sm1, u_ + 1, (u_ + 1) & 1); \
+      PIPE_FENCE();                                                     \
+      MMA_STEP(1, u_, u_ & 1);                                          \
+      PIPE_FENCE();                                                     \
+    });                                                                 \
+    for (int kt = 2; kt < nk - 2; kt += 2) {                            \
+      ITER(kt, sm0, sm1)                                                \
+      ITER(kt + 1, sm1, sm0)                                            \
+    }                                                                   \
+    ITER(nk - 2, sm0, sm1)                                              \
+  }
+// The last stage (slot 1) of a tile; with NEXT, the first two stages of the
+// next tile are issued (its setup done) around the matrix work.
+#define LAST_STAGE(NEXT)                                                \
+  {                                                                     \
+    wait_vmcnt<0>();                                                    \
+    STAGE_BARRIER();                                                    \
+    LOAD_SCALES(nk - 1, sm1);                                           \
+    LOAD_OPS(sm1, 0, 0);                                                \
+    em = tile_m;                                                        \
+    en = tile_n;                                                        \
+    if constexpr (NEXT) {                                               \
+      t += G;                                                           \
+      setup(t);                                                         \
+      ISSUE(0, sm0);                                                    \
+    }                                                                   \
+    static_for<NSTEP>([&](auto uc_) {                                   \
+      constexpr int u_ = decltype(uc_)::value;                          \
+      if constexpr (u_ + 1 < NSTEP) LOAD_OPS(sm1, u_ + 1, (u_ + 1) & 1); \
+      PIPE_FENCE();                                                     \
+      MMA_STEP(nk - 1, u_, u_ & 1);                                     \
+      PIPE_FENCE();                                                     \
+    });                                                                 \
+    if constexpr (NEXT) {                                               \
+      STAGE_BARRIER();                                                  \
+      ISSUE(1, sm1);                                                    \
+    }                                                                   \
+    store_tile(em, en, BM);                                             \
+  }
+    // this workgroup's tile count: the tile loop runs a fixed number of
+    // times, so no load is issued under a condition the compiler cannot
+    // follow into the waits that depend on it
+    const int ntile = (nblk - t + G - 1) / G;
+    int em = 0, en = 0;
+    setup(t);
+    ISSUE(0, sm0);
+    ISSUE(1, sm1);
+    STAGE0(PER_STAGE)
+    STAGE1_TO_NK2(0)
+    for (int it = 1; it < ntile; ++it) {
+      LAST_STAGE(true)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      STAGE0(W0)
+      STAGE1_TO_NK2(W1)
+    }
+    LAST_STAGE(false)
+#undef LAST_STAGE
+#undef STAGE0
+#undef STAGE1_TO_NK2
   } else {
-    for (int kt = 0;; kt += 2) {
-      ITER(kt, sm0, sm1)
-      if (kt + 1 >= nk) break;
-      ITER(kt + 1, sm1, sm0)
-      if (kt + 2 >= nk) break;
+    setup(blockIdx.x);
+    ISSUE(0, sm0);
+    if (S == 3 && nk > 1) ISSUE(1, sm1);
+    // Unrolled by the ring depth, so every stage names its slot statically and
+    // the loop has one back edge: the accumulators stay in the registers the
+    // matrix instructions write, with no copies between stages.
+    if constexpr (S == 3) {
+      for (int kt = 0;; kt += 3) {
+        ITER(kt, sm0, sm2)
+        if (kt + 1 >= nk) break;
+        ITER(kt + 1, sm1, sm0)
+        if (kt + 2 >= nk) break;
+        ITER(kt + 2, sm2, sm1)
+        if (kt + 3 >= nk) break;
+      }
+    } else {
+      for (int kt = 0;; kt += 2) {
+        ITER(kt, sm0, sm1)
+        if (kt + 1 >= nk) break;
+        ITER(kt + 1, sm1, sm0)
+        if (kt + 2 >= nk) break;
+      }
     }
+    if constexpr (!PARTIALS) store_tile(tile_m, tile_n, a_rows);
   }
 #undef ITER
 #undef STAGE_BARRIER
@@ -379,88 +564,68 @@ void k_mxfp4_gemm(Params p) {
 #undef LOAD_SCALES
 #undef MMA_SEL
 #undef ISSUE
-
-  if constexpr (!PARTIALS) {
-    const int esz = p.ydtype == 0 ? 4 : 2;
-    if (a_rows == BM && (int64_t)BM * p.ldy * esz < (int64_t{1} << 31)) {
-      // Every row of the tile is valid and the tile spans < 2^31 bytes: buffer
-      // stores with the row offset of each accumulator register in the scalar
-      // offset and no per-element address arithmetic or branches. A lane whose
-      // column is >= N gets a vector offset past the resource, so the hardware
-      // drops its stores (the range check covers the vector offset; rows need
-      // none here).
-      const int ldb = (int)(p.ldy * esz);
-      const __amdgpu_buffer_rsrc_t rY =
-          buffer_rsrc(static_cast<uint8_t*>(p.y) + (int64_t)tile_m * ldb, BM * ldb);
-      const int row0 = wm * (BM / WM) + 4 * lhi;       // tile row of register 0, block 0
-      int voffY[TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
-        voffY[j] = n < p.N ? row0 * ldb + n * esz : kDroppedOffset;
-      }
-      if (p.ydtype == 0) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int soff = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rY, voffY[j], soff, kStoreNT);
-          }
-      } else {
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int soff = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-              __builtin_amdgcn_raw_buffer_store_b16(__half_as_ushort(__float2half_rn(acc[i][j][r])), rY,
-                                                    voffY[j], soff, kStoreNT);
-          }
-      }
-    } else {
-      // last row tile of a ragged M (or a huge ldy): per-element checked stores
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = tile_m + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * lhi + (r & 3);
-            const int n = tile_n + wn * (BN / WN) + 32 * j + l32;
-            if (m < p.M && n < p.N) {
-              if (p.ydtype == 0)
-                static_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = acc[i][j][r];
-              else
-                static_cast<__half*>(p.y)[(int64_t)m * p.ldy + n] = __float2half_rn(acc[i][j][r]);
-            }
-          }
-    }
-  }
 }
 
-template <int BM, int BN, int WM, int WN, int KB, int S, bool PARTIALS>
-void launch_cfg(Params p, const GemmArgs& g, hipStream_t stream) {
-  p.tile_m0 = (int)(g.m0 / BM);
-  p.tile_n0 = (int)(g.n0 / BN);
-  p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
-  p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
-  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, KB, S, PARTIALS>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
-                     dim3(64 * WM * WN), 0, stream, p);
+// YT: the Y dtype fixed at compile time (0 fp32, 1 fp16), or -1 to read it
+// from the call. The persistent kernel fixes it: its stores are then one
+// straight-line block, which the compiler's wait counting follows exactly.
+template <int BM, int BN, int WM, int WN, int KB, int S, bool PARTIALS, bool PERSIST, int YT>
+void launch_cfg(Params p, const GemmArgs& g, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((k_mxfp4_gemm<BM, BN, WM, WN, KB, S, PARTIALS, PERSIST, YT>), dim3(grid), dim3(64 * WM * WN),
+                     0, stream, p);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 // 256 x 256 tiles (2 x 4 waves of 128 x 64) with 256-deep stages in a 2-stage
 // ring (2 x 68 KB) when K allows, else 128 x 128 tiles (2 x 2 waves) with
-// 128-deep stages in a 3-stage ring.
+// 128-deep stages in a 3-stage ring. The 256 x 256 kernel runs the persistent
+// schedule (one workgroup per CU, the ring running on across tiles) when the
+// grid holds more tiles than CUs, every row tile is full (M a multiple of
+// 256) and K is an even number >= 4 of 256-deep stages.
 template <bool PARTIALS>
 void launch_for(Params p, const GemmArgs& g, hipStream_t stream) {
-  if (g.K % 256 == 0)
-    launch_cfg<256, 256, 2, 4, 256, 2, PARTIALS>(p, g, stream);
-  else
-    launch_cfg<128, 128, 2, 2, 128, 3, PARTIALS>(p, g, stream);
+  const int esz = g.ydtype == 0 ? 4 : 2;
+  const int64_t ldb = g.ldy * esz;
+  if (g.K % 256 == 0) {
+    constexpr int BM = 256, BN = 256;
+    p.tile_m0 = (int)(g.m0 / BM);
+    p.tile_n0 = (int)(g.n0 / BN);
+    p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
+    p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
+    const int64_t nblk = (int64_t)p.tiles_m * p.tiles_n;
+    if constexpr (!PARTIALS) {
+      const int64_t slots = cu_count() / 8 * 8;
+      const int64_t nk = g.K / 256;
+      if (slots >= 8 && nblk > slots && g.M % BM == 0 && nk >= 4 && nk % 2 == 0 &&
+          BM * ldb < (int64_t{1} << 31)) {
+        if (g.ydtype == 0)
+          launch_cfg<256, 256, 2, 4, 256, 2, false, true, 0>(p, g, (unsigned)slots, stream);
+        else
+          launch_cfg<256, 256, 2, 4, 256, 2, false, true, 1>(p, g, (unsigned)slots, stream);
+        return;
+      }
+    }
+    launch_cfg<256, 256, 2, 4, 256, 2, PARTIALS, false, -1>(p, g, (unsigned)nblk, stream);
+  } else {
+    constexpr int BM = 128, BN = 128;
+    p.tile_m0 = (int)(g.m0 / BM);
+    p.tile_n0 = (int)(g.n0 / BN);
+    p.tiles_m = (int)((g.m0 + g.mc - 1) / BM) - p.tile_m0 + 1;
+    p.tiles_n = (int)((g.n0 + g.nc - 1) / BN) - p.tile_n0 + 1;
+    launch_cfg<128, 128, 2, 2, 128, 3, PARTIALS, false, -1>(p, g, (unsigned)(p.tiles_m * p.tiles_n), stream);
+  }
 }
 
 }  // namespace

@@ -293,3 +293,34 @@ def test_partials_production_tiles(M, N, K, window):
     qw, _ = oracle.int4_quantize(w, 128)
     for b, P in oracle.w4a4_block_partials(qa, qw, 128):
         assert np.array_equal(part[b], P), f"partials block {b}, M={M} window={window}"
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 16896, 768), (512, 16640, 512)])
+def test_many_tiles_matches_column_halves(M, N, K):
+    """More 256 x 128 tiles than CUs (264 tiles: a multiple of 8, so the
+    XCD-contiguous raster remaps the tile order; and 260): Y must be
+    bit-identical to the same product computed in two column halves (a
+    different raster), so every tile is computed once and lands where it
+    belongs, including into a strided output whose padding stays untouched;
+    sampled rows against the oracle."""
+    import torch
+    o = ops()
+    x = synth.activations(M, K, dist="t3", seed=41)
+    w = synth.weights(N, K, seed=42)
+    xq, xs = o.w4a4_quantize_act(dev(x), 128)
+    wq, ws = o.w4a4_pack_weight(dev(w), 128)
+    h = N // 2
+    halves = [o.w4a4_pack_weight(dev(w[:h]), 128), o.w4a4_pack_weight(dev(w[h:]), 128)]
+    ref = np.concatenate([host(o.w4a4_gemm(xq, xs, 128, q, s, 128)) for q, s in halves], axis=1)
+    y = host(o.w4a4_gemm(xq, xs, 128, wq, ws, 128))
+    assert np.array_equal(y, ref), "full launch differs from its column halves"
+    big = torch.full((M, N + 40), 7.0, dtype=torch.float32, device="cuda")
+    o.w4a4_gemm(xq, xs, 128, wq, ws, 128, out=big[:, :N])
+    b = host(big)
+    assert np.all(b[:, N:] == 7.0), "padding columns written"
+    assert np.array_equal(b[:, :N], ref), "strided output differs"
+    rows = synth.sample_rows(M, 12, seed=43)
+    qa, sa = oracle.int4_quantize(x[rows], 128)
+    qw, sw = oracle.int4_quantize(w, 128)
+    Y, T = oracle.w4a4_gemm(qa, sa, 128, qw, sw, 128)
+    assert_y_close(y[rows], Y, T, f"many tiles M={M} N={N} K={K}")

@@ -109,7 +109,8 @@ def quant_standalone(shapes, ga, fmt, reps: int = 24, nrot: int = 6):
     """Activation quantization on its own: for each distinct [M, K], ``reps``
     back-to-back launches rotating over ``nrot`` resident inputs (more bytes
     than the 256 MB last-level cache, so every launch reads HBM), queued behind
-    a spin kernel and timed with HIP events on the launch stream. Returns per-shape rows and the overall
+    a spin kernel and one untimed pass over the inputs, and timed with HIP
+    events on the launch stream. Returns per-shape rows and the overall
     GB/s over the algorithmic bytes (fp16 in, codes and scales out)."""
     import torch
     from w4a4_quantized_gemm_quantize_amd import ops
@@ -141,8 +142,11 @@ def quant_standalone(shapes, ga, fmt, reps: int = 24, nrot: int = 6):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         # a spin kernel holds the stream while the host enqueues every launch, so
-        # the timed launches run back to back (host launch cost excluded)
+        # the timed launches run back to back (host launch cost excluded); one
+        # untimed pass over the inputs behind it brings the clocks back up
         torch.cuda._sleep(5_000_000)
+        for i in range(nrot):
+            call(xs[i])
         e0.record()
         for i in range(reps):
             call(xs[i % nrot])
@@ -423,12 +427,19 @@ def main() -> int:
         kernel holds the stream while the host enqueues them, so they run back
         to back as a captured graph would (at few tokens a launch takes longer
         to enqueue than to run); the start event is queued behind the spin,
-        which is not timed. Returns (seconds, per-step launch events or None)."""
+        which is not timed. While the spin runs the GPU is all but idle and
+        lowers its clocks, so args.warmup more untimed steps run between the
+        spin and the start event (measured at M = 4096: without them the
+        timed steps ran ~5 % slower, the clocks still rising; a longer warm-up
+        before the spin did not help). Returns (seconds, per-step launch
+        events or None)."""
         evs = ([[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
                 for _ in range(args.steps)] if per_launch_events else None)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2e6) * args.steps)
+        torch.cuda._sleep(int(2e6) * (args.steps + args.warmup))
+        for _ in range(args.warmup):
+            step(None, shared)
         start.record()
         for s in range(args.steps):
             step(evs[s] if evs else None, shared)
@@ -513,7 +524,7 @@ def main() -> int:
                       "method": "per-launch events inside the timed steps (each launch follows a GEMM "
                                 "whose output fills the caches with dirty lines)"},
         "act_quant_standalone": {"GB/s": q_gbs, "frac_hbm": q_gbs / PEAK_HBM_GBS, "per_shape": q_rows,
-                                 "method": "24 back-to-back launches over 6 rotating resident inputs, queued behind a spin kernel, HIP events"},
+                                 "method": "24 back-to-back launches over 6 rotating resident inputs, queued behind a spin kernel and an untimed pass over the inputs, HIP events"},
         "per_linear": per_linear,
         "w13_shared_quant": ({"value": ops_per_step * args.steps / shared_elapsed / 1e12, "unit": "TOPS",
                               "ms_per_step": shared_elapsed / args.steps * 1e3,

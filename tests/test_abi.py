@@ -273,3 +273,21 @@ def test_fused_linear_validation(lib):
     assert st(f, None, 2, 256, 256, 128, P, P, 128, 64, P, 0, 64, None) == E_NULL
     assert st(f, P + 8, 2, 256, 256, 128, P, P, 128, 64, P, 0, 64, None) == E_ALIGN
     assert st(f, None, 0, 256, 256, 128, None, None, 128, 64, None, 0, 64, None) == OK   # empty
+
+
+def test_fused_policy_choices(lib):
+    """w4a4_linear's own choice of the fused launch (host logic): the measured
+    decode crossovers (LLaMA-2-70B w1/w3 fused up to M = 3; LLaMA-2-7B up to
+    M = 5), never past the kernel's LDS limit, never for empty shapes."""
+    from w4a4_quantized_gemm_quantize_amd import ops
+    picks = lambda N, K: [M for M in range(1, 33) if ops.use_fused(M, N, K, 128, 128)]
+    assert picks(28672, 8192) == [1, 2, 3]          # LLaMA-2-70B w1 / w3
+    assert picks(8192, 28672) == [1]                # w2: the LDS copy of X fits M = 1 only
+    assert picks(11008, 4096) == [1, 2, 3, 4, 5]    # LLaMA-2-7B w1 / w3
+    assert picks(4096, 11008) == [1, 2, 3, 4, 5]    # LLaMA-2-7B w2
+    for M, N, K in ((0, 64, 256), (1, 0, 256)):
+        assert not ops.use_fused(M, N, K, 128, 128)
+    for M in range(1, 33):                          # the policy never asks for an unsupported launch
+        for N, K in ((28672, 8192), (8192, 28672), (11008, 4096), (64, 1024)):
+            if ops.use_fused(M, N, K, 128, 128):
+                assert lib.w4a4_linear_fused_supported(M, N, K, 128, 128) == 1

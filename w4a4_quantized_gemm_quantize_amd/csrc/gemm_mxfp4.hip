@@ -21,7 +21,11 @@
 // registers): 2 x 68 KB stages for the 256 x 256 tile (one stage in flight
 // behind the matrix work), 3 x 34 KB for the 128 x 128 tile (two in flight).
 // The debug-partials variant runs the same instruction one 32-block at a time
-// with unit scales.
+// with unit scales. Grids with more 256 x 256 tiles than CUs run a persistent
+// variant: one workgroup per CU takes tile after tile and the ring runs on
+// across tile edges, so a tile's Y stores drain under the next tile's first
+// stages instead of every workgroup of a round writing its Y at once and
+// refilling its ring from nothing.
 //
 // 32x32 MFMA output layout: D element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
 // col l%32.

@@ -784,7 +784,12 @@ __global__ __launch_bounds__(64 * SM_WAVES) void k_w4a4_gemm_small(Params p, int
 // integer partials and epilogue order as k_w4a4_gemm_small, so Y is
 // bit-identical to it; the scale product is one multiply per output.
 constexpr int SM16_TILE = 16;
-constexpr int SM16_RING = 8;        // 128-k steps in flight per wave (refilled two at a time)
+// 128-k steps in flight per wave, refilled two at a time. A short ring keeps the
+// kernel at ~52 VGPRs, so every workgroup of a LLaMA-2-70B w1 launch (1792)
+// is resident at once; rings of 4 and 8 (78 / 130 VGPRs: 1536 / 768 resident
+// workgroups) measured slower at M = 1, 4 and 16 with W streamed from HBM
+// (w1 M = 4: 30.0 / 30.3 / 33.5 us).
+constexpr int SM16_RING = 2;
 
 typedef float v4f_16 __attribute__((ext_vector_type(4)));
 

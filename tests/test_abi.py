@@ -257,10 +257,13 @@ def test_fused_linear_validation(lib):
     st = _lib.status_of
     sup = lib.w4a4_linear_fused_supported
     assert sup(1, 28672, 8192, 128, 128) == 1 and sup(8, 28672, 8192, 128, 128) == 1
-    # 16-column tiles (4 accumulators per lane to sum across waves): M = 9 fits
-    # 64 KiB, M = 10 does not; 32-column tiles (16 per lane): M = 2 at K = 28672 does not
+    # the fused path's 16-column tiles (4 accumulators per lane to sum across
+    # waves): M = 9 fits 64 KiB at K = 8192, M = 10 does not; M = 2 at K = 28672,
+    # M = 3 not
     assert sup(9, 28672, 8192, 128, 128) == 1 and sup(10, 28672, 8192, 128, 128) == 0
-    assert sup(1, 8192, 28672, 128, 128) == 1 and sup(2, 8192, 28672, 128, 128) == 0
+    assert sup(2, 8192, 28672, 128, 128) == 1 and sup(3, 8192, 28672, 128, 128) == 0
+    # groups of 64 take the 32-column tiles (16 accumulators per lane)
+    assert sup(2, 8192, 8192, 64, 64) == 1 and sup(4, 8192, 28672, 64, 64) == 0
     assert sup(33, 64, 256, 128, 128) == 0 and sup(4, 64, 1024, 1024, 128) == 0   # per-token A: not fused
     assert sup(4, 64, 1024, 96, 128) == 0 and sup(0, 64, 256, 128, 128) == 0
     f = "w4a4_linear_fused"
@@ -282,7 +285,7 @@ def test_fused_policy_choices(lib):
     from w4a4_quantized_gemm_quantize_amd import ops
     picks = lambda N, K: [M for M in range(1, 33) if ops.use_fused(M, N, K, 128, 128)]
     assert picks(28672, 8192) == [1, 2, 3]          # LLaMA-2-70B w1 / w3
-    assert picks(8192, 28672) == [1]                # w2: the LDS copy of X fits M = 1 only
+    assert picks(8192, 28672) == [1, 2]             # w2: the LDS copy of X fits M <= 2
     assert picks(11008, 4096) == [1, 2, 3, 4, 5]    # LLaMA-2-7B w1 / w3
     assert picks(4096, 11008) == [1, 2, 3, 4, 5]    # LLaMA-2-7B w2
     for M, N, K in ((0, 64, 256), (1, 0, 256)):

@@ -76,7 +76,7 @@ def test_fused_zero_rows_and_unsupported():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 28672, 8192), (8, 28672, 8192), (9, 28672, 8192), (1, 8192, 28672),
-                                   (7, 11008, 4096), (4, 4096, 11008)])   # last two: LLaMA-2-7B
+                                   (2, 8192, 28672), (7, 11008, 4096), (4, 4096, 11008)])   # last two: LLaMA-2-7B
 def test_fused_llama_decode(M, N, K):
     o = ops()
     x = synth.activations(M, K, dist="t3", seed=0)

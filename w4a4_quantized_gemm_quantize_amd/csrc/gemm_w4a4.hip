@@ -1198,13 +1198,23 @@ int tile_rows(int64_t M, int64_t gmin) { return M > 128 && gmin != 64 ? 256 : 12
 // grid is one 32-column tile per workgroup): 8 below 512 workgroups, else 4.
 int small_waves(int64_t tiles) { return tiles < 512 ? 8 : 4; }
 
-// Few-token tile width: 16 columns (k_w4a4_gemm_small16 and its fused twin)
-// for M <= 16 with groups of 128 or more and per-group activation scales where
-// the 32-column grid does not spread evenly over the 256 CUs, else 32.
-bool use_small16(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw) {
+// Few-token tile widths. The two widths split K between the waves alike (the
+// wave count of the 32-column grid) and sum in the same order, so Y does not
+// depend on the choice. 16 columns (k_w4a4_linear_small16) for the fused path
+// wherever they apply: M <= 16, groups of 128 or more, per-group activation
+// scales.
+bool use_small16_fused(int64_t M, int64_t K, int64_t ga, int64_t gw) {
   const int64_t gmin = ga < gw ? ga : gw;
+  return M <= SM16_TILE && gmin >= 128 && ga != K;
+}
+// The GEMM (k_w4a4_gemm_small16) likewise, except at M = 1 on a 32-column grid
+// that spreads evenly over the 256 CUs (LLaMA-2-70B w2: 256 workgroups of 8
+// waves, one per CU), which streams W faster there (measured 30.1 against
+// 32.5 us; at M = 4 and 16 the 16-column tiles: 31.1 / 40.6 against 34.0 /
+// 45.1 us).
+bool use_small16(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw) {
   const int64_t nwg = ((M + SM_TILE - 1) / SM_TILE) * ((N + SM_TILE - 1) / SM_TILE);
-  return M <= SM16_TILE && gmin >= 128 && ga != K && nwg % 256 != 0;
+  return use_small16_fused(M, K, ga, gw) && (M > 1 || nwg % 256 != 0);
 }
 
 template <bool PARTIALS, bool ROWA>
@@ -1252,9 +1262,7 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
     // partials window runs the configuration the plain launch of this shape
     // runs, and both tile widths split K between the waves alike
     const int64_t nwg = ((g.M + SM_TILE - 1) / SM_TILE) * ((g.N + SM_TILE - 1) / SM_TILE);
-    // 16-column tiles where the 32-column grid leaves the CUs unevenly loaded
-    // (LLaMA-2-70B w1: 896 workgroups; w2's 256 workgroups of 8 waves, one per
-    // CU, stream faster as they are)
+    // 16-column tiles (see use_small16)
     if (use_small16(g.M, g.N, g.K, g.ga, g.gw)) {
       p.tile_m0 = (int)(g.m0 / SM16_TILE);
       p.tile_n0 = (int)(g.n0 / SM16_TILE);
@@ -1301,7 +1309,7 @@ void launch_w4a4_gemm(const GemmArgs& g, hipStream_t stream) {
 // 32-column tiles, 4 on 16-column tiles) for every wave but the first.
 int64_t linear_small_lds_bytes(int64_t M, int64_t N, int64_t K, int64_t ga, int64_t gw) {
   const int nw = small_waves((N + SM_TILE - 1) / SM_TILE);
-  const int acc = use_small16(M, N, K, ga, gw) ? 4 : 16;
+  const int acc = use_small16_fused(M, K, ga, gw) ? 4 : 16;
   return 24 * M * (K / 32) + 4 * M * (K / ga) + 4 * acc * 64 * (nw - 1);
 }
 
@@ -1355,9 +1363,10 @@ void launch_w4a4_linear_small(const void* x, int64_t M, int64_t K, int64_t ldx, 
   const int spg = (int)(gmin / 64);
   const int tiles_n = (int)((N + SM_TILE - 1) / SM_TILE);
   const size_t lds = (size_t)linear_small_lds_bytes(M, N, K, ga, gw);
-  // the tile width and wave count of the few-token GEMM of this shape, so the
-  // waves' K ranges and the fixed-order sum of their accumulators are the same
-  if (use_small16(M, N, K, ga, gw)) {
+  // the wave count of the few-token GEMM of this shape (from its 32-column
+  // grid), so the waves' K ranges and the fixed-order sum of their
+  // accumulators are the same whichever tile width either path takes
+  if (use_small16_fused(M, K, ga, gw)) {
     const dim3 grid16((unsigned)((N + SM16_TILE - 1) / SM16_TILE));
     if (small_waves(tiles_n) == 8)
       launch_linear16_waves<8>(ga, grid16, lds, p, (int)(gmin / 128), stream);

@@ -175,10 +175,9 @@ int64_t w4a4_gemm_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t grou
  *   x        fp16 [M][ldx], 16-byte aligned, ldx >= K, ldx % 8 == 0
  *   group_a  64, 128, 256 or 512; group_w and wq, ws as for w4a4_gemm
  *   M, N, K  1 <= M <= 32 and 24 M K/32 + 4 M K/group_a + the cross-wave
- *            reduction buffer (3 or 7 KiB on the 16-column tiles the few-token
- *            GEMM takes for M <= 16 and groups >= 128 where the 32-column grid
- *            does not spread evenly over the CUs; else 12 or 28 KiB) within
- *            64 KiB (LLaMA-2-70B FFN: M <= 9 for w1/w3, K = 8192; M = 1 for
+ *            reduction buffer (3 or 7 KiB on the 16-column tiles this path
+ *            takes for M <= 16 with groups >= 128; else 12 or 28 KiB) within
+ *            64 KiB (LLaMA-2-70B FFN: M <= 9 for w1/w3, K = 8192; M <= 2 for
  *            w2, K = 28672); otherwise W4A4_E_SHAPE
  *   y        as for w4a4_gemm
  */
